@@ -1,0 +1,171 @@
+/*
+ * mok.h — C ABI of the MI355X (gfx950) Mixture-of-Kittens-style MoE layer library.
+ *
+ * One MoE layer on one GPU's share of an expert-parallel layer: a schedule (per-expert
+ * counts, offsets and a dispatch table), dispatch of routed rows into a fixed ring of
+ * minibatch slots, the SwiGLU expert FFN as grouped MFMA GEMMs, and the gate-weighted
+ * combine back to token order — forward in one persistent kernel whose workgroups are
+ * split between data movement (dispatch/combine) and MFMA compute, handing work to
+ * each other through device-memory counters.
+ *
+ * Sources (web pages on Cursor's open-sourced Mixture-of-Kittens, MoK):
+ *   [L] Leiphone, "MoK：把 token 调度、跨 GPU 通信和专家计算塞进同一个 GPU 内核",
+ *       sections 01, 02, 03;
+ *   [M] news brief "Cursor开源MoK：GB300 NVL72机架上的确定性MoE训练大内核",
+ *       section "三个重要的设计决策".
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller.  The
+ *     library never allocates or frees device memory and keeps no global state; calls
+ *     on different workspaces are independent.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; no entry point synchronises except mok_read_device_status.
+ *   - Host-side argument checks (null pointers, shapes, workspace size, unsupported
+ *     modes) return an error code synchronously and enqueue nothing.  These checks run
+ *     before any HIP runtime call, so they work on a machine without a GPU.
+ *   - Data-dependent faults are recorded in a sticky device status word inside the
+ *     workspace (MOK_DEV_* bits), read back with mok_read_device_status.
+ *   - Same inputs and descriptor give bitwise-identical outputs (fixed-order sums, no
+ *     floating-point atomics).
+ *
+ * Layouts (row-major, "nn.Linear" convention: the K dimension of every GEMM operand
+ * is contiguous):
+ *   x, y, dy, dx      [T, D]           bf16
+ *   topk_ids          [T, k]           int32  (global expert id, -1 = masked slot)
+ *   topk_w, d_topk_w  [T, k]           fp32   (gate weights and their gradient)
+ *   w_gate, w_up      [E_loc, I, D]    bf16   (index 0 = expert e0)
+ *   w_down            [E_loc, D, I]    bf16
+ *   dw_gate, dw_up    [E_loc, I, D]    fp32;   dw_down [E_loc, D, I] fp32
+ *   MXFP8 weights: e4m3 codes with the same shapes (uint8) plus e8m0 scales, one byte
+ *   per 32 consecutive elements along the contiguous K axis ([E_loc, I, D/32] and
+ *   [E_loc, D, I/32]).
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOK_OK = 0,
+  MOK_E_NULL = 1,        /* a required pointer is NULL                               */
+  MOK_E_SHAPE = 2,       /* a size is out of range or inconsistent                   */
+  MOK_E_UNSUPPORTED = 3, /* valid request this build does not implement              */
+  MOK_E_WORKSPACE = 4,   /* workspace smaller than mok_workspace_size                */
+  MOK_E_LAUNCH = 5,      /* the HIP runtime refused a launch                         */
+  MOK_E_DEVICE = 6       /* no usable gfx950 device / runtime error                  */
+} mok_status_t;
+
+/* precision */
+#define MOK_PREC_BF16 0
+#define MOK_PREC_MXFP8 1
+
+/* flags */
+#define MOK_FLAG_SAVE_FOR_BWD 0x1u  /* forward keeps X and the gate/up pre-activations of
+                                       the resident minibatches for mok_moe_bwd          */
+#define MOK_FLAG_UNFUSED 0x2u       /* run the same steps as separate kernels over
+                                       full-size buffers (comparison / phase timing)     */
+
+/* sticky device status bits (mok_read_device_status) */
+#define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */
+#define MOK_DEV_TIMEOUT 0x2u  /* a bounded wait inside a persistent kernel expired      */
+
+/* Layer descriptor.  Symbols follow the pages' vocabulary: a minibatch is the number of
+ * routed rows handed to expert compute at once ([L] section 02); the ring of
+ * minibatch slots is the fixed-size token buffer ([L] section 02, [M] design
+ * decisions); comm_cus is the explicit split of compute units between data movement
+ * and expert FFN ([L] section 02). */
+typedef struct {
+  int32_t num_tokens;        /* T: tokens in the pool                                   */
+  int32_t hidden;            /* D: hidden size (multiple of 64)                         */
+  int32_t intermediate;      /* I: expert intermediate size (multiple of 64)            */
+  int32_t num_experts;       /* E: experts over all GPUs                                */
+  int32_t top_k;             /* k: slots per token (1..64)                              */
+  int32_t expert_begin;      /* e0: first local expert                                  */
+  int32_t num_local_experts; /* E_loc: local experts [e0, e0+E_loc), 1..1024            */
+  int32_t minibatch_rows;    /* M: routed rows per minibatch / ring slot                */
+  int32_t ring_slots;        /* S: slots in the ring (>= 1)                             */
+  int32_t comm_cus;          /* workgroups doing dispatch/combine in the fused kernel   */
+  int32_t precision;         /* MOK_PREC_BF16 or MOK_PREC_MXFP8 (forward only)          */
+  uint32_t flags;            /* MOK_FLAG_*                                              */
+} mok_desc_t;
+
+/* Bytes of workspace the layer needs for `desc` (host only, no HIP call).
+ * The workspace holds the schedule, the ring of S minibatch slots, the per-slot
+ * result buffer and the device counters.  Errors: MOK_E_NULL, MOK_E_SHAPE,
+ * MOK_E_UNSUPPORTED. */
+mok_status_t mok_workspace_size(const mok_desc_t* desc, size_t* bytes);
+
+/* Schedule ([L] section 01: count every expert's rows, choose their positions, keep
+ * one expert's rows contiguous for the grouped GEMM; [M] design decisions: one table
+ * serves the four transfers).  Reads topk_ids [T, k] and writes into the workspace:
+ * per-local-expert counts and offsets, perm[r] = t*k + j for every routed row r (rows
+ * of one expert contiguous, in ascending (token, slot) order), pos[t*k+j] = row or -1,
+ * and the minibatch tile table.  Ids outside [e0, e0+E_loc) are not local; -1 is
+ * masked; ids < -1 or >= E set MOK_DEV_BAD_ID and are skipped.  Also clears the
+ * device status word.  Must precede mok_moe_fwd with the same ids and workspace. */
+mok_status_t mok_schedule(const mok_desc_t* desc, const int32_t* topk_ids, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Copy the schedule tables out of the workspace (device to device, async on stream):
+ * counts [E_loc], offsets [E_loc+1], perm [T*k] (entries >= R are unspecified),
+ * pos [T*k], and hdr[4] = {R, number of minibatches, number of m-tiles, status}.
+ * Any output pointer may be NULL to skip it. */
+mok_status_t mok_schedule_tables(const mok_desc_t* desc, const void* ws, size_t ws_bytes,
+                                 int32_t* counts, int32_t* offsets, int32_t* perm,
+                                 int32_t* pos, int32_t* hdr, void* stream);
+
+/* Quantise bf16 rows to MXFP8 ([L] section 02 names MXFP8; the block format is OCP MX:
+ * e4m3 elements, one e8m0 scale per 32 elements).  src [rows, cols] bf16 (cols a
+ * multiple of 32) -> codes [rows, cols] uint8, scales [rows, cols/32] uint8.  The
+ * shared exponent is the smallest n with amax * 2^-n <= 448 (clamped to [-127, 127];
+ * an all-zero block gets n = -127), code = e4m3 round-to-nearest-even of v * 2^-n.
+ * Used for the weights before a MXFP8 forward. */
+mok_status_t mok_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, uint8_t* codes,
+                             uint8_t* scales, void* stream);
+
+/* Forward ([L] sections 02-03: dispatch, expert FFN, combine and the final weighted sum
+ * in one persistent kernel; [M] design decisions).  y [T, D] bf16:
+ *   y[t] = sum over slots j in ascending order with a local expert e = ids[t,j]-e0 of
+ *          topk_w[t,j] * ( silu(x[t] W_gate[e]^T) * (x[t] W_up[e]^T) ) W_down[e]^T
+ * accumulated in fp32, rounded once to bf16; tokens with no local slot get 0.
+ * bf16 mode: weights are bf16 (s_* must be NULL).  MXFP8 mode: w_* point to e4m3 codes
+ * and s_* to their e8m0 scales (from mok_quantize_mx); X is quantised during dispatch
+ * and H inside the SwiGLU epilogue.  Requires a preceding mok_schedule on `ws`. */
+mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* topk_ids,
+                         const float* topk_w, const void* w_gate, const void* w_up,
+                         const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                         const uint8_t* s_down, void* y, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Backward (bf16) ([L] section 02: reverse-combine pulls dY, reverse-dispatch pushes dX;
+ * [M] design decisions: the ring is walked in reverse to limit replay of forward
+ * activations, and the router-weight gradient is formed inside the SwiGLU backward).
+ * Needs the workspace of a preceding mok_moe_fwd run with MOK_FLAG_SAVE_FOR_BWD and the
+ * same inputs.  Outputs: dx [T, D] bf16, d_topk_w [T, k] fp32 (0 for non-local slots),
+ * dw_gate, dw_up [E_loc, I, D] fp32 and dw_down [E_loc, D, I] fp32 (overwritten, not
+ * accumulated; experts with no rows get 0).  dW sums over rows run in a fixed order. */
+mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
+                         const int32_t* topk_ids, const float* topk_w, const void* w_gate,
+                         const void* w_up, const void* w_down, void* dx, float* d_topk_w,
+                         float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, then read the sticky device status word (MOK_DEV_* bits). */
+mok_status_t mok_read_device_status(const void* ws, void* stream, uint32_t* out);
+
+/* Static text for a status code. */
+const char* mok_status_string(mok_status_t s);
+
+/* Number of compute units of the current device (0 on error); a helper for choosing
+ * comm_cus. */
+int32_t mok_device_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOK_H */

@@ -1,0 +1,77 @@
+// Device pointers into the workspace (derived from Layout) and the launchers the C ABI
+// calls.  Host and device code share this header.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "layout.h"
+
+namespace mok {
+
+struct Ptrs {
+  uint32_t* hdr;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* blk;
+  int32_t* perm;
+  int32_t* pos;
+  int4* mt_tab;       // [n_mb_max][mt_max] = (first row, rows, local expert, 0)
+  int32_t* mt_cnt;    // [n_mb_max]
+  int32_t* tile_base; // [n_mb_max + 1]
+  uint32_t* sync;     // device counters
+  uint16_t* obuf;     // [T*k, D] bf16: expert output of pair t*k + j
+  uint8_t* ring;      // S slots
+  uint8_t* full_x;    // unfused: [T*k, D] dispatched rows (bf16 or MX codes)
+  uint8_t* full_xs;   // unfused MX scales
+  uint8_t* full_h;    // unfused: [T*k, I] hidden rows
+  uint8_t* full_hs;
+  uint16_t* dxbuf;    // backward: [T*k, D] bf16 per-pair dX contributions
+  float* dgpart;      // backward: [T*k, nN1] partial router-weight gradients
+  uint8_t* bring;     // backward slots
+};
+
+inline Ptrs make_ptrs(const Layout& L, void* ws) {
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  Ptrs P;
+  P.hdr = reinterpret_cast<uint32_t*>(b + L.off_hdr);
+  P.counts = reinterpret_cast<int32_t*>(b + L.off_counts);
+  P.offsets = reinterpret_cast<int32_t*>(b + L.off_offsets);
+  P.blk = reinterpret_cast<int32_t*>(b + L.off_blk);
+  P.perm = reinterpret_cast<int32_t*>(b + L.off_perm);
+  P.pos = reinterpret_cast<int32_t*>(b + L.off_pos);
+  P.mt_tab = reinterpret_cast<int4*>(b + L.off_mt_tab);
+  P.mt_cnt = reinterpret_cast<int32_t*>(b + L.off_mt_cnt);
+  P.tile_base = reinterpret_cast<int32_t*>(b + L.off_tile_base);
+  P.sync = reinterpret_cast<uint32_t*>(b + L.off_sync);
+  P.obuf = reinterpret_cast<uint16_t*>(b + L.off_obuf);
+  P.ring = b + L.off_ring;
+  P.full_x = L.unfused ? b + L.off_full_x : nullptr;
+  P.full_xs = L.unfused ? b + L.off_full_xs : nullptr;
+  P.full_h = L.unfused ? b + L.off_full_h : nullptr;
+  P.full_hs = L.unfused ? b + L.off_full_hs : nullptr;
+  P.dxbuf = L.save ? reinterpret_cast<uint16_t*>(b + L.off_dxbuf) : nullptr;
+  P.dgpart = L.save ? reinterpret_cast<float*>(b + L.off_dgpart) : nullptr;
+  P.bring = L.save ? b + L.off_bring : nullptr;
+  return P;
+}
+
+// Layer inputs of one forward/backward call.
+struct FwdArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* gates;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const uint8_t* sg;
+  const uint8_t* su;
+  const uint8_t* sd;
+  uint16_t* y;
+  int comm_cus;
+};
+
+mok_status_t launch_schedule(const Layout& L, const Ptrs& P, const int32_t* ids, hipStream_t st);
+mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st);
+mok_status_t launch_quantize_mx(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
+                                uint8_t* scales, hipStream_t st);
+
+}  // namespace mok

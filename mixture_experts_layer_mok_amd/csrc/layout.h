@@ -1,0 +1,145 @@
+// Workspace layout of one layer call, computed identically on the host (sizes,
+// pointer arithmetic) and described to the kernels through MokParams.
+//
+// Everything the layer keeps between its kernels lives in one caller-owned workspace:
+//   header words, schedule tables, device counters, the per-pair result buffer,
+//   the ring of S minibatch slots and (optional) full-size buffers for the unfused
+//   path and the backward pass.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mok.h"
+
+namespace mok {
+
+// GEMM tiling shared by every grouped-GEMM kernel.
+constexpr int kBM = 128;       // rows per m-tile
+constexpr int kBN1 = 128;      // intermediate columns per GEMM1 tile (gate and up each)
+constexpr int kBN2 = 256;      // hidden columns per GEMM2 tile
+constexpr int kBK = 64;        // K step (bf16 elements)
+constexpr int kThreads = 256;  // threads per workgroup (4 waves of 64)
+
+// Schedule kernels.
+constexpr int kSchedChunk = 4096;  // pairs per counting block (4 waves x 1024)
+constexpr int kSchedSub = 1024;    // pairs per wave sub-chunk
+constexpr int kMaxLocalExperts = 1024;
+
+// Header words (int32) at the start of the workspace.
+enum HdrWord : int {
+  kHdrStatus = 0,      // sticky MOK_DEV_* bits
+  kHdrR = 1,           // routed local rows
+  kHdrNmb = 2,         // minibatches
+  kHdrMtiles = 3,      // m-tiles over all minibatches
+  kHdrFwdTicket = 4,   // fused forward: next tile ticket
+  kHdrAbort = 5,       // set when a bounded wait expires; every loop exits
+  kHdrFwdTiles = 6,    // fused forward: total tiles
+  kHdrBwdTicket = 7,   // fused backward: next tile ticket
+  kHdrBwdTiles = 8,
+  kHdrWords = 64
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  // shape
+  int64_t T, D, I, E, k, e0, nl, M, S, TK;
+  int64_t NB;        // counting blocks of the schedule
+  int64_t NS;        // wave sub-chunks (4 per block)
+  int64_t n_mb_max;  // ceil(T*k / M)
+  int64_t mt_max;    // m-tiles per minibatch, upper bound
+  int64_t nN1, nN2;  // n-tiles of GEMM1 (over I) and GEMM2 (over D)
+  bool mx, save, unfused;
+  // byte offsets into the workspace
+  size_t off_hdr, off_counts, off_offsets, off_blk, off_perm, off_pos, off_mt_tab, off_mt_cnt,
+      off_tile_base, off_sync, sync_bytes, off_obuf, off_ring, slot_bytes;
+  size_t slot_x, slot_xs, slot_h, slot_hs, slot_ab;  // offsets inside one slot
+  size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
+  // backward
+  size_t off_bwd, off_dxbuf, off_dgpart, bslot_bytes, bslot_dy, bslot_dab, off_bring;
+  size_t total;
+};
+
+// Fills `L` from the descriptor; returns MOK_OK or the first violated check.
+inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
+  if (!d || !L) return MOK_E_NULL;
+  const int64_t T = d->num_tokens, D = d->hidden, I = d->intermediate, E = d->num_experts;
+  const int64_t k = d->top_k, e0 = d->expert_begin, nl = d->num_local_experts;
+  const int64_t M = d->minibatch_rows, S = d->ring_slots;
+  if (T < 1 || T > (1 << 24)) return MOK_E_SHAPE;
+  if (D < 64 || D % 64 != 0 || D > 65536) return MOK_E_SHAPE;
+  if (I < 64 || I % 64 != 0 || I > 65536) return MOK_E_SHAPE;
+  if (E < 1 || k < 1 || k > 64 || k > E) return MOK_E_SHAPE;
+  if (nl < 1 || nl > kMaxLocalExperts || e0 < 0 || e0 + nl > E) return MOK_E_SHAPE;
+  if (M < 1 || M > (1 << 20) || S < 1 || S > 64) return MOK_E_SHAPE;
+  if (T * k > (int64_t(1) << 24)) return MOK_E_SHAPE;
+  if (d->comm_cus < 1) return MOK_E_SHAPE;
+  if (d->precision != MOK_PREC_BF16 && d->precision != MOK_PREC_MXFP8) return MOK_E_UNSUPPORTED;
+  if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED)) return MOK_E_UNSUPPORTED;
+  L->T = T; L->D = D; L->I = I; L->E = E; L->k = k; L->e0 = e0; L->nl = nl; L->M = M; L->S = S;
+  L->TK = T * k;
+  L->mx = d->precision == MOK_PREC_MXFP8;
+  L->save = (d->flags & MOK_FLAG_SAVE_FOR_BWD) != 0;
+  L->unfused = (d->flags & MOK_FLAG_UNFUSED) != 0;
+  if (L->mx && L->save) return MOK_E_UNSUPPORTED;  // MXFP8 backward is not built
+  L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
+  L->NS = L->NB * (kSchedChunk / kSchedSub);
+  L->n_mb_max = (L->TK + M - 1) / M;
+  L->mt_max = (M + kBM - 1) / kBM + nl;
+  if (L->mt_max > L->TK / kBM + 1 + nl) L->mt_max = L->TK / kBM + 1 + nl;
+  L->nN1 = (I + kBN1 - 1) / kBN1;
+  L->nN2 = (D + kBN2 - 1) / kBN2;
+
+  const size_t A = 256;
+  size_t o = 0;
+  L->off_hdr = o; o = align_up(o + kHdrWords * 4, A);
+  L->off_counts = o; o = align_up(o + nl * 4, A);
+  L->off_offsets = o; o = align_up(o + (nl + 1) * 4, A);
+  L->off_blk = o; o = align_up(o + L->NS * (nl + 1) * 4, A);  // per sub-chunk counts + bad
+  L->off_perm = o; o = align_up(o + L->TK * 4, A);
+  L->off_pos = o; o = align_up(o + L->TK * 4, A);
+  L->off_mt_tab = o; o = align_up(o + L->n_mb_max * L->mt_max * 16, A);
+  L->off_mt_cnt = o; o = align_up(o + L->n_mb_max * 4, A);
+  L->off_tile_base = o; o = align_up(o + (L->n_mb_max + 1) * 4, A);
+  // forward counters: ready[n_mb], done[n_mb], hdone[n_mb * mt_max];
+  // backward counters: bready[n_mb], bdone[n_mb], hd[n_mb*mt_max], dxd[n_mb*mt_max],
+  // wdone[n_mb * nl * 3]
+  L->sync_bytes = align_up((2 * L->n_mb_max + L->n_mb_max * L->mt_max) * 4, A) +
+                  align_up((2 * L->n_mb_max + 2 * L->n_mb_max * L->mt_max +
+                            3 * L->n_mb_max * nl) * 4, A);
+  L->off_sync = o; o = align_up(o + L->sync_bytes, A);
+  L->off_obuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
+  // one ring slot
+  size_t so = 0;
+  L->slot_x = so; so = align_up(so + size_t(M) * D * (L->mx ? 1 : 2), A);
+  L->slot_xs = so; so = align_up(so + (L->mx ? size_t(M) * (D / 32) : 0), A);
+  L->slot_h = so; so = align_up(so + size_t(M) * I * (L->mx ? 1 : 2), A);
+  L->slot_hs = so; so = align_up(so + (L->mx ? size_t(M) * (I / 32) : 0), A);
+  L->slot_ab = so; so = align_up(so + (L->save ? size_t(M) * 2 * I * 2 : 0), A);
+  L->slot_bytes = so;
+  L->off_ring = o; o = align_up(o + L->slot_bytes * S, A);
+  // full-size buffers for the unfused path
+  L->off_full_x = L->off_full_xs = L->off_full_h = L->off_full_hs = 0;
+  if (L->unfused) {
+    L->off_full_x = o; o = align_up(o + size_t(L->TK) * D * (L->mx ? 1 : 2), A);
+    L->off_full_xs = o; o = align_up(o + (L->mx ? size_t(L->TK) * (D / 32) : 0), A);
+    L->off_full_h = o; o = align_up(o + size_t(L->TK) * I * (L->mx ? 1 : 2), A);
+    L->off_full_hs = o; o = align_up(o + (L->mx ? size_t(L->TK) * (I / 32) : 0), A);
+  }
+  // backward regions (present when the forward saves for backward)
+  L->off_bwd = L->off_dxbuf = L->off_dgpart = L->off_bring = 0;
+  L->bslot_bytes = L->bslot_dy = L->bslot_dab = 0;
+  if (L->save) {
+    L->off_dxbuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
+    L->off_dgpart = o; o = align_up(o + size_t(L->TK) * L->nN1 * 4, A);
+    size_t bo = 0;
+    L->bslot_dy = bo; bo = align_up(bo + size_t(M) * D * 2, A);
+    L->bslot_dab = bo; bo = align_up(bo + size_t(M) * 2 * I * 2, A);
+    L->bslot_bytes = bo;
+    L->off_bring = o; o = align_up(o + L->bslot_bytes * S, A);
+  }
+  L->total = o;
+  return MOK_OK;
+}
+
+}  // namespace mok

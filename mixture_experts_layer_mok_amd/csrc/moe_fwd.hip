@@ -1,0 +1,386 @@
+// Forward of the MoE layer on one GPU's share (bf16).
+//
+// Steps (Leiphone article on MoK, sections 02-03; news brief, design decisions):
+//   dispatch  — pull: row r of minibatch mb is copied from the token pool,
+//               X[perm[r] / k], into ring slot mb % S (the owner lays rows out itself,
+//               already grouped by expert);
+//   GEMM1     — per expert segment: a = X W_gate^T, b = X W_up^T sharing the A tile,
+//               SwiGLU h = silu(a) * b in the epilogue, H written to the slot;
+//   GEMM2     — o = H W_down^T, pushed straight to its pair's row of the result buffer
+//               (the destination of every result is known from the schedule);
+//   combine   — the final weighted sum: y[t] = sum_j gate[t,j] * o[t*k+j] over local
+//               slots in ascending j, fp32 (multiply, then add), rounded once to bf16.
+//
+// Fused form (one persistent cooperative kernel): the first comm_cus workgroups move
+// data (dispatch + combine), the rest run MFMA tiles.  Handoff goes through device
+// counters with agent-scope release/acquire (each MI355X XCD has its own L2):
+//   ready[mb]  comm workgroups that finished gathering their share of mb;
+//   hdone[mb][i]  GEMM1 tiles finished for m-tile i of mb (GEMM2 of that m-tile waits);
+//   done[mb]   GEMM2 tiles finished for mb — frees slot mb % S and allows combining
+//              the tokens whose last local row lies in mb.
+// Compute workgroups take tiles from an atomic ticket in minibatch order (GEMM1 tiles
+// of mb, then its GEMM2 tiles), so every wait is on work with a smaller ticket or on a
+// comm step that only depends on such work: no cycle, given all workgroups are
+// co-resident (cooperative launch).  A token is combined by the comm workgroup that
+// owns its highest local row, right after that row's minibatch is done, so most of the
+// combine overlaps later minibatches' GEMMs.
+#include <algorithm>
+
+#include "gemm_bf16.h"
+#include "launch.h"
+
+namespace mok {
+
+struct FwdParams {
+  Ptrs P;
+  FwdArgs a;
+  int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
+  int64_t slot_bytes, slot_x, slot_h, slot_ab;
+};
+
+// ------------------------------------------------------------------------------------
+// wave-level data movement
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
+                                              const uint16_t* __restrict__ src, int D) {
+  const int lane = threadIdx.x & 63;
+  const int nch = D >> 3;
+  const v4u* s = reinterpret_cast<const v4u*>(src);
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  int c = lane;
+  for (; c + 192 < nch; c += 256) {
+    const v4u v0 = s[c], v1 = s[c + 64], v2 = s[c + 128], v3 = s[c + 192];
+    d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
+  }
+  for (; c < nch; c += 64) d[c] = s[c];
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Highest local row of token t (-1 when it has none).  Lanes j < k read pos[t*k+j].
+__device__ __forceinline__ int token_last_row(const int32_t* pos, int t, int k) {
+  const int lane = threadIdx.x & 63;
+  const int v = lane < k ? pos[int64_t(t) * k + lane] : -1;
+  return wave_max(v);
+}
+
+// y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.
+__device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
+  const int lane = threadIdx.x & 63;
+  const int D = p.D, k = p.k;
+  const int64_t q0 = int64_t(t) * k;
+  const int32_t my_pos = lane < k ? p.P.pos[q0 + lane] : -1;
+  const float my_g = lane < k ? p.a.gates[q0 + lane] : 0.f;
+  const uint64_t has = __ballot(my_pos >= 0);
+  v4u* yrow = reinterpret_cast<v4u*>(p.a.y + int64_t(t) * D);
+  for (int c = lane; c < (D >> 3); c += 64) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    uint64_t m = has;
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const float g = __shfl(my_g, j);
+      const v4u v = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + j) * D)[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = __fadd_rn(acc[2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
+        acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
+      }
+    }
+    v4u out;
+    out.x = pack_bf16x2(acc[0], acc[1]);
+    out.y = pack_bf16x2(acc[2], acc[3]);
+    out.z = pack_bf16x2(acc[4], acc[5]);
+    out.w = pack_bf16x2(acc[6], acc[7]);
+    yrow[c] = out;
+  }
+}
+
+__device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
+  const int lane = threadIdx.x & 63;
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  for (int c = lane; c < (D >> 3); c += 64) d[c] = v4u{0u, 0u, 0u, 0u};
+}
+
+// ------------------------------------------------------------------------------------
+// GEMM tiles
+// ------------------------------------------------------------------------------------
+// GEMM1 + SwiGLU for rows [0, rows) of A (already offset to the tile's first row) and
+// intermediate columns [n0, n0 + 128).  Writes H (and, when AB != null, the gate/up
+// pre-activations as [rows, 2I]: gate in [0, I), up in [I, 2I)).
+__device__ __forceinline__ void gemm1_tile(TileSmem& sm, const uint16_t* A, int64_t lda, int rows,
+                                           const uint16_t* wg_e, const uint16_t* wu_e, int n0,
+                                           int I, int D, uint16_t* H, int64_t ldh,
+                                           uint16_t* AB) {
+  TileSrc src;
+  tile_src_init(src, A, lda, rows, wg_e, wu_e, D, n0, n0, I);
+  TileAcc acc;
+  tile_gemm(sm, src, D, acc);
+  const int lane = threadIdx.x & 63;
+  const int wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(i, v);
+        if (row < rows && col < I) {
+          const float g = acc.c[i][j][v], u = acc.c[i][j + 2][v];
+          H[int64_t(row) * ldh + col] = f32_to_bf16(silu_f(g) * u);
+          if (AB) {
+            AB[int64_t(row) * 2 * I + col] = f32_to_bf16(g);
+            AB[int64_t(row) * 2 * I + I + col] = f32_to_bf16(u);
+          }
+        }
+      }
+    }
+}
+
+// GEMM2 for rows [0, rows) of H and hidden columns [n0, n0 + 256); row r's result goes
+// to obuf row perm_rows[r] (its pair index).
+__device__ __forceinline__ void gemm2_tile(TileSmem& sm, const uint16_t* Hrows, int64_t ldh,
+                                           int rows, const uint16_t* wd_e, int n0, int D, int I,
+                                           const int32_t* perm_rows, uint16_t* obuf) {
+  TileSrc src;
+  tile_src_init(src, Hrows, ldh, rows, wd_e, wd_e, I, n0, n0 + 128, D);
+  TileAcc acc;
+  tile_gemm(sm, src, I, acc);
+  const int lane = threadIdx.x & 63;
+  const int wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int dst[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = acc_row(i, v);
+      dst[v] = row < rows ? perm_rows[row] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + brow_of(j, wn) + (lane & 31);
+      if (col >= D) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (dst[v] >= 0) obuf[int64_t(dst[v]) * D + col] = f32_to_bf16(acc.c[i][j][v]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Unfused kernels: the same steps over full-size buffers, one launch per step.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
+  const int R = int(p.P.hdr[kHdrR]);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  uint16_t* X = reinterpret_cast<uint16_t*>(p.P.full_x);
+  for (int r = gw; r < R; r += nw)
+    wave_copy_row(X + int64_t(r) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+}
+
+__global__ __launch_bounds__(256) void k_gemm1_all(FwdParams p) {
+  __shared__ TileSmem sm;
+  const int nt = blockIdx.x % p.nN1;
+  const int f = blockIdx.x / p.nN1;
+  const int mb = f / p.mt_max, i = f % p.mt_max;
+  if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return;
+  const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(p.P.full_x);
+  uint16_t* H = reinterpret_cast<uint16_t*>(p.P.full_h);
+  const int64_t wsz = int64_t(p.I) * p.D;
+  gemm1_tile(sm, X + int64_t(e.x) * p.D, p.D, e.y,
+             reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
+             reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.I, p.D,
+             H + int64_t(e.x) * p.I, p.I, nullptr);
+}
+
+__global__ __launch_bounds__(256) void k_gemm2_all(FwdParams p) {
+  __shared__ TileSmem sm;
+  const int nt = blockIdx.x % p.nN2;
+  const int f = blockIdx.x / p.nN2;
+  const int mb = f / p.mt_max, i = f % p.mt_max;
+  if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return;
+  const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+  const uint16_t* H = reinterpret_cast<const uint16_t*>(p.P.full_h);
+  const int64_t wsz = int64_t(p.I) * p.D;
+  gemm2_tile(sm, H + int64_t(e.x) * p.I, p.I, e.y,
+             reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nt * kBN2, p.D, p.I,
+             p.P.perm + e.x, p.P.obuf);
+}
+
+__global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  for (int t = gw; t < p.T; t += nw) {
+    if (token_last_row(p.P.pos, t, p.k) >= 0) wave_combine_token(p, t);
+    else wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Fused persistent kernel
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fwd_prep(FwdParams p) {
+  const int64_t words = 2 * int64_t(p.n_mb_max) + int64_t(p.n_mb_max) * p.mt_max;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p.P.sync[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    p.P.hdr[kHdrFwdTicket] = 0;
+    p.P.hdr[kHdrAbort] = 0;
+  }
+}
+
+__device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uint32_t* done) {
+  uint32_t* hdr = p.P.hdr;
+  const int R = int(hdr[kHdrR]);
+  const int n_mb = int(hdr[kHdrNmb]);
+  const int w = threadIdx.x >> 6;
+  const int gw = c * 4 + w, nw = C * 4;
+  // tokens without a local slot: y = 0
+  for (int t = gw; t < p.T; t += nw)
+    if (token_last_row(p.P.pos, t, p.k) < 0) wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
+
+  auto combine_mb = [&](int cm) {
+    const int lo = cm * p.M, hi = min(lo + p.M, R);
+    for (int r = lo + gw; r < hi; r += nw) {
+      const int t = p.P.perm[r] / p.k;
+      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token(p, t);
+    }
+  };
+  auto mb_tiles2 = [&](int mb) { return uint32_t(p.P.mt_cnt[mb] * p.nN2); };
+
+  for (int mb = 0; mb < n_mb; ++mb) {
+    const int s = mb % p.S;
+    if (mb >= p.S) {
+      if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr)) return;
+    }
+    uint16_t* slot_x = reinterpret_cast<uint16_t*>(p.P.ring + s * p.slot_bytes + p.slot_x);
+    const int lo = mb * p.M, hi = min(lo + p.M, R);
+    for (int r = lo + gw; r < hi; r += nw)
+      wave_copy_row(slot_x + int64_t(r - lo) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+    wg_signal_add(ready + mb, 1);
+    if (mb >= p.S) combine_mb(mb - p.S);
+  }
+  for (int cm = max(0, n_mb - p.S); cm < n_mb; ++cm) {
+    if (!wg_wait_geq(done + cm, mb_tiles2(cm), hdr)) return;
+    combine_mb(cm);
+  }
+}
+
+__device__ void compute_role(const FwdParams& p, TileSmem& sm, int C, uint32_t* ready,
+                             uint32_t* done, uint32_t* hdone) {
+  uint32_t* hdr = p.P.hdr;
+  const uint32_t total = hdr[kHdrFwdTiles];
+  const int n_mb = int(hdr[kHdrNmb]);
+  const int64_t wsz = int64_t(p.I) * p.D;
+  __shared__ uint32_t s_ticket;
+  int mb = 0;
+  while (true) {
+    if (threadIdx.x == 0) s_ticket = fetch_add_relaxed(hdr + kHdrFwdTicket, 1u);
+    __syncthreads();
+    const uint32_t tk = s_ticket;
+    __syncthreads();
+    if (tk >= total || aborted(hdr)) break;
+    while (mb + 1 < n_mb && uint32_t(p.P.tile_base[mb + 1]) <= tk) ++mb;
+    const int q = int(tk - uint32_t(p.P.tile_base[mb]));
+    const int nmt = p.P.mt_cnt[mb];
+    const int s = mb % p.S;
+    uint8_t* slot = p.P.ring + s * p.slot_bytes;
+    uint16_t* slot_x = reinterpret_cast<uint16_t*>(slot + p.slot_x);
+    uint16_t* slot_h = reinterpret_cast<uint16_t*>(slot + p.slot_h);
+    const int lo = mb * p.M;
+    if (q < nmt * p.nN1) {
+      const int i = q / p.nN1, nt = q % p.nN1;
+      if (!wg_wait_geq(ready + mb, uint32_t(C), hdr)) break;
+      const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+      const int r0 = e.x - lo;
+      uint16_t* ab = p.save ? reinterpret_cast<uint16_t*>(slot + p.slot_ab) + int64_t(r0) * 2 * p.I
+                            : nullptr;
+      gemm1_tile(sm, slot_x + int64_t(r0) * p.D, p.D, e.y,
+                 reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
+                 reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.I, p.D,
+                 slot_h + int64_t(r0) * p.I, p.I, ab);
+      wg_signal_add(hdone + int64_t(mb) * p.mt_max + i, 1);
+    } else {
+      const int q2 = q - nmt * p.nN1;
+      const int i = q2 / p.nN2, nt = q2 % p.nN2;
+      if (!wg_wait_geq(hdone + int64_t(mb) * p.mt_max + i, uint32_t(p.nN1), hdr)) break;
+      const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+      const int r0 = e.x - lo;
+      gemm2_tile(sm, slot_h + int64_t(r0) * p.I, p.I, e.y,
+                 reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nt * kBN2, p.D, p.I,
+                 p.P.perm + e.x, p.P.obuf);
+      wg_signal_add(done + mb, 1);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fwd_fused(FwdParams p) {
+  __shared__ TileSmem sm;
+  uint32_t* ready = p.P.sync;
+  uint32_t* done = ready + p.n_mb_max;
+  uint32_t* hdone = done + p.n_mb_max;
+  const int C = p.a.comm_cus;
+  if (int(blockIdx.x) < C) comm_role(p, blockIdx.x, C, ready, done);
+  else compute_role(p, sm, C, ready, done, hdone);
+}
+
+// ------------------------------------------------------------------------------------
+// host
+// ------------------------------------------------------------------------------------
+static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
+  FwdParams p;
+  p.P = P;
+  p.a = a;
+  p.T = int(L.T); p.D = int(L.D); p.I = int(L.I); p.k = int(L.k); p.M = int(L.M);
+  p.S = int(L.S); p.mt_max = int(L.mt_max); p.nN1 = int(L.nN1); p.nN2 = int(L.nN2);
+  p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
+  p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
+  p.slot_h = int64_t(L.slot_h); p.slot_ab = int64_t(L.slot_ab);
+  return p;
+}
+
+int fused_grid_size() {
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k_fwd_fused),
+                                                   256, 0) != hipSuccess)
+    return 0;
+  return cus * occ;
+}
+
+mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st) {
+  FwdParams p = make_params(L, P, a);
+  if (L.unfused) {
+    const unsigned gw = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
+    hipLaunchKernelGGL(k_gather_all, dim3(gw), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_gemm1_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN1)), dim3(256), 0,
+                       st, p);
+    hipLaunchKernelGGL(k_gemm2_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN2)), dim3(256), 0,
+                       st, p);
+    hipLaunchKernelGGL(k_combine_all, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
+                       dim3(256), 0, st, p);
+    return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
+  }
+  const int grid = fused_grid_size();
+  if (grid <= 0) return MOK_E_DEVICE;
+  if (a.comm_cus >= grid) return MOK_E_SHAPE;
+  hipLaunchKernelGGL(k_fwd_prep, dim3(64), dim3(256), 0, st, p);
+  if (hipGetLastError() != hipSuccess) return MOK_E_LAUNCH;
+  void* args[] = {&p};
+  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_fused), dim3(grid), dim3(256),
+                                 args, 0, st) != hipSuccess)
+    return MOK_E_LAUNCH;
+  return MOK_OK;
+}
+
+}  // namespace mok

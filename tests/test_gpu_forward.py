@@ -1,0 +1,156 @@
+"""GPU parity of the schedule and the bf16 forward against the float64 oracle.
+
+Schedule tables are compared bit-exactly.  Layer outputs are compared by relative
+Frobenius error against the oracle's float64 result (bound 1e-2 for bf16): the GPU reads
+bf16 inputs, accumulates in fp32, rounds H and the expert outputs to bf16 and the layer
+output once to bf16, so the expected error is a few 1e-3 at most."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_mok_amd import _lib as L
+from mixture_experts_layer_mok_amd import gen
+from tests.gpu_util import DevInputs, rel_fro, run_forward, say, y_values
+
+pytestmark = pytest.mark.gpu
+TOL_BF16 = 1e-2
+
+
+def _check_schedule(cfg, d, ids, layer):
+    tab = layer.tables()
+    s = O.schedule(ids, cfg.e0, cfg.n_local, cfg.E, cfg.M)
+    assert tab["R"] == s.R
+    assert tab["n_mb"] == s.n_mb
+    assert np.array_equal(tab["counts"], s.counts)
+    assert np.array_equal(tab["offsets"], s.offsets)
+    assert np.array_equal(tab["perm"], s.perm)
+    assert np.array_equal(tab["pos"], s.pos)
+    return tab
+
+
+SMALL = [
+    gen.CONFIGS[1],
+    gen.small_config("ragged", T=300, D=192, I=192, E=6, k=2, M=96, S=2, comm_cus=8),
+    gen.small_config("e0", T=257, D=128, I=128, E=16, k=4, e0=5, E_loc=6, M=64, S=3, comm_cus=16),
+    gen.small_config("zipf", T=512, D=256, I=320, E=8, k=3, M=200, S=1, comm_cus=8, zipf_s=1.2),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_forward_small_parity(cfg, fused):
+    say(f"[fwd-small] {cfg.name} fused={fused}")
+    d = gen.make_inputs(cfg, seed=101)
+    dev = DevInputs(d)
+    y, layer = run_forward(cfg, dev, flags=0 if fused else L.MOK_FLAG_UNFUSED)
+    assert layer.status() == 0
+    _check_schedule(cfg, d, d["ids"], layer)
+    ref = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0, E=cfg.E,
+                    M=cfg.M)
+    err = rel_fro(y_values(y), ref)
+    say(f"  rel_fro={err:.3e}")
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_forward_c1_ring_slots(S):
+    cfg = gen.CONFIGS[1]
+    d = gen.make_inputs(cfg)
+    dev = DevInputs(d)
+    ys = []
+    for comm in (1, 8, 24):
+        y, layer = run_forward(cfg, dev, S=S, comm_cus=comm)
+        assert layer.status() == 0
+        ys.append(y.clone())
+    ref = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0, E=cfg.E, M=32)
+    assert rel_fro(y_values(ys[0]), ref) < TOL_BF16
+    # error against the unrounded float32 draws, for information
+    if d["x_raw"] is not None:
+        ref_raw = O.forward(d["x_raw"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0,
+                            E=cfg.E, M=32)
+        say(f"  c1 vs unrounded draws: {rel_fro(y_values(ys[0]), ref_raw):.3e}")
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
+def test_forward_edge_cases():
+    cfg = gen.small_config("edge", T=200, D=128, I=128, E=8, k=2, M=64, S=2, comm_cus=8)
+    d = gen.make_inputs(cfg, seed=5)
+    ref_args = (d["x"], None, d["gates"], d["wg"], d["wu"], d["wd"])
+    cases = {
+        "none_local": np.full_like(d["ids"], -1),
+        "all_to_one": np.stack([np.full(200, 3), np.full(200, -1)], 1).astype(np.int32),
+        "masked": gen.mask_ids(d["ids"], 0.4, seed=1),
+    }
+    for name, ids in cases.items():
+        say(f"[edge] {name}")
+        dev = DevInputs(d, ids=ids)
+        y, layer = run_forward(cfg, dev)
+        assert layer.status() == 0
+        _check_schedule(cfg, d, ids, layer)
+        ref = O.forward(ref_args[0], ids, *ref_args[2:], e0=0, E=cfg.E, M=cfg.M)
+        yv = y_values(y)
+        if name == "none_local":
+            assert np.all(yv == 0)
+        else:
+            assert rel_fro(yv, ref) < TOL_BF16
+    # out-of-range ids are flagged and skipped
+    bad = d["ids"].copy()
+    bad[::7, 0] = cfg.E + 3
+    bad[1::11, 1] = -5
+    dev = DevInputs(d, ids=bad)
+    y, layer = run_forward(cfg, dev)
+    assert layer.status() == L.MOK_DEV_BAD_ID
+    ref = O.forward(d["x"], bad, d["gates"], d["wg"], d["wu"], d["wd"], e0=0, E=cfg.E, M=cfg.M)
+    assert rel_fro(y_values(y), ref) < TOL_BF16
+
+
+def test_forward_config2_full():
+    cfg = gen.CONFIGS[2]
+    say("[c2] generating")
+    d = gen.make_inputs(cfg)
+    dev = DevInputs(d)
+    y, layer = run_forward(cfg, dev)
+    assert layer.status() == 0
+    tab = _check_schedule(cfg, d, d["ids"], layer)
+    assert tab["R"] == cfg.T * cfg.k
+    ref = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0, E=cfg.E,
+                    M=cfg.M)
+    err = rel_fro(y_values(y), ref)
+    say(f"  c2 rel_fro={err:.3e}")
+    assert err < TOL_BF16
+    y2, _ = run_forward(cfg, dev, flags=L.MOK_FLAG_UNFUSED)
+    assert torch.equal(y, y2)
+
+
+@pytest.fixture(scope="module")
+def c3_inputs():
+    cfg = gen.CONFIGS[3]
+    say("[c3] generating inputs")
+    d = gen.make_inputs(cfg)
+    return cfg, d, DevInputs(d)
+
+
+def test_forward_config3_sampled_and_deterministic(c3_inputs):
+    cfg, d, dev = c3_inputs
+    y, layer = run_forward(cfg, dev)
+    assert layer.status() == 0
+    _check_schedule(cfg, d, d["ids"], layer)
+    rng = np.random.default_rng(33)
+    toks = np.sort(rng.choice(cfg.T, 48, replace=False))
+    ref = O.forward_tokens(toks, d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0)
+    yv = y_values(y)[toks]
+    err = rel_fro(yv, ref)
+    say(f"  c3 sampled rel_fro={err:.3e}")
+    assert err < TOL_BF16
+    y_again, _ = run_forward(cfg, dev)
+    assert torch.equal(y, y_again)
+    # per-row arithmetic does not depend on the minibatch split, the ring or the CU split
+    for over in (dict(M=512, S=2, comm_cus=16), dict(M=4096, S=1, comm_cus=64)):
+        say(f"  invariance {over}")
+        y_o, lay = run_forward(cfg, dev, **over)
+        assert lay.status() == 0
+        assert torch.equal(y, y_o)
+    y_u, _ = run_forward(cfg, dev, flags=L.MOK_FLAG_UNFUSED)
+    assert torch.equal(y, y_u)
