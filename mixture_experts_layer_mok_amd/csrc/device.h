@@ -40,23 +40,24 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(v4u a, v4u b, f32x16_t c) {
 }
 
 // ------------------------------------------------------------------------------------
-// Cross-workgroup handoff.  Producers: every thread fences its own stores at agent
-// scope (so they leave this XCD's L2), the workgroup meets at a barrier, and one
-// thread publishes with an agent-scope release add.  Consumers: one thread waits with
-// agent-scope acquire loads, then the workgroup meets and every thread acquires.
+// Cross-workgroup handoff inside the persistent kernels.
+//
+// MI355X has 8 XCDs, each with its own L2; plain stores may sit in the producer's L2 and
+// plain loads may hit a stale line in the consumer's L2.  Instead of agent-scope
+// release/acquire fences (which write back and invalidate the whole L2 of the XCD on
+// every handoff and so destroy the weight reuse of every workgroup on it), all data
+// that crosses workgroups inside a kernel is written with device-scope stores and read
+// with device-scope loads (the sc1 cache policy), which are coherent on their own.
+// The counters are agent-scope atomics.
+//   producer: device-scope data stores; wait for them (vmcnt 0); meet; one thread adds.
+//   consumer: one thread polls the counter; meet; device-scope data loads.
 // Waits are bounded: on expiry the waiter sets MOK_DEV_TIMEOUT and the abort word,
 // and every loop of the persistent kernels exits once the abort word is set.
 // ------------------------------------------------------------------------------------
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s of the 100 MHz constant clock
 
-__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void add_release(uint32_t* p, uint32_t v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t fetch_add_relaxed(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -65,14 +66,32 @@ __device__ __forceinline__ void or_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// device-scope (coherent across XCDs) data movement
+__device__ __forceinline__ void st_dev_u16(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_b128(void* p, v4u v) {
+  uint64_t* q = static_cast<uint64_t*>(p);
+  __hip_atomic_store(q, uint64_t(v.x) | (uint64_t(v.y) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, uint64_t(v.z) | (uint64_t(v.w) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ v4u ld_dev_b128(const void* p) {
+  const uint64_t* q = static_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v4u{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
 // Whole workgroup: wait until *p >= target.  Returns false when aborted/timed out.
 __device__ __forceinline__ bool wg_wait_geq(const uint32_t* p, uint32_t target, uint32_t* hdr) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
     int ok = 1;
-    if (ld_acquire(p) < target) {
+    if (ld_relaxed(p) < target) {
       const uint64_t t0 = wall_clock64();
-      while (ld_acquire(p) < target) {
+      while (ld_relaxed(p) < target) {
         if (ld_relaxed(hdr + kHdrAbort)) { ok = 0; break; }
         if (wall_clock64() - t0 > kWaitTicks) {
           or_relaxed(hdr + kHdrStatus, MOK_DEV_TIMEOUT);
@@ -87,16 +106,15 @@ __device__ __forceinline__ bool wg_wait_geq(const uint32_t* p, uint32_t target, 
   }
   __syncthreads();
   const bool ok = s_ok != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();  // s_ok may be rewritten by the next wait
   return ok;
 }
 
-// Whole workgroup: publish this workgroup's stores, then *p += v.
+// Whole workgroup: this workgroup's device-scope stores are complete, then *p += v.
 __device__ __forceinline__ void wg_signal_add(uint32_t* p, uint32_t v) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) add_release(p, v);
+  if (threadIdx.x == 0) fetch_add_relaxed(p, v);
 }
 
 __device__ __forceinline__ bool aborted(const uint32_t* hdr) { return ld_relaxed(hdr + kHdrAbort) != 0; }

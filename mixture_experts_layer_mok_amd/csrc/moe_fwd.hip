@@ -41,6 +41,7 @@ struct FwdParams {
 // ------------------------------------------------------------------------------------
 // wave-level data movement
 // ------------------------------------------------------------------------------------
+template <bool kCoherent>
 __device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
                                               const uint16_t* __restrict__ src, int D) {
   const int lane = threadIdx.x & 63;
@@ -50,9 +51,17 @@ __device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
   int c = lane;
   for (; c + 192 < nch; c += 256) {
     const v4u v0 = s[c], v1 = s[c + 64], v2 = s[c + 128], v3 = s[c + 192];
-    d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
+    if (kCoherent) {
+      st_dev_b128(d + c, v0); st_dev_b128(d + c + 64, v1);
+      st_dev_b128(d + c + 128, v2); st_dev_b128(d + c + 192, v3);
+    } else {
+      d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
+    }
   }
-  for (; c < nch; c += 64) d[c] = s[c];
+  for (; c < nch; c += 64) {
+    if (kCoherent) st_dev_b128(d + c, s[c]);
+    else d[c] = s[c];
+  }
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -69,6 +78,7 @@ __device__ __forceinline__ int token_last_row(const int32_t* pos, int t, int k) 
 }
 
 // y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.
+template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
   const int lane = threadIdx.x & 63;
   const int D = p.D, k = p.k;
@@ -86,7 +96,8 @@ __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
       const int j = __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
       const float g = __shfl(my_g, j);
-      const v4u v = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + j) * D)[c];
+      const v4u* src = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + j) * D) + c;
+      const v4u v = kCoherent ? ld_dev_b128(src) : *src;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -112,17 +123,14 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // ------------------------------------------------------------------------------------
 // GEMM tiles
 // ------------------------------------------------------------------------------------
-// GEMM1 + SwiGLU for rows [0, rows) of A (already offset to the tile's first row) and
-// intermediate columns [n0, n0 + 128).  Writes H (and, when AB != null, the gate/up
-// pre-activations as [rows, 2I]: gate in [0, I), up in [I, 2I)).
-__device__ __forceinline__ void gemm1_tile(TileSmem& sm, const uint16_t* A, int64_t lda, int rows,
-                                           const uint16_t* wg_e, const uint16_t* wu_e, int n0,
-                                           int I, int D, uint16_t* H, int64_t ldh,
-                                           uint16_t* AB) {
-  TileSrc src;
-  tile_src_init(src, A, lda, rows, wg_e, wu_e, D, n0, n0, I);
-  TileAcc acc;
-  tile_gemm(sm, src, D, acc);
+// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) and intermediate columns
+// [n0, n0 + 128) of both W_gate (B rows 0..127) and W_up (B rows 128..255); the lane
+// holding a gate value holds the matching up value.  Writes H (and, when AB != null,
+// the gate/up pre-activations as [rows, 2I]: gate in [0, I), up in [I, 2I)).  With
+// kCoherent, H is written at device scope (handoff data of the fused kernel).
+template <bool kCoherent>
+__device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
+                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
   const int lane = threadIdx.x & 63;
   const int wn = (threadIdx.x >> 6) & 1;
 #pragma unroll
@@ -135,25 +143,24 @@ __device__ __forceinline__ void gemm1_tile(TileSmem& sm, const uint16_t* A, int6
         const int row = acc_row(i, v);
         if (row < rows && col < I) {
           const float g = acc.c[i][j][v], u = acc.c[i][j + 2][v];
-          H[int64_t(row) * ldh + col] = f32_to_bf16(silu_f(g) * u);
+          const uint16_t h = f32_to_bf16(silu_f(g) * u);
+          const int off = row * int(ldh) + col;  // < 2^31: row < 128, ldh <= 65536
+          if (kCoherent) st_dev_u16(H + off, h);
+          else H[off] = h;
           if (AB) {
-            AB[int64_t(row) * 2 * I + col] = f32_to_bf16(g);
-            AB[int64_t(row) * 2 * I + I + col] = f32_to_bf16(u);
+            AB[row * 2 * I + col] = f32_to_bf16(g);
+            AB[row * 2 * I + I + col] = f32_to_bf16(u);
           }
         }
       }
     }
 }
 
-// GEMM2 for rows [0, rows) of H and hidden columns [n0, n0 + 256); row r's result goes
-// to obuf row perm_rows[r] (its pair index).
-__device__ __forceinline__ void gemm2_tile(TileSmem& sm, const uint16_t* Hrows, int64_t ldh,
-                                           int rows, const uint16_t* wd_e, int n0, int D, int I,
-                                           const int32_t* perm_rows, uint16_t* obuf) {
-  TileSrc src;
-  tile_src_init(src, Hrows, ldh, rows, wd_e, wd_e, I, n0, n0 + 128, D);
-  TileAcc acc;
-  tile_gemm(sm, src, I, acc);
+// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256); row r's result is
+// pushed to obuf row perm_rows[r] (its pair index t*k + j).
+template <bool kCoherent>
+__device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
+                                            const int32_t* perm_rows, uint16_t* obuf) {
   const int lane = threadIdx.x & 63;
   const int wn = (threadIdx.x >> 6) & 1;
 #pragma unroll
@@ -170,9 +177,27 @@ __device__ __forceinline__ void gemm2_tile(TileSmem& sm, const uint16_t* Hrows, 
       if (col >= D) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (dst[v] >= 0) obuf[int64_t(dst[v]) * D + col] = f32_to_bf16(acc.c[i][j][v]);
+        if (dst[v] >= 0) {
+          uint16_t* o = obuf + int64_t(dst[v]) * D + col;
+          const uint16_t b = f32_to_bf16(acc.c[i][j][v]);
+          if (kCoherent) st_dev_u16(o, b);
+          else *o = b;
+        }
     }
   }
+}
+
+// Operands of one tile of either GEMM (one K loop serves both).
+//   GEMM1: A = dispatched rows [rows, D], B = W_gate/W_up rows n0.., K = D.
+//   GEMM2: A = hidden rows [rows, I], B = W_down rows n0..n0+255, K = I.
+template <bool kCoherent>
+__device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows,
+                                         const uint16_t* w0, const uint16_t* w1, int n0, int D,
+                                         int I, TileAcc& acc) {
+  TileSrc src;
+  if (gemm1) tile_src_init(src, A, D, rows, w0, w1, D, n0, n0, I);
+  else tile_src_init(src, A, I, rows, w0, w0, I, n0, n0 + 128, D);
+  tile_gemm<kCoherent>(src, gemm1 ? D : I, acc);
 }
 
 // ------------------------------------------------------------------------------------
@@ -184,11 +209,10 @@ __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
   const int nw = gridDim.x * 4;
   uint16_t* X = reinterpret_cast<uint16_t*>(p.P.full_x);
   for (int r = gw; r < R; r += nw)
-    wave_copy_row(X + int64_t(r) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+    wave_copy_row<false>(X + int64_t(r) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
 }
 
 __global__ __launch_bounds__(256) void k_gemm1_all(FwdParams p) {
-  __shared__ TileSmem sm;
   const int nt = blockIdx.x % p.nN1;
   const int f = blockIdx.x / p.nN1;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -197,14 +221,14 @@ __global__ __launch_bounds__(256) void k_gemm1_all(FwdParams p) {
   const uint16_t* X = reinterpret_cast<const uint16_t*>(p.P.full_x);
   uint16_t* H = reinterpret_cast<uint16_t*>(p.P.full_h);
   const int64_t wsz = int64_t(p.I) * p.D;
-  gemm1_tile(sm, X + int64_t(e.x) * p.D, p.D, e.y,
-             reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
-             reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.I, p.D,
-             H + int64_t(e.x) * p.I, p.I, nullptr);
+  TileAcc acc;
+  run_tile<false>(true, X + int64_t(e.x) * p.D, e.y,
+                  reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
+                  reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.D, p.I, acc);
+  epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, H + int64_t(e.x) * p.I, p.I, nullptr);
 }
 
 __global__ __launch_bounds__(256) void k_gemm2_all(FwdParams p) {
-  __shared__ TileSmem sm;
   const int nt = blockIdx.x % p.nN2;
   const int f = blockIdx.x / p.nN2;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -212,16 +236,18 @@ __global__ __launch_bounds__(256) void k_gemm2_all(FwdParams p) {
   const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
   const uint16_t* H = reinterpret_cast<const uint16_t*>(p.P.full_h);
   const int64_t wsz = int64_t(p.I) * p.D;
-  gemm2_tile(sm, H + int64_t(e.x) * p.I, p.I, e.y,
-             reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nt * kBN2, p.D, p.I,
-             p.P.perm + e.x, p.P.obuf);
+  TileAcc acc;
+  run_tile<false>(false, H + int64_t(e.x) * p.I, e.y,
+                  reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nullptr, nt * kBN2, p.D,
+                  p.I, acc);
+  epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
 }
 
 __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   for (int t = gw; t < p.T; t += nw) {
-    if (token_last_row(p.P.pos, t, p.k) >= 0) wave_combine_token(p, t);
+    if (token_last_row(p.P.pos, t, p.k) >= 0) wave_combine_token<false>(p, t);
     else wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
   }
 }
@@ -252,7 +278,7 @@ __device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uin
     const int lo = cm * p.M, hi = min(lo + p.M, R);
     for (int r = lo + gw; r < hi; r += nw) {
       const int t = p.P.perm[r] / p.k;
-      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token(p, t);
+      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
     }
   };
   auto mb_tiles2 = [&](int mb) { return uint32_t(p.P.mt_cnt[mb] * p.nN2); };
@@ -265,7 +291,8 @@ __device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uin
     uint16_t* slot_x = reinterpret_cast<uint16_t*>(p.P.ring + s * p.slot_bytes + p.slot_x);
     const int lo = mb * p.M, hi = min(lo + p.M, R);
     for (int r = lo + gw; r < hi; r += nw)
-      wave_copy_row(slot_x + int64_t(r - lo) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+      wave_copy_row<true>(slot_x + int64_t(r - lo) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D,
+                          p.D);
     wg_signal_add(ready + mb, 1);
     if (mb >= p.S) combine_mb(mb - p.S);
   }
@@ -275,7 +302,7 @@ __device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uin
   }
 }
 
-__device__ void compute_role(const FwdParams& p, TileSmem& sm, int C, uint32_t* ready,
+__device__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
                              uint32_t* done, uint32_t* hdone) {
   uint32_t* hdr = p.P.hdr;
   const uint32_t total = hdr[kHdrFwdTiles];
@@ -297,40 +324,43 @@ __device__ void compute_role(const FwdParams& p, TileSmem& sm, int C, uint32_t* 
     uint16_t* slot_x = reinterpret_cast<uint16_t*>(slot + p.slot_x);
     uint16_t* slot_h = reinterpret_cast<uint16_t*>(slot + p.slot_h);
     const int lo = mb * p.M;
-    if (q < nmt * p.nN1) {
-      const int i = q / p.nN1, nt = q % p.nN1;
+    const bool g1 = q < nmt * p.nN1;
+    const int qq = g1 ? q : q - nmt * p.nN1;
+    const int nn = g1 ? p.nN1 : p.nN2;
+    const int i = qq / nn, nt = qq % nn;
+    uint32_t* hd = hdone + int64_t(mb) * p.mt_max + i;
+    if (g1) {
       if (!wg_wait_geq(ready + mb, uint32_t(C), hdr)) break;
-      const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
-      const int r0 = e.x - lo;
+    } else {
+      if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr)) break;
+    }
+    const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+    const int r0 = e.x - lo;
+    const uint16_t* A = g1 ? slot_x + int64_t(r0) * p.D : slot_h + int64_t(r0) * p.I;
+    const uint16_t* w0 = reinterpret_cast<const uint16_t*>(g1 ? p.a.wg : p.a.wd) + e.z * wsz;
+    const uint16_t* w1 = reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz;
+    const int n0 = nt * (g1 ? kBN1 : kBN2);
+    TileAcc acc;
+    run_tile<true>(g1, A, e.y, w0, w1, n0, p.D, p.I, acc);
+    if (g1) {
       uint16_t* ab = p.save ? reinterpret_cast<uint16_t*>(slot + p.slot_ab) + int64_t(r0) * 2 * p.I
                             : nullptr;
-      gemm1_tile(sm, slot_x + int64_t(r0) * p.D, p.D, e.y,
-                 reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
-                 reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.I, p.D,
-                 slot_h + int64_t(r0) * p.I, p.I, ab);
-      wg_signal_add(hdone + int64_t(mb) * p.mt_max + i, 1);
+      epi_swiglu<true>(acc, e.y, n0, p.I, slot_h + int64_t(r0) * p.I, p.I, ab);
+      wg_signal_add(hd, 1);
     } else {
-      const int q2 = q - nmt * p.nN1;
-      const int i = q2 / p.nN2, nt = q2 % p.nN2;
-      if (!wg_wait_geq(hdone + int64_t(mb) * p.mt_max + i, uint32_t(p.nN1), hdr)) break;
-      const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
-      const int r0 = e.x - lo;
-      gemm2_tile(sm, slot_h + int64_t(r0) * p.I, p.I, e.y,
-                 reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nt * kBN2, p.D, p.I,
-                 p.P.perm + e.x, p.P.obuf);
+      epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
       wg_signal_add(done + mb, 1);
     }
   }
 }
 
 __global__ __launch_bounds__(256) void k_fwd_fused(FwdParams p) {
-  __shared__ TileSmem sm;
   uint32_t* ready = p.P.sync;
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
   const int C = p.a.comm_cus;
   if (int(blockIdx.x) < C) comm_role(p, blockIdx.x, C, ready, done);
-  else compute_role(p, sm, C, ready, done, hdone);
+  else compute_role(p, C, ready, done, hdone);
 }
 
 // ------------------------------------------------------------------------------------
