@@ -1,48 +1,59 @@
-// bf16 grouped-GEMM tile for gfx950: one workgroup (4 waves) computes a 128 x 256 fp32
-// tile C = A * B^T with A [rows, K] and B [256 rows, K] both K-contiguous, using
-// v_mfma_f32_32x32x16_bf16.  Each wave owns 64 rows x 128 columns (2 x 4 MFMA blocks).
+// bf16 grouped-GEMM tile for gfx950: one workgroup (8 waves, two per SIMD) computes a
+// 256 x 256 fp32 tile C = A * B^T with A [rows, K] and B [256 rows, K] both K-contiguous,
+// using v_mfma_f32_32x32x16_bf16.  Wave w owns rows 128 * (w / 4) .. +128 and B rows
+// 64 * (w % 4) .. +64 (4 x 2 MFMA blocks, 128 accumulator registers), which leaves room
+// for double-buffered fragments without spills, and the second wave per SIMD covers the
+// other's waits.
 //
-// The 256 B rows come from two 128-row halves (B0, B1) so the same tile serves
-//   GEMM1: B0 = W_gate rows, B1 = W_up rows of the same 128 intermediate columns
-//          (the SwiGLU epilogue pairs gate and up values held by the same lane);
+// The 256 B rows come from two matrices (B0, B1) so the same tile serves
+//   GEMM1: W_gate and W_up rows of the same 128 intermediate columns, paired per MFMA
+//          block (16 gate rows then the same 16 up rows), so the SwiGLU epilogue pairs
+//          each gate value with the up value one lane swap (l ^ 16) away;
 //   GEMM2: B0, B1 = two consecutive 128-row blocks of W_down.
 //
-// Global -> LDS uses gfx950's direct-to-LDS loads (global_load_lds_dwordx4) in a
-// three-stage ring: the loads of K step k+2 are issued while step k is multiplied, and
-// each step waits only for its own loads (explicit vmcnt, then a bare s_barrier, so the
-// later stages stay in flight).  A direct-to-LDS load writes 64 consecutive 16-byte
-// chunks per wave; each lane picks the global chunk that belongs at its LDS position.
-// LDS rows are 64 bf16 = 8 chunks and chunk c of row r sits at position c ^ (r & 7),
-// so the 32 rows read by one MFMA operand fetch spread over all banks.  The three
-// stages are separate LDS objects so the compiler can tell a stage being loaded from
-// a stage being read.
+// Data movement per K step of 64 (128 bytes per row, whole cache lines): 64 KB of A and
+// B move from global memory straight into LDS with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4) through a two-stage ring.  Measured on MI355X, the L2 -> CU
+// path delivers about 36 bytes per clock per CU for whole 128-byte row segments but
+// only about 23 for half lines, and the 256 x 256 tile needs 32 bytes per MFMA-cycle, so
+// whole-line steps and the largest tile the LDS holds are what bound this kernel.  Per
+// step each wave multiplies four 16-deep slices, reading the next slice's fragments
+// under the current slice's MFMAs; before the last slice it waits for the next step's
+// loads, meets the other waves at one barrier, starts the loads two steps ahead into
+// the stage just drained, and reads the next step's first fragments.  The loads are
+// inline asm: the compiler's wait-count pass cannot tell the stages apart and would
+// otherwise wait for every stage before each LDS read.
+//
+// LDS rows are 8 chunks of 16 bytes; chunk c of row r sits at position
+// c ^ (r & 7) ^ ((r >> 3) & 1).  The LDS has 64 four-byte banks, so a 128-byte row covers
+// half of them; one ds_read_b128 pass serves 16 lanes = 16 consecutive rows at one
+// logical chunk, which this swizzle spreads over all 64 banks.  Direct-to-LDS writes
+// are contiguous.
 //
 // Rows past the valid range are clamped to the last valid row (always in bounds);
-// their results are never stored.  With kCoherent the A operand is read with
-// device-scope (sc1) loads: the persistent kernel's A rows are written by workgroups on
-// other XCDs, whose L2s are not coherent with this one.
+// their results are never stored.  Byte offsets stay below 2^32: an A tile spans at
+// most 256 rows of at most 65536 bf16, and a weight matrix holds fewer than 2^31 bf16
+// (checked on the host).  With COH the A operand is read with
+// device-scope
+// (sc1) loads: in the persistent kernel the A rows are written by workgroups on other
+// XCDs, whose L2s are not coherent with this one.
 #pragma once
 #include "device.h"
+#include "tile_geom.h"
 
 namespace mok {
 
-constexpr int kStages = 3;
+constexpr int kStageChunks = kBM * 8;  // 16-byte chunks per operand per stage (32 KB)
+constexpr int kStageBytes = kStageChunks * 16;
 
-static __shared__ v4u g_lds_a0[kBM * 8], g_lds_a1[kBM * 8], g_lds_a2[kBM * 8];  // 3 x 16 KB
-static __shared__ v4u g_lds_b0[256 * 8], g_lds_b1[256 * 8], g_lds_b2[256 * 8];  // 3 x 32 KB
+static __shared__ v4u g_lds_a[2 * kStageChunks];  // two stages of A
+static __shared__ v4u g_lds_b[2 * kStageChunks];  // two stages of B
 
-// Stage arrays named at compile time (never through a runtime select), so every LDS
-// access carries the identity of its array.
-template <int S> __device__ __forceinline__ v4u* stage_a();
-template <int S> __device__ __forceinline__ v4u* stage_b();
-template <> __device__ __forceinline__ v4u* stage_a<0>() { return g_lds_a0; }
-template <> __device__ __forceinline__ v4u* stage_a<1>() { return g_lds_a1; }
-template <> __device__ __forceinline__ v4u* stage_a<2>() { return g_lds_a2; }
-template <> __device__ __forceinline__ v4u* stage_b<0>() { return g_lds_b0; }
-template <> __device__ __forceinline__ v4u* stage_b<1>() { return g_lds_b1; }
-template <> __device__ __forceinline__ v4u* stage_b<2>() { return g_lds_b2; }
+template <int S> __device__ __forceinline__ v4u* stage_a() { return g_lds_a + S * kStageChunks; }
+template <int S> __device__ __forceinline__ v4u* stage_b() { return g_lds_b + S * kStageChunks; }
 
-__device__ __forceinline__ int lds_chunk(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_chunk(int r, int c) { return r * 8 + (c ^ lds_swz(r)); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -50,20 +61,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<void*>(p))));
 }
 
-// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address
-// lds_wave_base + 16 * l (the base is wave-uniform and travels in M0).  Written as
-// inline asm so the compiler's wait-count pass, which cannot tell the three stages
-// apart, does not force every outstanding stage to land before each LDS read; the
-// tile's own vmcnt waits order the stages instead.  COHERENT adds the sc1 (device
-// scope) cache policy.
-template <bool COHERENT>
-__device__ __forceinline__ void dma16(const void* src, v4u* lds_wave_base) {
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource for byte offsets below 2^32 from `base` (wave-uniform).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
+  const uint64_t x = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(x)));
+  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(x >> 32) & 0xFFFFu));  // stride 0
+  r.z = -16;           // number of records (bytes): all offsets used here are far below
+  r.w = 0x00020000;    // raw buffer, 32-bit data
+  return r;
+}
+
+// Direct-to-LDS load of 16 bytes per lane from rsrc + voff + soff: lane l's bytes land
+// at LDS address lds_wave_base + 16 * l (the wave-uniform base travels in M0).  COH adds
+// sc1 (device scope).
+template <bool COH>
+__device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t voff, uint32_t soff,
+                                      const v4u* lds_wave_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  if (COHERENT)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src), "s"(m0)
+  if (COH)
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen sc1 lds" ::"v"(voff),
+                 "s"(rsrc), "s"(soff), "s"(m0)
                  : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
+                 "s"(rsrc), "s"(soff), "s"(m0)
                  : "memory", "m0");
 }
 
@@ -75,120 +99,187 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 struct TileAcc {
-  f32x16_t c[2][4];
+  f32x16_t c[4][2];
 };
 
-// Global source of this lane's chunk for each of its 4 A and 8 B direct-to-LDS loads.
+// Sources of this lane's 8 A and 8 B direct-to-LDS loads: one buffer resource per
+// operand (based at its first row / the weight matrix's first row) and a fixed,
+// non-negative per-lane byte offset (tile_geom.h); the K step travels in the scalar
+// offset.  Load p of wave w fills LDS positions [(4p + w) * 64, +64): rows
+// (4p + w) * 8 + l/8 at physical position l % 8, i.e. logical chunk (l % 8) ^
+// lds_swz(row), and for those rows lds_swz(row) = (l / 8) ^ (w % 2).  Which B matrix
+// a load reads depends on the B layout (geom::b_matrix): per load p for kSplit, per
+// wave for kPaired.
 struct TileSrc {
-  const uint16_t* pa[4];
-  const uint16_t* pb[8];
+  i32x4_t ra, rb0, rb1;
+  uint32_t oa[geom::kLoads], ob[geom::kLoads];
+  int layout;
 };
 
-// Load p of wave w fills LDS chunk positions [(4p + w) * 64, +64): rows (4p + w) * 8 + l/8,
-// physical chunk l % 8, i.e. logical chunk (l % 8) ^ (row % 8).
-__device__ __forceinline__ void tile_src_init(TileSrc& s, const uint16_t* A, int64_t lda,
-                                              int rows_valid, const uint16_t* B0,
+__device__ __forceinline__ void tile_src_init(TileSrc& s, int layout, const uint16_t* A,
+                                              int64_t lda, int rows_valid, const uint16_t* B0,
                                               const uint16_t* B1, int64_t ldb, int nb0, int nb1,
                                               int N) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = (l & 7) ^ ((l >> 3) & 7);
+  s.layout = layout;
+  s.ra = make_rsrc(A);
+  s.rb0 = make_rsrc(B0);
+  s.rb1 = make_rsrc(B1);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = min((p * 4 + w) * 8 + (l >> 3), rows_valid - 1);
-    s.pa[p] = A + int64_t(r) * lda + c * 8;
-  }
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int r = (p * 4 + w) * 8 + (l >> 3);
-    if (r < 128) {
-      s.pb[p] = B0 + int64_t(min(nb0 + r, N - 1)) * ldb + c * 8;
-    } else {
-      s.pb[p] = B1 + int64_t(min(nb1 + r - 128, N - 1)) * ldb + c * 8;
-    }
+  for (int p = 0; p < geom::kLoads; ++p) {
+    s.oa[p] = uint32_t(geom::a_offset(p, w, l, rows_valid, lda));
+    s.ob[p] = uint32_t(geom::b_offset(layout, p, w, l, nb0, nb1, N, ldb));
   }
 }
 
-template <bool COH_A, int STAGE>
+template <bool COH, int STAGE>
 __device__ __forceinline__ void tile_issue(const TileSrc& s, int k0) {
-  const int w = threadIdx.x >> 6;
-  v4u* a = stage_a<STAGE>();
-  v4u* b = stage_b<STAGE>();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const uint32_t kb = uint32_t(k0) * 2;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) dma16<COH_A>(s.pa[p] + k0, a + (p * 4 + w) * 64);
+  for (int p = 0; p < geom::kLoads; ++p)
+    dma16<COH>(s.ra, s.oa[p], kb, stage_a<STAGE>() + (p * 8 + w) * 64);
+  const bool paired_up = s.layout == geom::kPaired && ((w >> 1) & 1);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) dma16<false>(s.pb[p] + k0, b + (p * 4 + w) * 64);
+  for (int p = 0; p < geom::kLoads; ++p) {
+    const bool use_b1 = s.layout == geom::kPaired ? paired_up : (p >= 2);
+    dma16<false>(use_b1 ? s.rb1 : s.rb0, s.ob[p], kb, stage_b<STAGE>() + (p * 8 + w) * 64);
+  }
 }
 
-// B row (within the 256-row tile) of MFMA block j for wave column wn.
-__device__ __forceinline__ int brow_of(int j, int wn) {
-  return (j < 2) ? (wn * 64 + j * 32) : (128 + wn * 64 + (j - 2) * 32);
-}
+// B row (within the 256-row tile) of MFMA block j (0..1) of wave column wn (0..3).
+__device__ __forceinline__ int brow_of(int j, int wn) { return wn * 64 + j * 32; }
 
-template <int STAGE>
-__device__ __forceinline__ void tile_compute(TileAcc& acc) {
-  const v4u* sa = stage_a<STAGE>();
-  const v4u* sb = stage_b<STAGE>();
+struct TileFrag {
+  v4u a[4], b[2];
+};
+
+typedef __attribute__((address_space(3))) const v4u lds_cv4u;
+
+// Per-lane LDS byte addresses of the fragment reads of slice ks in stage 0: A rows
+// 128 * wm + r32 (+32 i), B rows 64 * wn + r32 (+32 j), chunk (2 ks + l/32) swizzled.
+// The swizzle only depends on r32, so block and stage offsets are immediates.
+struct FragAddr {
+  uint32_t a[4], b[4];
+};
+
+__device__ __forceinline__ void frag_addr_init(FragAddr& fa) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   const int r32 = lane & 31;
+  const int sw = lds_swz(r32);
+  const uint32_t a0 = lds_addr(g_lds_a) + uint32_t(wm * 128 + r32) * 128;
+  const uint32_t b0 = lds_addr(g_lds_b) + uint32_t(wn * 64 + r32) * 128;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int c = ks * 2 + (lane >> 5);
-    v4u a[2], b[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = sa[lds_chunk(wm * 64 + i * 32 + r32, c)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = sb[lds_chunk(brow_of(j, wn) + r32, c)];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc.c[i][j] = mfma32x32x16(a[i], b[j], acc.c[i][j]);
+    const uint32_t ch = uint32_t(((ks * 2 + (lane >> 5)) ^ sw) * 16);
+    fa.a[ks] = a0 + ch;
+    fa.b[ks] = b0 + ch;
   }
 }
 
-// One K step: wait for this step's loads (the next step's may stay in flight), meet,
-// start the loads two steps ahead into the stage freed by the previous step, multiply.
-template <bool COH_A, int CS, int IS>
-__device__ __forceinline__ void tile_step(const TileSrc& src, int kb, int nk, TileAcc& acc) {
-  if (kb + 1 < nk) wait_vmcnt<12>();
-  else wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  if (kb + 2 < nk) tile_issue<COH_A, IS>(src, (kb + 2) * kBK);
-  tile_compute<CS>(acc);
+// Fragments of slice ks (16 deep) of stage S.
+template <int S>
+__device__ __forceinline__ void frag_load(TileFrag& f, const FragAddr& fa, int ks) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<lds_cv4u*>(uintptr_t(fa.a[ks] + S * kStageBytes + i * 32 * 128));
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    f.b[j] = *reinterpret_cast<lds_cv4u*>(uintptr_t(fa.b[ks] + S * kStageBytes + j * 32 * 128));
+}
+
+__device__ __forceinline__ void frag_mma(const TileFrag& f, TileAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc.c[i][j] = mfma32x32x16(f.a[i], f.b[j], acc.c[i][j]);
+}
+
+// One K step kb held in stage S (S = kb % 2).  On entry f0 holds slice 0 of step kb.
+template <bool COH, int S>
+__device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa, int kb, int nk,
+                                          TileFrag& f0, TileFrag& f1, TileAcc& acc) {
+  constexpr int SN = S ^ 1;
+  frag_load<S>(f1, fa, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_load<S>(f0, fa, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_load<S>(f1, fa, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kb + 1 < nk) {
+    // step kb+1 (the only loads in flight) must have landed: mine by vmcnt, everyone's
+    // by the barrier, which also tells that every wave has read all of stage S.
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + 2 < nk) tile_issue<COH, S>(src, (kb + 2) * kBK);
+    frag_load<SN>(f0, fa, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f1, acc);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Full K loop (K a multiple of kBK).  Ends with a barrier, so the stages may be
 // reused as soon as it returns.
-template <bool kCoherent>
+template <bool COH>
 __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& acc) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
   const int nk = K / kBK;
   asm volatile("" ::: "memory");
-  tile_issue<kCoherent, 0>(src, 0);
-  if (nk > 1) tile_issue<kCoherent, 1>(src, kBK);
-  for (int kb = 0; kb < nk; kb += 3) {
-    tile_step<kCoherent, 0, 2>(src, kb, nk, acc);
-    if (kb + 1 < nk) tile_step<kCoherent, 1, 0>(src, kb + 1, nk, acc);
-    if (kb + 2 < nk) tile_step<kCoherent, 2, 1>(src, kb + 2, nk, acc);
+  tile_issue<COH, 0>(src, 0);
+  if (nk > 1) {
+    tile_issue<COH, 1>(src, kBK);
+    wait_vmcnt<2 * geom::kLoads>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  FragAddr fa;
+  frag_addr_init(fa);
+  TileFrag f0, f1;
+  frag_load<0>(f0, fa, 0);
+  for (int kb = 0; kb < nk; kb += 2) {
+    tile_step<COH, 0>(src, fa, kb, nk, f0, f1, acc);
+    if (kb + 1 < nk) tile_step<COH, 1>(src, fa, kb + 1, nk, f0, f1, acc);
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Row (within the 128-row tile) held by accumulator element v of block i for this lane.
-__device__ __forceinline__ int acc_row(int i, int v) {
-  const int lane = threadIdx.x & 63;
-  const int wm = (threadIdx.x >> 6) >> 1;
-  return wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+// A value the compiler must treat as produced here: epilogue address arithmetic derived
+// from it cannot be hoisted above the K loop, where it would hold registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// Row (within the 256-row tile) held by accumulator element v of block i for a lane
+// with index tid in the workgroup.
+__device__ __forceinline__ int acc_row(int tid, int i, int v) {
+  const int lane = tid & 63;
+  const int wm = (tid >> 6) >> 2;
+  return wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// silu(a) = a / (1 + e^-a), with the hardware exponential and reciprocal (about 1 ulp
+// each; H is rounded to bf16 or e4m3 right after).
+__device__ __forceinline__ float silu_f(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 }  // namespace mok

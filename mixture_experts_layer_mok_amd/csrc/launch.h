@@ -17,6 +17,7 @@ struct Ptrs {
   int4* mt_tab;       // [n_mb_max][mt_max] = (first row, rows, local expert, 0)
   int32_t* mt_cnt;    // [n_mb_max]
   int32_t* tile_base; // [n_mb_max + 1]
+  int32_t* mb_start;  // [n_mb_max + 1]: first row of each minibatch; [n_mb] = R
   uint32_t* sync;     // device counters
   uint16_t* obuf;     // [T*k, D] bf16: expert output of pair t*k + j
   uint8_t* ring;      // S slots
@@ -41,6 +42,7 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.mt_tab = reinterpret_cast<int4*>(b + L.off_mt_tab);
   P.mt_cnt = reinterpret_cast<int32_t*>(b + L.off_mt_cnt);
   P.tile_base = reinterpret_cast<int32_t*>(b + L.off_tile_base);
+  P.mb_start = reinterpret_cast<int32_t*>(b + L.off_mb_start);
   P.sync = reinterpret_cast<uint32_t*>(b + L.off_sync);
   P.obuf = reinterpret_cast<uint16_t*>(b + L.off_obuf);
   P.ring = b + L.off_ring;

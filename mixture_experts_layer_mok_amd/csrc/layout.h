@@ -14,11 +14,11 @@
 namespace mok {
 
 // GEMM tiling shared by every grouped-GEMM kernel.
-constexpr int kBM = 128;       // rows per m-tile
+constexpr int kBM = 256;       // rows per m-tile (m-tiles start at expert offsets)
 constexpr int kBN1 = 128;      // intermediate columns per GEMM1 tile (gate and up each)
 constexpr int kBN2 = 256;      // hidden columns per GEMM2 tile
-constexpr int kBK = 64;        // K step (bf16 elements)
-constexpr int kThreads = 256;  // threads per workgroup (4 waves of 64)
+constexpr int kBK = 64;        // K step (bf16 elements, 128 bytes per row)
+constexpr int kThreads = 512;  // threads per GEMM workgroup (8 waves of 64)
 
 // Schedule kernels.
 constexpr int kSchedChunk = 4096;  // pairs per counting block (4 waves x 1024)
@@ -52,7 +52,8 @@ struct Layout {
   bool mx, save, unfused;
   // byte offsets into the workspace
   size_t off_hdr, off_counts, off_offsets, off_blk, off_perm, off_pos, off_mt_tab, off_mt_cnt,
-      off_tile_base, off_sync, sync_bytes, off_obuf, off_ring, slot_bytes;
+      off_tile_base, off_mb_start, off_sync, sync_bytes, off_obuf, off_ring, slot_bytes;
+  int64_t slot_rows;  // rows one slot holds: a minibatch's tiles may run past its window
   size_t slot_x, slot_xs, slot_h, slot_hs, slot_ab;  // offsets inside one slot
   size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
   // backward
@@ -73,6 +74,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   if (nl < 1 || nl > kMaxLocalExperts || e0 < 0 || e0 + nl > E) return MOK_E_SHAPE;
   if (M < 1 || M > (1 << 20) || S < 1 || S > 64) return MOK_E_SHAPE;
   if (T * k > (int64_t(1) << 24)) return MOK_E_SHAPE;
+  if (D * I >= (int64_t(1) << 31)) return MOK_E_SHAPE;  // a weight matrix in 32-bit offsets
   if (d->comm_cus < 1) return MOK_E_SHAPE;
   if (d->precision != MOK_PREC_BF16 && d->precision != MOK_PREC_MXFP8) return MOK_E_UNSUPPORTED;
   if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED)) return MOK_E_UNSUPPORTED;
@@ -85,8 +87,12 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
   L->NS = L->NB * (kSchedChunk / kSchedSub);
   L->n_mb_max = (L->TK + M - 1) / M;
-  L->mt_max = (M + kBM - 1) / kBM + nl;
+  // m-tiles start at expert offsets and every kBM rows after; a minibatch holds the
+  // m-tiles whose first row lies in its window [i*M, (i+1)*M): at most M/kBM + 1 per
+  // expert segment it touches.
+  L->mt_max = (M + kBM - 1) / kBM + nl + 1;
   if (L->mt_max > L->TK / kBM + 1 + nl) L->mt_max = L->TK / kBM + 1 + nl;
+  L->slot_rows = M + kBM;
   L->nN1 = (I + kBN1 - 1) / kBN1;
   L->nN2 = (D + kBN2 - 1) / kBN2;
 
@@ -101,6 +107,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->off_mt_tab = o; o = align_up(o + L->n_mb_max * L->mt_max * 16, A);
   L->off_mt_cnt = o; o = align_up(o + L->n_mb_max * 4, A);
   L->off_tile_base = o; o = align_up(o + (L->n_mb_max + 1) * 4, A);
+  L->off_mb_start = o; o = align_up(o + (L->n_mb_max + 1) * 4, A);
   // forward counters: ready[n_mb], done[n_mb], hdone[n_mb * mt_max];
   // backward counters: bready[n_mb], bdone[n_mb], hd[n_mb*mt_max], dxd[n_mb*mt_max],
   // wdone[n_mb * nl * 3]
@@ -111,11 +118,12 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->off_obuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
   // one ring slot
   size_t so = 0;
-  L->slot_x = so; so = align_up(so + size_t(M) * D * (L->mx ? 1 : 2), A);
-  L->slot_xs = so; so = align_up(so + (L->mx ? size_t(M) * (D / 32) : 0), A);
-  L->slot_h = so; so = align_up(so + size_t(M) * I * (L->mx ? 1 : 2), A);
-  L->slot_hs = so; so = align_up(so + (L->mx ? size_t(M) * (I / 32) : 0), A);
-  L->slot_ab = so; so = align_up(so + (L->save ? size_t(M) * 2 * I * 2 : 0), A);
+  const size_t SR = size_t(L->slot_rows);
+  L->slot_x = so; so = align_up(so + SR * D * (L->mx ? 1 : 2), A);
+  L->slot_xs = so; so = align_up(so + (L->mx ? SR * (D / 32) : 0), A);
+  L->slot_h = so; so = align_up(so + SR * I * (L->mx ? 1 : 2), A);
+  L->slot_hs = so; so = align_up(so + (L->mx ? SR * (I / 32) : 0), A);
+  L->slot_ab = so; so = align_up(so + (L->save ? SR * 2 * I * 2 : 0), A);
   L->slot_bytes = so;
   L->off_ring = o; o = align_up(o + L->slot_bytes * S, A);
   // full-size buffers for the unfused path
@@ -133,8 +141,8 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_dxbuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
     L->off_dgpart = o; o = align_up(o + size_t(L->TK) * L->nN1 * 4, A);
     size_t bo = 0;
-    L->bslot_dy = bo; bo = align_up(bo + size_t(M) * D * 2, A);
-    L->bslot_dab = bo; bo = align_up(bo + size_t(M) * 2 * I * 2, A);
+    L->bslot_dy = bo; bo = align_up(bo + SR * D * 2, A);
+    L->bslot_dab = bo; bo = align_up(bo + SR * 2 * I * 2, A);
     L->bslot_bytes = bo;
     L->off_bring = o; o = align_up(o + L->bslot_bytes * S, A);
   }

@@ -123,56 +123,63 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // ------------------------------------------------------------------------------------
 // GEMM tiles
 // ------------------------------------------------------------------------------------
-// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) and intermediate columns
-// [n0, n0 + 128) of both W_gate (B rows 0..127) and W_up (B rows 128..255); the lane
-// holding a gate value holds the matching up value.  Writes H (and, when AB != null,
-// the gate/up pre-activations as [rows, 2I]: gate in [0, I), up in [I, 2I)).  With
-// kCoherent, H is written at device scope (handoff data of the fused kernel).
+// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
+// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
+// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
+// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
+// Writes H (and, when AB != null, the gate/up pre-activations as [rows, 2I]: gate in
+// [0, I), up in [I, 2I)).  With kCoherent, H is written at device scope (handoff data of
+// the fused kernel).
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
                                            uint16_t* H, int64_t ldh, uint16_t* AB) {
-  const int lane = threadIdx.x & 63;
-  const int wn = (threadIdx.x >> 6) & 1;
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+  const bool gate_lane = (lane & 16) == 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      const int col = n0 + (brow_of(j, wn) >> 5) * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = acc_row(i, v);
+        const float x = acc.c[i][j][v];
+        const float y = __shfl_xor(x, 16);
+        const int row = acc_row(tid, i, v);
         if (row < rows && col < I) {
-          const float g = acc.c[i][j][v], u = acc.c[i][j + 2][v];
-          const uint16_t h = f32_to_bf16(silu_f(g) * u);
-          const int off = row * int(ldh) + col;  // < 2^31: row < 128, ldh <= 65536
-          if (kCoherent) st_dev_u16(H + off, h);
-          else H[off] = h;
-          if (AB) {
-            AB[row * 2 * I + col] = f32_to_bf16(g);
-            AB[row * 2 * I + I + col] = f32_to_bf16(u);
+          if (gate_lane) {
+            const uint16_t h = f32_to_bf16(silu_f(x) * y);
+            const int off = row * int(ldh) + col;  // < 2^31: row < 256, ldh <= 65536
+            if (kCoherent) st_dev_u16(H + off, h);
+            else H[off] = h;
           }
+          if (AB) AB[row * 2 * I + (gate_lane ? col : I + col)] = f32_to_bf16(x);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // one block at a time: few live registers
     }
 }
 
-// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256); row r's result is
+// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256) (B tile row b is
+// hidden column n0 + b in the split layout); row r's result is
 // pushed to obuf row perm_rows[r] (its pair index t*k + j).
 template <bool kCoherent>
 __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
                                             const int32_t* perm_rows, uint16_t* obuf) {
-  const int lane = threadIdx.x & 63;
-  const int wn = (threadIdx.x >> 6) & 1;
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     int dst[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = acc_row(i, v);
+      const int row = acc_row(tid, i, v);
       dst[v] = row < rows ? perm_rows[row] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int col = n0 + brow_of(j, wn) + (lane & 31);
       if (col >= D) continue;
 #pragma unroll
@@ -183,6 +190,7 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
           if (kCoherent) st_dev_u16(o, b);
           else *o = b;
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -195,8 +203,8 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
                                          const uint16_t* w0, const uint16_t* w1, int n0, int D,
                                          int I, TileAcc& acc) {
   TileSrc src;
-  if (gemm1) tile_src_init(src, A, D, rows, w0, w1, D, n0, n0, I);
-  else tile_src_init(src, A, I, rows, w0, w0, I, n0, n0 + 128, D);
+  if (gemm1) tile_src_init(src, geom::kPaired, A, D, rows, w0, w1, D, n0, n0, I);
+  else tile_src_init(src, geom::kSplit, A, I, rows, w0, w0, I, n0, n0 + 128, D);
   tile_gemm<kCoherent>(src, gemm1 ? D : I, acc);
 }
 
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
     wave_copy_row<false>(X + int64_t(r) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
 }
 
-__global__ __launch_bounds__(256) void k_gemm1_all(FwdParams p) {
+__global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
   const int nt = blockIdx.x % p.nN1;
   const int f = blockIdx.x / p.nN1;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(256) void k_gemm1_all(FwdParams p) {
   epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, H + int64_t(e.x) * p.I, p.I, nullptr);
 }
 
-__global__ __launch_bounds__(256) void k_gemm2_all(FwdParams p) {
+__global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
   const int nt = blockIdx.x % p.nN2;
   const int f = blockIdx.x / p.nN2;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -264,18 +272,17 @@ __global__ __launch_bounds__(256) void k_fwd_prep(FwdParams p) {
   }
 }
 
-__device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uint32_t* done) {
+__device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uint32_t* done) {
   uint32_t* hdr = p.P.hdr;
-  const int R = int(hdr[kHdrR]);
   const int n_mb = int(hdr[kHdrNmb]);
   const int w = threadIdx.x >> 6;
-  const int gw = c * 4 + w, nw = C * 4;
+  const int gw = c * (kThreads / 64) + w, nw = C * (kThreads / 64);
   // tokens without a local slot: y = 0
   for (int t = gw; t < p.T; t += nw)
     if (token_last_row(p.P.pos, t, p.k) < 0) wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
 
   auto combine_mb = [&](int cm) {
-    const int lo = cm * p.M, hi = min(lo + p.M, R);
+    const int lo = p.P.mb_start[cm], hi = p.P.mb_start[cm + 1];
     for (int r = lo + gw; r < hi; r += nw) {
       const int t = p.P.perm[r] / p.k;
       if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
@@ -289,7 +296,7 @@ __device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uin
       if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr)) return;
     }
     uint16_t* slot_x = reinterpret_cast<uint16_t*>(p.P.ring + s * p.slot_bytes + p.slot_x);
-    const int lo = mb * p.M, hi = min(lo + p.M, R);
+    const int lo = p.P.mb_start[mb], hi = p.P.mb_start[mb + 1];
     for (int r = lo + gw; r < hi; r += nw)
       wave_copy_row<true>(slot_x + int64_t(r - lo) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D,
                           p.D);
@@ -302,7 +309,7 @@ __device__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uin
   }
 }
 
-__device__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
+__device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
                              uint32_t* done, uint32_t* hdone) {
   uint32_t* hdr = p.P.hdr;
   const uint32_t total = hdr[kHdrFwdTiles];
@@ -323,7 +330,7 @@ __device__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
     uint8_t* slot = p.P.ring + s * p.slot_bytes;
     uint16_t* slot_x = reinterpret_cast<uint16_t*>(slot + p.slot_x);
     uint16_t* slot_h = reinterpret_cast<uint16_t*>(slot + p.slot_h);
-    const int lo = mb * p.M;
+    const int lo = p.P.mb_start[mb];
     const bool g1 = q < nmt * p.nN1;
     const int qq = g1 ? q : q - nmt * p.nN1;
     const int nn = g1 ? p.nN1 : p.nN2;
@@ -354,7 +361,7 @@ __device__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
   }
 }
 
-__global__ __launch_bounds__(256) void k_fwd_fused(FwdParams p) {
+__global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   uint32_t* ready = p.P.sync;
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
@@ -383,7 +390,7 @@ int fused_grid_size() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k_fwd_fused),
-                                                   256, 0) != hipSuccess)
+                                                   kThreads, 0) != hipSuccess)
     return 0;
   return cus * occ;
 }
@@ -393,10 +400,10 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
   if (L.unfused) {
     const unsigned gw = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
     hipLaunchKernelGGL(k_gather_all, dim3(gw), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_gemm1_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN1)), dim3(256), 0,
-                       st, p);
-    hipLaunchKernelGGL(k_gemm2_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN2)), dim3(256), 0,
-                       st, p);
+    hipLaunchKernelGGL(k_gemm1_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN1)), dim3(kThreads),
+                       0, st, p);
+    hipLaunchKernelGGL(k_gemm2_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN2)), dim3(kThreads),
+                       0, st, p);
     hipLaunchKernelGGL(k_combine_all, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
                        dim3(256), 0, st, p);
     return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
@@ -407,8 +414,8 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
   hipLaunchKernelGGL(k_fwd_prep, dim3(64), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return MOK_E_LAUNCH;
   void* args[] = {&p};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_fused), dim3(grid), dim3(256),
-                                 args, 0, st) != hipSuccess)
+  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_fused), dim3(grid),
+                                 dim3(kThreads), args, 0, st) != hipSuccess)
     return MOK_E_LAUNCH;
   return MOK_OK;
 }

@@ -104,27 +104,37 @@ __global__ __launch_bounds__(1024) void sched_scan(Ptrs P, int64_t NS, int nl, i
     const int e = int(idx % nl);
     P.blk[s * (nl + 1) + e] += s_off[e];
   }
-  // m-tile table: the expert segments of each minibatch window cut into <= kBM rows
+  // m-tile table.  Expert e's rows are cut into m-tiles [off_e + kBM*q, +kBM) (the last
+  // one may be short); minibatch mb holds the m-tiles whose first row lies in its
+  // window [mb*M, (mb+1)*M), so it covers rows [mb_start[mb], mb_start[mb+1]) and may
+  // run up to kBM-1 rows past its window.  mb_start[n_mb] = R.
   for (int mb = tid; mb < n_mb; mb += 1024) {
     const int32_t lo = mb * M;
     const int32_t hi = min(lo + M, R);
-    // first expert whose rows reach past lo
+    // expert whose rows contain lo
     int e_lo = 0, e_hi = nl - 1;
     while (e_lo < e_hi) {
       const int mid = (e_lo + e_hi) >> 1;
       if (s_off[mid + 1] <= lo) e_lo = mid + 1; else e_hi = mid;
     }
+    int e = e_lo;
+    int32_t t = s_off[e] + ((lo - s_off[e] + kBM - 1) / kBM) * kBM;  // first tile start >= lo
+    if (t >= s_off[e + 1]) {
+      t = s_off[e + 1];
+      ++e;
+    }
+    P.mb_start[mb] = t;
     int cnt = 0;
-    for (int e = e_lo; e < nl && s_off[e] < hi; ++e) {
-      const int32_t a = max(lo, s_off[e]);
-      const int32_t b = min(hi, s_off[e + 1]);
-      for (int32_t r = a; r < b; r += kBM) {
-        P.mt_tab[int64_t(mb) * mt_max + cnt] = make_int4(r, min(kBM, b - r), e, 0);
-        ++cnt;
-      }
+    while (t < hi) {
+      while (e < nl && s_off[e + 1] <= t) ++e;  // skip finished and empty experts
+      const int32_t rows = min(kBM, s_off[e + 1] - t);
+      P.mt_tab[int64_t(mb) * mt_max + cnt] = make_int4(t, rows, e, 0);
+      ++cnt;
+      t += rows;
     }
     P.mt_cnt[mb] = cnt;
   }
+  if (tid == 0) P.mb_start[n_mb] = R;
   __syncthreads();
   __threadfence_block();
   // tile_base: prefix over minibatches of m-tiles * (nN1 + nN2); total m-tiles
