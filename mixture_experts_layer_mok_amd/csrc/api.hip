@@ -109,8 +109,21 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
   mok_status_t s = make_layout(desc, &L);
   if (s != MOK_OK) return s;
   if ((s = check_ws(L, ws, ws_bytes)) != MOK_OK) return s;
-  (void)stream;
-  return MOK_E_UNSUPPORTED;
+  if (!L.save || L.mx) return MOK_E_UNSUPPORTED;  // needs a bf16 forward that saved
+  BwdArgs a;
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = topk_ids;
+  a.gates = topk_w;
+  a.wg = static_cast<const uint16_t*>(w_gate);
+  a.wu = static_cast<const uint16_t*>(w_up);
+  a.wd = static_cast<const uint16_t*>(w_down);
+  a.dx = static_cast<uint16_t*>(dx);
+  a.dg = d_topk_w;
+  a.dwg = dw_gate;
+  a.dwu = dw_up;
+  a.dwd = dw_down;
+  return launch_backward(L, make_ptrs(L, ws), a, static_cast<hipStream_t>(stream));
 }
 
 mok_status_t mok_read_device_status(const void* ws, void* stream, uint32_t* out) {

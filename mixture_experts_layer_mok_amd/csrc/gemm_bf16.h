@@ -239,6 +239,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
   const int nk = K / kBK;
+  if (nk == 0) return;  // empty contraction: the tile is zero
   asm volatile("" ::: "memory");
   tile_issue<COH, 0>(src, 0);
   if (nk > 1) {

@@ -25,9 +25,21 @@ struct Ptrs {
   uint8_t* full_xs;   // unfused MX scales
   uint8_t* full_h;    // unfused: [T*k, I] hidden rows
   uint8_t* full_hs;
-  uint16_t* dxbuf;    // backward: [T*k, D] bf16 per-pair dX contributions
-  float* dgpart;      // backward: [T*k, nN1] partial router-weight gradients
-  uint8_t* bring;     // backward slots
+  // backward
+  uint16_t* bx;       // [T*k, D] dispatched X rows
+  uint16_t* bdy;      // [T*k, D] dispatched dY rows
+  uint16_t* bab;      // [T*k, 2I] gate / up pre-activations
+  uint16_t* bdab;     // [T*k, 2I] their gradients
+  uint16_t* dxbuf;    // [T*k, D] per-pair dX contributions (pair-indexed)
+  float* dgpart;      // [T*k, nNdh] router-weight gradient partials per dH n-tile
+  uint16_t* wdt;      // [E_loc, I, D] W_down transposed
+  uint16_t* wgut;     // [E_loc, D, 2I] [W_gate | W_up] transposed
+  uint16_t* xt;       // [D, TKP] panels of X columns per expert
+  uint16_t* gdyt;     // [D, TKP] panels of gate * dY
+  uint16_t* ht;       // [I, TKP] panels of h
+  uint16_t* dat;      // [I, TKP] panels of dL/da
+  uint16_t* dbt;      // [I, TKP] panels of dL/db
+  int32_t* roff;      // [E_loc + 1] first panel column of each expert
 };
 
 inline Ptrs make_ptrs(const Layout& L, void* ws) {
@@ -50,9 +62,21 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.full_xs = L.unfused ? b + L.off_full_xs : nullptr;
   P.full_h = L.unfused ? b + L.off_full_h : nullptr;
   P.full_hs = L.unfused ? b + L.off_full_hs : nullptr;
-  P.dxbuf = L.save ? reinterpret_cast<uint16_t*>(b + L.off_dxbuf) : nullptr;
+  auto u16 = [&](size_t off) { return L.save ? reinterpret_cast<uint16_t*>(b + off) : nullptr; };
+  P.bx = u16(L.off_bx);
+  P.bdy = u16(L.off_bdy);
+  P.bab = u16(L.off_bab);
+  P.bdab = u16(L.off_bdab);
+  P.dxbuf = u16(L.off_dxbuf);
   P.dgpart = L.save ? reinterpret_cast<float*>(b + L.off_dgpart) : nullptr;
-  P.bring = L.save ? b + L.off_bring : nullptr;
+  P.wdt = u16(L.off_wdt);
+  P.wgut = u16(L.off_wgut);
+  P.xt = u16(L.off_xt);
+  P.gdyt = u16(L.off_gdyt);
+  P.ht = u16(L.off_ht);
+  P.dat = u16(L.off_dat);
+  P.dbt = u16(L.off_dbt);
+  P.roff = L.save ? reinterpret_cast<int32_t*>(b + L.off_roff) : nullptr;
   return P;
 }
 
@@ -73,6 +97,23 @@ struct FwdArgs {
 
 mok_status_t launch_schedule(const Layout& L, const Ptrs& P, const int32_t* ids, hipStream_t st);
 mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st);
+
+// Layer inputs and outputs of one backward call.
+struct BwdArgs {
+  const uint16_t* dy;
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* gates;
+  const uint16_t* wg;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  uint16_t* dx;
+  float* dg;
+  float* dwg;
+  float* dwu;
+  float* dwd;
+};
+mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, hipStream_t st);
 mok_status_t launch_quantize_mx(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
                                 uint8_t* scales, hipStream_t st);
 

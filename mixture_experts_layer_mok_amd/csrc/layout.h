@@ -56,8 +56,11 @@ struct Layout {
   int64_t slot_rows;  // rows one slot holds: a minibatch's tiles may run past its window
   size_t slot_x, slot_xs, slot_h, slot_hs, slot_ab;  // offsets inside one slot
   size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
-  // backward
-  size_t off_bwd, off_dxbuf, off_dgpart, bslot_bytes, bslot_dy, bslot_dab, off_bring;
+  // backward (present with MOK_FLAG_SAVE_FOR_BWD)
+  int64_t TKP;      // width of the transposed per-expert panels: T*k + 64*E_loc
+  int64_t nNdh;     // n-tiles of the dH GEMM (over I)
+  size_t off_bx, off_bdy, off_bab, off_bdab, off_dxbuf, off_dgpart, off_wdt, off_wgut, off_xt,
+      off_gdyt, off_ht, off_dat, off_dbt, off_roff;
   size_t total;
 };
 
@@ -134,17 +137,33 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_full_h = o; o = align_up(o + size_t(L->TK) * I * (L->mx ? 1 : 2), A);
     L->off_full_hs = o; o = align_up(o + (L->mx ? size_t(L->TK) * (I / 32) : 0), A);
   }
-  // backward regions (present when the forward saves for backward)
-  L->off_bwd = L->off_dxbuf = L->off_dgpart = L->off_bring = 0;
-  L->bslot_bytes = L->bslot_dy = L->bslot_dab = 0;
+  // backward regions (present when the forward saves for backward).  Row buffers are
+  // indexed by routed row (at most T*k rows); the transposed panels hold, per local
+  // expert, its rows as columns, padded with zeros to a multiple of 64.
+  L->TKP = align_up(size_t(L->TK), 64) + 64 * nl;
+  L->nNdh = (I + kBN2 - 1) / kBN2;
+  L->off_bx = L->off_bdy = L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = 0;
+  L->off_wdt = L->off_wgut = L->off_xt = L->off_gdyt = L->off_ht = L->off_dat = L->off_dbt = 0;
+  L->off_roff = 0;
   if (L->save) {
-    L->off_dxbuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
-    L->off_dgpart = o; o = align_up(o + size_t(L->TK) * L->nN1 * 4, A);
-    size_t bo = 0;
-    L->bslot_dy = bo; bo = align_up(bo + SR * D * 2, A);
-    L->bslot_dab = bo; bo = align_up(bo + SR * 2 * I * 2, A);
-    L->bslot_bytes = bo;
-    L->off_bring = o; o = align_up(o + L->bslot_bytes * S, A);
+    // panel and transposed-weight offsets of the backward GEMM tiles stay below 2^32 bytes
+    if ((D > I ? D : I) * L->TKP >= (int64_t(1) << 31) || 2 * I * D >= (int64_t(1) << 31))
+      return MOK_E_SHAPE;
+    const size_t TK = size_t(L->TK), TKP = size_t(L->TKP);
+    L->off_bx = o; o = align_up(o + TK * D * 2, A);
+    L->off_bdy = o; o = align_up(o + TK * D * 2, A);
+    L->off_bab = o; o = align_up(o + TK * 2 * I * 2, A);
+    L->off_bdab = o; o = align_up(o + TK * 2 * I * 2, A);
+    L->off_dxbuf = o; o = align_up(o + TK * D * 2, A);
+    L->off_dgpart = o; o = align_up(o + TK * L->nNdh * 4, A);
+    L->off_wdt = o; o = align_up(o + size_t(nl) * I * D * 2, A);
+    L->off_wgut = o; o = align_up(o + size_t(nl) * D * 2 * I * 2, A);
+    L->off_xt = o; o = align_up(o + size_t(D) * TKP * 2, A);
+    L->off_gdyt = o; o = align_up(o + size_t(D) * TKP * 2, A);
+    L->off_ht = o; o = align_up(o + size_t(I) * TKP * 2, A);
+    L->off_dat = o; o = align_up(o + size_t(I) * TKP * 2, A);
+    L->off_dbt = o; o = align_up(o + size_t(I) * TKP * 2, A);
+    L->off_roff = o; o = align_up(o + (nl + 1) * 4, A);
   }
   L->total = o;
   return MOK_OK;

@@ -1,0 +1,326 @@
+// Backward of the MoE layer on one GPU's share (bf16 in, fp32 weight gradients).
+//
+// What is computed (Leiphone article on MoK, section 02: the backward reverses the two
+// transfers, pulling dY by the schedule's table and pushing dX contributions back to
+// their tokens; news brief, design decisions: the router-weight gradient is formed
+// inside the SwiGLU backward), per routed row r of expert e (token t, slot j, gate g):
+//   u = dY[t] W_down[e]                      dH GEMM, against W_down transposed
+//   dG[t,j] = <u, h>                          in the dH epilogue (no second pass over o)
+//   da, db  = SwiGLU backward of g u          in the dH epilogue
+//   dx_r = da W_gate[e] + db W_up[e]          dX GEMM, against [W_gate | W_up] transposed
+//   dX[t] = sum over local slots j (ascending) of dx_r          fixed order
+//   dW_down[e] = sum_r (g dY[t])^T h,  dW_gate[e] = sum_r da^T x,  dW_up[e] = sum_r db^T x
+// The dW contractions run over the expert's rows; both operands are read from per-expert
+// transposed panels (rows of the expert as columns, zero padded to a multiple of 64) so
+// that every MFMA operand is K-contiguous, and each dW tile has one owner and one K
+// order: no atomics, bitwise reproducible.
+//
+// This file holds the path as separate kernels; the gate/up pre-activations are
+// recomputed from the dispatched rows (replay of GEMM1).
+#include <algorithm>
+
+#include "tile_ops.h"
+
+namespace mok {
+
+struct BwdParams {
+  Ptrs P;
+  BwdArgs a;
+  int T, D, I, k, nl, mt_max, nDt, nIt, nNdh, n_mb_max;
+  int64_t TKP;
+};
+
+// ------------------------------------------------------------------------------------
+// preparation
+// ------------------------------------------------------------------------------------
+// Panel column offsets: roff[e+1] = roff[e] + round_up(count[e], 64).
+__global__ __launch_bounds__(64) void k_bwd_prep(BwdParams p) {
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    p.P.roff[0] = 0;
+    for (int e = 0; e < p.nl; ++e) {
+      acc += (p.P.counts[e] + 63) & ~63;
+      p.P.roff[e + 1] = acc;
+    }
+  }
+}
+
+// dst[r] = src[perm[r] / k] for routed rows r < R (one wave per row).
+__global__ __launch_bounds__(256) void k_bwd_gather(BwdParams p, const uint16_t* src, uint16_t* dst) {
+  const int R = int(p.P.hdr[kHdrR]);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  for (int r = gw; r < R; r += nw)
+    wave_copy_row<false>(dst + int64_t(r) * p.D, src + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+}
+
+// 64 x 64 transpose through LDS: dst[c][r] = src[r][c] for a [rows, cols] block of a
+// batch item.  Each thread moves 16 bytes on both sides.
+__device__ __forceinline__ void transpose_tile(const uint16_t* src, int64_t lds_src, int rows,
+                                               int cols, uint16_t* dst, int64_t ldd, int r0,
+                                               int c0, uint16_t (*tile)[72]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + t;  // 512 chunks of 8 elements
+    const int r = idx >> 3, c8 = (idx & 7) * 8;
+    v4u v = v4u{0u, 0u, 0u, 0u};
+    if (r0 + r < rows && c0 + c8 < cols)
+      v = *reinterpret_cast<const v4u*>(src + int64_t(r0 + r) * lds_src + c0 + c8);
+    *reinterpret_cast<v4u*>(&tile[r][c8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + t;
+    const int c = idx >> 3, r8 = (idx & 7) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(tile[r8 + 2 * e][c]) | (uint32_t(tile[r8 + 2 * e + 1][c]) << 16);
+    if (c0 + c < cols && r0 + r8 < rows)
+      *reinterpret_cast<v4u*>(dst + int64_t(c0 + c) * ldd + r0 + r8) = v4u{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+}
+
+// W_down[e] [D, I] -> wdt[e] [I, D];  W_gate[e], W_up[e] [I, D] -> wgut[e] [D, 2I].
+// grid: (max(D, I)/64 column blocks, max(D, I)/64 row blocks, 3 * E_loc)
+__global__ __launch_bounds__(256) void k_bwd_transpose_weights(BwdParams p) {
+  __shared__ uint16_t tile[64][72];
+  const int which = blockIdx.z % 3, e = blockIdx.z / 3;
+  const int64_t wsz = int64_t(p.I) * p.D;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (which == 0) {
+    if (r0 >= p.D || c0 >= p.I) return;
+    transpose_tile(p.a.wd + e * wsz, p.I, p.D, p.I, p.P.wdt + e * wsz, p.D, r0, c0, tile);
+  } else {
+    if (r0 >= p.I || c0 >= p.D) return;
+    const uint16_t* src = (which == 1 ? p.a.wg : p.a.wu) + e * wsz;
+    uint16_t* dst = p.P.wgut + e * 2 * wsz + (which == 1 ? 0 : p.I);
+    transpose_tile(src, p.D, p.I, p.D, dst, 2 * int64_t(p.I), r0, c0, tile);
+  }
+}
+
+// Expert panels of X and of gate * dY: column roff[e] + q holds routed row offsets[e] + q
+// of expert e (zero for q >= count[e]).  grid: (TKP / 64, D / 64).
+__global__ __launch_bounds__(256) void k_bwd_panels(BwdParams p) {
+  __shared__ uint16_t tx[64][72];
+  __shared__ uint16_t tg[64][72];
+  const int pc0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  if (pc0 >= p.P.roff[p.nl]) return;
+  int e = 0;
+  while (p.P.roff[e + 1] <= pc0) ++e;
+  const int q0 = pc0 - p.P.roff[e];
+  const int cnt = p.P.counts[e];
+  const int rbase = p.P.offsets[e] + q0;
+  const int t = threadIdx.x;
+  // rows of the 64 x 64 block: panel column c <-> routed row rbase + c
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + t;
+    const int c = idx >> 3, d8 = (idx & 7) * 8;
+    v4u vx = v4u{0u, 0u, 0u, 0u}, vg = v4u{0u, 0u, 0u, 0u};
+    if (q0 + c < cnt && d0 + d8 < p.D) {
+      const int q = p.P.perm[rbase + c];
+      const int64_t tok = q / p.k;
+      vx = *reinterpret_cast<const v4u*>(p.a.x + tok * p.D + d0 + d8);
+      const v4u vy = *reinterpret_cast<const v4u*>(p.a.dy + tok * p.D + d0 + d8);
+      const float g = p.a.gates[q];
+      const uint32_t w[4] = {vy.x, vy.y, vy.z, vy.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        o[e2] = pack_bf16x2(g * bf16_to_f32(uint16_t(w[e2] & 0xFFFF)),
+                            g * bf16_to_f32(uint16_t(w[e2] >> 16)));
+      vg = v4u{o[0], o[1], o[2], o[3]};
+    }
+    *reinterpret_cast<v4u*>(&tx[c][d8]) = vx;
+    *reinterpret_cast<v4u*>(&tg[c][d8]) = vg;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + t;
+    const int d = idx >> 3, c8 = (idx & 7) * 8;
+    if (d0 + d >= p.D) continue;
+    uint32_t wx[4], wg[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      wx[e2] = uint32_t(tx[c8 + 2 * e2][d]) | (uint32_t(tx[c8 + 2 * e2 + 1][d]) << 16);
+      wg[e2] = uint32_t(tg[c8 + 2 * e2][d]) | (uint32_t(tg[c8 + 2 * e2 + 1][d]) << 16);
+    }
+    const int64_t off = int64_t(d0 + d) * p.TKP + pc0 + c8;
+    *reinterpret_cast<v4u*>(p.P.xt + off) = v4u{wx[0], wx[1], wx[2], wx[3]};
+    *reinterpret_cast<v4u*>(p.P.gdyt + off) = v4u{wg[0], wg[1], wg[2], wg[3]};
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// GEMM kernels (one m-tile of the schedule's table per workgroup row)
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ bool tile_of(const BwdParams& p, int f, int4& e) {
+  const int mb = f / p.mt_max, i = f % p.mt_max;
+  if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return false;
+  e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+  return true;
+}
+
+// Replay of GEMM1: gate/up pre-activations of every routed row into bab [R, 2I].
+__global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
+  int4 e;
+  const int nN1 = (p.I + kBN1 - 1) / kBN1;
+  if (!tile_of(p, blockIdx.x / nN1, e)) return;
+  const int nt = blockIdx.x % nN1;
+  const int64_t wsz = int64_t(p.I) * p.D;
+  TileAcc acc;
+  run_tile<false>(true, p.P.bx + int64_t(e.x) * p.D, e.y, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz,
+                  nt * kBN1, p.D, p.I, acc);
+  epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, nullptr, p.I, p.P.bab + int64_t(e.x) * 2 * p.I);
+}
+
+// dH GEMM: u = dY rows x W_down[e] (wdt rows), fused SwiGLU backward and dG partials.
+__global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
+  int4 e;
+  if (!tile_of(p, blockIdx.x / p.nNdh, e)) return;
+  const int nt = blockIdx.x % p.nNdh;
+  const int n0 = nt * kBN2;
+  const int64_t wsz = int64_t(p.I) * p.D;
+  const uint16_t* wdt = p.P.wdt + e.z * wsz;
+  TileSrc src;
+  tile_src_init(src, geom::kSplit, p.P.bdy + int64_t(e.x) * p.D, p.D, e.y, wdt, wdt, p.D, n0,
+                n0 + 128, p.I);
+  TileAcc acc;
+  tile_gemm<false>(src, p.D, acc);
+  const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
+  epi_dh(acc, e.y, e.x, pc0, p.P.roff[e.z + 1], n0, p.I, p.TKP, p.P.bab, p.a.gates, p.P.perm,
+         p.P.bdab, p.P.ht, p.P.dat, p.P.dbt, p.P.dgpart, nt, p.nNdh);
+}
+
+// dX GEMM: dx rows = [da | db] x [W_gate; W_up][e] (wgut rows), pushed to their pairs.
+__global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
+  int4 e;
+  if (!tile_of(p, blockIdx.x / p.nDt, e)) return;
+  const int n0 = (blockIdx.x % p.nDt) * kBN2;
+  const int64_t K = 2 * int64_t(p.I);
+  const uint16_t* wg = p.P.wgut + e.z * K * p.D;
+  TileSrc src;
+  tile_src_init(src, geom::kSplit, p.P.bdab + int64_t(e.x) * K, K, e.y, wg, wg, K, n0, n0 + 128,
+                p.D);
+  TileAcc acc;
+  tile_gemm<false>(src, int(K), acc);
+  epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+}
+
+// dW GEMMs over the expert panels.  Per expert: dW_down tiles (D x I), then dW_gate and
+// dW_up tiles (I x D); K = the expert's padded row count (zero rows give zero tiles).
+__global__ __launch_bounds__(512) void k_bwd_dw(BwdParams p) {
+  const int per = p.nDt * p.nIt;
+  const int e = blockIdx.x / (3 * per);
+  const int q = blockIdx.x % (3 * per);
+  const int which = q / per, r = q % per;
+  const int c0 = p.P.roff[e];
+  const int K = p.P.roff[e + 1] - c0;
+  const int64_t wsz = int64_t(p.I) * p.D;
+  const uint16_t *A, *B;
+  float* C;
+  int M, N, mt, nt;
+  if (which == 0) {  // dW_down[e] = gdY^T h : rows d, columns i
+    M = p.D; N = p.I; mt = r / p.nIt; nt = r % p.nIt;
+    A = p.P.gdyt; B = p.P.ht; C = p.a.dwd + e * wsz;
+  } else {           // dW_gate / dW_up[e] = da^T x / db^T x : rows i, columns d
+    M = p.I; N = p.D; mt = r / p.nDt; nt = r % p.nDt;
+    A = which == 1 ? p.P.dat : p.P.dbt; B = p.P.xt; C = (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz;
+  }
+  const int m0 = mt * kBM, n0 = nt * kBN2;
+  const int rows = min(kBM, M - m0);
+  TileSrc src;
+  tile_src_init(src, geom::kSplit, A + int64_t(m0) * p.TKP + c0, p.TKP, rows, B + c0, B + c0,
+                p.TKP, n0, n0 + 128, N);
+  TileAcc acc;
+  tile_gemm<false>(src, K, acc);
+  epi_store_f32(acc, rows, n0, N, C + int64_t(m0) * N, N);
+}
+
+// ------------------------------------------------------------------------------------
+// reductions back to token order
+// ------------------------------------------------------------------------------------
+// dG[t, j] = sum over dH n-tiles (ascending) of the partials of row pos[t, j]; 0 if none.
+__global__ __launch_bounds__(256) void k_bwd_dg(BwdParams p) {
+  const int64_t TK = int64_t(p.T) * p.k;
+  for (int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x; q < TK; q += int64_t(gridDim.x) * 256) {
+    const int r = p.P.pos[q];
+    float s = 0.f;
+    if (r >= 0)
+      for (int nt = 0; nt < p.nNdh; ++nt) s += p.P.dgpart[int64_t(r) * p.nNdh + nt];
+    p.a.dg[q] = s;
+  }
+}
+
+// dX[t] = sum over local slots j (ascending) of dxbuf[t*k + j], fp32, rounded once.
+__global__ __launch_bounds__(256) void k_bwd_dxsum(BwdParams p) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  for (int t = gw; t < p.T; t += nw) {
+    const int64_t q0 = int64_t(t) * p.k;
+    const uint64_t has = __ballot(lane < p.k && p.P.pos[q0 + (lane < p.k ? lane : 0)] >= 0);
+    v4u* out = reinterpret_cast<v4u*>(p.a.dx + int64_t(t) * p.D);
+    for (int c = lane; c < (p.D >> 3); c += 64) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      uint64_t m = has;
+      while (m) {
+        const int j = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const v4u v = reinterpret_cast<const v4u*>(p.P.dxbuf + (q0 + j) * p.D)[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = __fadd_rn(acc[2 * e], bf16_to_f32(uint16_t(w[e] & 0xFFFF)));
+          acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], bf16_to_f32(uint16_t(w[e] >> 16)));
+        }
+      }
+      out[c] = v4u{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// host
+// ------------------------------------------------------------------------------------
+mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, hipStream_t st) {
+  BwdParams p;
+  p.P = P;
+  p.a = a;
+  p.T = int(L.T); p.D = int(L.D); p.I = int(L.I); p.k = int(L.k); p.nl = int(L.nl);
+  p.mt_max = int(L.mt_max); p.n_mb_max = int(L.n_mb_max);
+  p.nDt = int((L.D + kBN2 - 1) / kBN2);
+  p.nIt = int((L.I + kBN2 - 1) / kBN2);
+  p.nNdh = int(L.nNdh);
+  p.TKP = int64_t(L.TKP);
+  const unsigned rows_grid = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
+  const unsigned ftiles = unsigned(L.n_mb_max * L.mt_max);
+  const unsigned nN1 = unsigned((L.I + kBN1 - 1) / kBN1);
+  const unsigned dmax = unsigned((std::max(L.D, L.I) + 63) / 64);
+  hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_gather, dim3(rows_grid), dim3(256), 0, st, p, a.x, P.bx);
+  hipLaunchKernelGGL(k_bwd_gather, dim3(rows_grid), dim3(256), 0, st, p, a.dy, P.bdy);
+  hipLaunchKernelGGL(k_bwd_transpose_weights, dim3(dmax, dmax, unsigned(3 * L.nl)), dim3(256), 0,
+                     st, p);
+  hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
+                     p);
+  hipLaunchKernelGGL(k_bwd_gemm1, dim3(ftiles * nN1), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dh, dim3(ftiles * unsigned(p.nNdh)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dx, dim3(ftiles * unsigned(p.nDt)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dw, dim3(unsigned(L.nl * 3 * p.nDt * p.nIt)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dg, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536))),
+                     dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dxsum, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
+                     dim3(256), 0, st, p);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
+}
+
+}  // namespace mok

@@ -26,8 +26,7 @@
 // combine overlaps later minibatches' GEMMs.
 #include <algorithm>
 
-#include "gemm_bf16.h"
-#include "launch.h"
+#include "tile_ops.h"
 
 namespace mok {
 
@@ -39,44 +38,8 @@ struct FwdParams {
 };
 
 // ------------------------------------------------------------------------------------
-// wave-level data movement
+// combine
 // ------------------------------------------------------------------------------------
-template <bool kCoherent>
-__device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
-                                              const uint16_t* __restrict__ src, int D) {
-  const int lane = threadIdx.x & 63;
-  const int nch = D >> 3;
-  const v4u* s = reinterpret_cast<const v4u*>(src);
-  v4u* d = reinterpret_cast<v4u*>(dst);
-  int c = lane;
-  for (; c + 192 < nch; c += 256) {
-    const v4u v0 = s[c], v1 = s[c + 64], v2 = s[c + 128], v3 = s[c + 192];
-    if (kCoherent) {
-      st_dev_b128(d + c, v0); st_dev_b128(d + c + 64, v1);
-      st_dev_b128(d + c + 128, v2); st_dev_b128(d + c + 192, v3);
-    } else {
-      d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
-    }
-  }
-  for (; c < nch; c += 64) {
-    if (kCoherent) st_dev_b128(d + c, s[c]);
-    else d[c] = s[c];
-  }
-}
-
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Highest local row of token t (-1 when it has none).  Lanes j < k read pos[t*k+j].
-__device__ __forceinline__ int token_last_row(const int32_t* pos, int t, int k) {
-  const int lane = threadIdx.x & 63;
-  const int v = lane < k ? pos[int64_t(t) * k + lane] : -1;
-  return wave_max(v);
-}
-
 // y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.
 template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
@@ -112,100 +75,6 @@ __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
     out.w = pack_bf16x2(acc[6], acc[7]);
     yrow[c] = out;
   }
-}
-
-__device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
-  const int lane = threadIdx.x & 63;
-  v4u* d = reinterpret_cast<v4u*>(dst);
-  for (int c = lane; c < (D >> 3); c += 64) d[c] = v4u{0u, 0u, 0u, 0u};
-}
-
-// ------------------------------------------------------------------------------------
-// GEMM tiles
-// ------------------------------------------------------------------------------------
-// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
-// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
-// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
-// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
-// Writes H (and, when AB != null, the gate/up pre-activations as [rows, 2I]: gate in
-// [0, I), up in [I, 2I)).  With kCoherent, H is written at device scope (handoff data of
-// the fused kernel).
-template <bool kCoherent>
-__device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
-                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
-  const int tid = opaque(threadIdx.x);
-  const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
-  const bool gate_lane = (lane & 16) == 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + (brow_of(j, wn) >> 5) * 16 + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = acc.c[i][j][v];
-        const float y = __shfl_xor(x, 16);
-        const int row = acc_row(tid, i, v);
-        if (row < rows && col < I) {
-          if (gate_lane) {
-            const uint16_t h = f32_to_bf16(silu_f(x) * y);
-            const int off = row * int(ldh) + col;  // < 2^31: row < 256, ldh <= 65536
-            if (kCoherent) st_dev_u16(H + off, h);
-            else H[off] = h;
-          }
-          if (AB) AB[row * 2 * I + (gate_lane ? col : I + col)] = f32_to_bf16(x);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one block at a time: few live registers
-    }
-}
-
-// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256) (B tile row b is
-// hidden column n0 + b in the split layout); row r's result is
-// pushed to obuf row perm_rows[r] (its pair index t*k + j).
-template <bool kCoherent>
-__device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
-                                            const int32_t* perm_rows, uint16_t* obuf) {
-  const int tid = opaque(threadIdx.x);
-  const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int dst[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = acc_row(tid, i, v);
-      dst[v] = row < rows ? perm_rows[row] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + brow_of(j, wn) + (lane & 31);
-      if (col >= D) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (dst[v] >= 0) {
-          uint16_t* o = obuf + int64_t(dst[v]) * D + col;
-          const uint16_t b = f32_to_bf16(acc.c[i][j][v]);
-          if (kCoherent) st_dev_u16(o, b);
-          else *o = b;
-        }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
-// Operands of one tile of either GEMM (one K loop serves both).
-//   GEMM1: A = dispatched rows [rows, D], B = W_gate/W_up rows n0.., K = D.
-//   GEMM2: A = hidden rows [rows, I], B = W_down rows n0..n0+255, K = I.
-template <bool kCoherent>
-__device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows,
-                                         const uint16_t* w0, const uint16_t* w1, int n0, int D,
-                                         int I, TileAcc& acc) {
-  TileSrc src;
-  if (gemm1) tile_src_init(src, geom::kPaired, A, D, rows, w0, w1, D, n0, n0, I);
-  else tile_src_init(src, geom::kSplit, A, I, rows, w0, w0, I, n0, n0 + 128, D);
-  tile_gemm<kCoherent>(src, gemm1 ? D : I, acc);
 }
 
 // ------------------------------------------------------------------------------------

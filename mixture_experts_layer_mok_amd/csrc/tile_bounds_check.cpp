@@ -5,6 +5,7 @@
 // row count 1..256, and that the paired layout covers each gate/up row exactly once.  Built with the host compiler only; exits non-zero on a violation.
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 
 #include "tile_geom.h"
 
@@ -40,6 +41,16 @@ int main(int argc, char** argv) {
       bad += check("gemm1", mok::geom::kPaired, D, D, D, I, n0, n0, rows);
     for (int n0 = 0; n0 < D; n0 += kBN2)
       bad += check("gemm2", mok::geom::kSplit, I, I, I, D, n0, n0 + 128, rows);
+    // backward: dH (A = dY rows, B = W_down^T [I, D]), dX (A = [da|db] rows, B =
+    // [W_gate|W_up]^T [D, 2I]), dW (A, B = expert panels of width TKP, K <= panel width)
+    for (int n0 = 0; n0 < I; n0 += kBN2)
+      bad += check("dh", mok::geom::kSplit, D, D, D, I, n0, n0 + 128, rows);
+    for (int n0 = 0; n0 < D; n0 += kBN2)
+      bad += check("dx", mok::geom::kSplit, 2 * I, 2 * I, 2 * I, D, n0, n0 + 128, rows);
+    const int TKP = 4096;
+    for (int K : {64, 1024, 4096})
+      for (int n0 = 0; n0 < I; n0 += kBN2)
+        bad += check("dw", mok::geom::kSplit, K, TKP, TKP, I, n0, n0 + 128, rows);
   }
   // paired layout: tile rows of block b cover intermediate columns n0 + 16 b .. +15 of
   // both matrices, each exactly once (unclamped case)

@@ -1,0 +1,248 @@
+// Device building blocks shared by the forward and backward kernels: wave-level row
+// copies and reductions, the grouped-GEMM tile runner and its epilogues.
+#pragma once
+#include "gemm_bf16.h"
+#include "launch.h"
+
+namespace mok {
+
+// ------------------------------------------------------------------------------------
+// wave-level data movement
+// ------------------------------------------------------------------------------------
+template <bool kCoherent>
+__device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
+                                              const uint16_t* __restrict__ src, int D) {
+  const int lane = threadIdx.x & 63;
+  const int nch = D >> 3;
+  const v4u* s = reinterpret_cast<const v4u*>(src);
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  int c = lane;
+  for (; c + 192 < nch; c += 256) {
+    const v4u v0 = s[c], v1 = s[c + 64], v2 = s[c + 128], v3 = s[c + 192];
+    if (kCoherent) {
+      st_dev_b128(d + c, v0); st_dev_b128(d + c + 64, v1);
+      st_dev_b128(d + c + 128, v2); st_dev_b128(d + c + 192, v3);
+    } else {
+      d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
+    }
+  }
+  for (; c < nch; c += 64) {
+    if (kCoherent) st_dev_b128(d + c, s[c]);
+    else d[c] = s[c];
+  }
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Highest local row of token t (-1 when it has none).  Lanes j < k read pos[t*k+j].
+__device__ __forceinline__ int token_last_row(const int32_t* pos, int t, int k) {
+  const int lane = threadIdx.x & 63;
+  const int v = lane < k ? pos[int64_t(t) * k + lane] : -1;
+  return wave_max(v);
+}
+
+__device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
+  const int lane = threadIdx.x & 63;
+  v4u* d = reinterpret_cast<v4u*>(dst);
+  for (int c = lane; c < (D >> 3); c += 64) d[c] = v4u{0u, 0u, 0u, 0u};
+}
+
+// ------------------------------------------------------------------------------------
+// GEMM tiles
+// ------------------------------------------------------------------------------------
+// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
+// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
+// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
+// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
+// Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
+// [rows, 2I]: gate in [0, I), up in [I, 2I).  With kCoherent, H is written at device scope (handoff data of
+// the fused kernel).
+template <bool kCoherent>
+__device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
+                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+  const bool gate_lane = (lane & 16) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + (brow_of(j, wn) >> 5) * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float x = acc.c[i][j][v];
+        const float y = __shfl_xor(x, 16);
+        const int row = acc_row(tid, i, v);
+        if (row < rows && col < I) {
+          if (H && gate_lane) {
+            const uint16_t h = f32_to_bf16(silu_f(x) * y);
+            const int off = row * int(ldh) + col;  // < 2^31: row < 256, ldh <= 65536
+            if (kCoherent) st_dev_u16(H + off, h);
+            else H[off] = h;
+          }
+          if (AB) AB[row * 2 * I + (gate_lane ? col : I + col)] = f32_to_bf16(x);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one block at a time: few live registers
+    }
+}
+
+// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256) (B tile row b is
+// hidden column n0 + b in the split layout); row r's result is
+// pushed to obuf row perm_rows[r] (its pair index t*k + j).
+template <bool kCoherent>
+__device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
+                                            const int32_t* perm_rows, uint16_t* obuf) {
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int dst[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = acc_row(tid, i, v);
+      dst[v] = row < rows ? perm_rows[row] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + brow_of(j, wn) + (lane & 31);
+      if (col >= D) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (dst[v] >= 0) {
+          uint16_t* o = obuf + int64_t(dst[v]) * D + col;
+          const uint16_t b = f32_to_bf16(acc.c[i][j][v]);
+          if (kCoherent) st_dev_u16(o, b);
+          else *o = b;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Operands of one tile of either GEMM (one K loop serves both).
+//   GEMM1: A = dispatched rows [rows, D], B = W_gate/W_up rows n0.., K = D.
+//   GEMM2: A = hidden rows [rows, I], B = W_down rows n0..n0+255, K = I.
+template <bool kCoherent>
+__device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows,
+                                         const uint16_t* w0, const uint16_t* w1, int n0, int D,
+                                         int I, TileAcc& acc) {
+  TileSrc src;
+  if (gemm1) tile_src_init(src, geom::kPaired, A, D, rows, w0, w1, D, n0, n0, I);
+  else tile_src_init(src, geom::kSplit, A, I, rows, w0, w0, I, n0, n0 + 128, D);
+  tile_gemm<kCoherent>(src, gemm1 ? D : I, acc);
+}
+
+// Epilogue of the dH GEMM of the backward (SwiGLU backward and router-weight gradient
+// fused).  The tile covered routed rows row0 + [0, rows) and intermediate columns
+// n0 + [0, 256) (split B layout: B tile row b is column n0 + b) of u = dY W_down.  Per
+// element, with a, b the saved gate/up pre-activations, g the row's gate weight,
+// s = sigmoid(a):  h = a s b;  dh = g u;  da = dh b s (1 + a (1 - s));  db = dh a s.
+// Writes da, db row-major into bdab [R, 2I] and, transposed, h / da / db into the
+// per-expert panels (row r of the tile is panel column pc0 + r; columns up to the
+// padded panel end pe are written, zeros past the valid rows), and the partial sum of
+// u h over this tile's columns for each row into dgpart[row][nt] (lanes first, then
+// the four column waves in order: a fixed summation order).
+__device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int pc0, int pe,
+                                       int n0, int I, int64_t TKP, const uint16_t* bab,
+                                       const float* gates, const int32_t* perm, uint16_t* bdab,
+                                       uint16_t* ht, uint16_t* dat, uint16_t* dbt, float* dgpart,
+                                       int nt, int nNdh) {
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+  float* red = reinterpret_cast<float*>(g_lds_a);  // [4][256] row partials per column wave
+  const int64_t twoI = 2 * int64_t(I);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int rr[4];
+      float gq[4], s[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rr[t] = acc_row(tid, i, 4 * q + t);  // four consecutive rows
+        gq[t] = rr[t] < rows ? gates[perm[row0 + rr[t]]] : 0.f;
+        s[t] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (col < I) {
+          uint32_t hv[2] = {0u, 0u}, dav[2] = {0u, 0u}, dbv[2] = {0u, 0u};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (rr[t] < rows) {
+              const float u = acc.c[i][j][4 * q + t];
+              const uint16_t* abr = bab + int64_t(row0 + rr[t]) * twoI;
+              const float a = bf16_to_f32(abr[col]);
+              const float b = bf16_to_f32(abr[I + col]);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+              const float sl = a * sg;
+              const float h = sl * b;
+              s[t] += u * h;
+              const float dh = gq[t] * u;
+              const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
+              const float db = dh * sl;
+              uint16_t* dr = bdab + int64_t(row0 + rr[t]) * twoI;
+              const uint16_t dab = f32_to_bf16(da), dbb = f32_to_bf16(db);
+              dr[col] = dab;
+              dr[I + col] = dbb;
+              hv[t >> 1] |= uint32_t(f32_to_bf16(h)) << (16 * (t & 1));
+              dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
+              dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
+            }
+          }
+          const int pc = pc0 + rr[0];  // multiple of 4: one 8-byte store per panel
+          if (pc < pe) {
+            const int64_t off = int64_t(col) * TKP + pc;
+            *reinterpret_cast<uint2*>(ht + off) = make_uint2(hv[0], hv[1]);
+            *reinterpret_cast<uint2*>(dat + off) = make_uint2(dav[0], dav[1]);
+            *reinterpret_cast<uint2*>(dbt + off) = make_uint2(dbv[0], dbv[1]);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v = s[t];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
+        if ((lane & 31) == 0 && rr[t] < rows) red[wn * 256 + rr[t]] = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kThreads)
+    dgpart[int64_t(row0 + r) * nNdh + nt] = ((red[r] + red[256 + r]) + red[512 + r]) + red[768 + r];
+  __syncthreads();
+}
+
+// Epilogue storing the fp32 tile: rows [0, rows) at C + row * ldc, columns n0 + b for
+// B tile row b (split layout) below N.
+__device__ __forceinline__ void epi_store_f32(const TileAcc& acc, int rows, int n0, int N,
+                                              float* C, int64_t ldc) {
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(tid, i, v);
+        if (row < rows && col < N) C[int64_t(row) * ldc + col] = acc.c[i][j][v];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+}  // namespace mok
