@@ -1,24 +1,33 @@
 """Benchmark of the MoE layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 2048] [--S 4] [--comm-cus 32]
-                    [--unfused] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--M 2048] [--S 4]
+                    [--comm-cus 32] [--unfused] [--fwd-only] [--no-cpu-baseline]
+    python bench.py --sweep            # minibatch x comm-CU sweep of the forward, JSON lines
+    python bench.py --copy-calibration # one plain device copy of known size (counter scale)
 
-A step is one pass of the layer over one batch: schedule + forward on one GPU's share of
-an expert-parallel layer (hidden 7168, expert intermediate 2048, 64 experts with 8
-local, top-8, a 16384-token pool: 2048 tokens from each of 8 sources), inputs resident
-in HBM before the timed region.  Prints one JSON line.
+A step is one pass of the layer over one batch of synthetic input on one GPU's share of
+an expert-parallel layer (hidden 7168, expert intermediate 2048, 64 experts of which 8
+are local, top-8, a 16384-token pool = 2048 tokens from each of 8 sources): schedule,
+forward (persistent fused kernel) and backward, inputs resident in HBM before the timed
+region.  Prints one JSON line.
 
-`value` is algorithmic TFLOP/s of the step (6*D*I flops per routed row forward).
-`roofline` reports the dominant kernel (the fused forward) against the bf16 dense
-MFMA peak, timed with HIP events on the stream the kernels run on.
-`cpu_baseline` times the float64 NumPy oracle on a bounded sample of the same workload
-(its first 8192 tokens) on this host's cores.
+`value` is the algorithmic TFLOP/s of the step: 6*D*I flops per routed row forward,
+12*D*I backward (the GEMM1 replay of rows whose ring slot was recycled is not counted).
+`roofline` reports the dominant kernel, the persistent forward k_fwd_fused, against the
+bf16 dense MFMA peak; its duration comes from HIP events recorded on the stream the
+kernel is launched on, around the forward call (which also holds a tiny counter-reset
+kernel).  `traffic` is the HBM byte count of that kernel read from the committed
+FETCH_SIZE / WRITE_SIZE counter summary, scaled by the copy calibration, and null when
+the kernel sources changed since the counters were taken.
+`cpu_baseline` times the float64 NumPy oracle (forward + backward) on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,134 +38,270 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_fused_c5_traffic.txt")
+KERNEL_SOURCES = ("moe_fwd.hip", "tile_ops.h", "gemm_bf16.h", "tile_geom.h", "device.h",
+                  "layout.h")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--S", type=int, default=None)
     ap.add_argument("--comm-cus", type=int, default=None)
     ap.add_argument("--unfused", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the layer shards by expert across GPUs, see the design notes)"}))
-        sys.exit(2)
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_mok_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the fused forward from the committed counter summary, or
+    None when it is absent or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_hash = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, three times, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: each launch moves exactly 1 GiB in and 1 GiB out."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def setup(cfg, unfused, save, device):
     import torch
 
     from mixture_experts_layer_mok_amd import _lib as L
     from mixture_experts_layer_mok_amd import gen
     from mixture_experts_layer_mok_amd.layer import MoKLayer, bf16_tensor
 
-    L.load()
-    cfg = gen.CONFIGS[args.config]
-    over = {}
-    if args.M:
-        over["M"] = args.M
-    if args.S:
-        over["S"] = args.S
-    if args.comm_cus:
-        over["comm_cus"] = args.comm_cus
-    cfg = cfg.replace(**over)
-    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    d = gen.make_inputs(cfg)
-    dev = torch.device("cuda:0")
-    x = bf16_tensor(d["x_bits"], dev)
-    ids = torch.from_numpy(d["ids"]).to(dev)
-    gates = torch.from_numpy(d["gates"]).to(dev)
-    wg, wu, wd = (bf16_tensor(d[n], dev) for n in ("wg_bits", "wu_bits", "wd_bits"))
-    flags = L.MOK_FLAG_UNFUSED if args.unfused else 0
-    layer = MoKLayer(L.desc_from_config(cfg, flags=flags), device=dev)
-    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev)
-    R = int(((d["ids"] >= cfg.e0) & (d["ids"] < cfg.e0 + cfg.n_local)).sum())
-    flops_fwd = 6.0 * cfg.D * cfg.I * R
+    log(f"generating {cfg.name} inputs")
+    d = gen.make_inputs(cfg, with_dy=save)
+    t = dict(x=bf16_tensor(d["x_bits"], device), ids=torch.from_numpy(d["ids"]).to(device),
+             gates=torch.from_numpy(d["gates"]).to(device))
+    for n in ("wg", "wu", "wd") + (("dy",) if save else ()):
+        t[n] = bf16_tensor(d[n + "_bits"], device)
+    flags = (L.MOK_FLAG_UNFUSED if unfused else 0) | (L.MOK_FLAG_SAVE_FOR_BWD if save else 0)
+    layer = MoKLayer(L.desc_from_config(cfg, flags=flags), device=device)
+    return d, t, layer
 
+
+def time_layer(cfg, t, layer, steps, warmup, with_bwd):
+    """Times `steps` steps after `warmup`; returns per-phase mean ms and total ms/step."""
+    import torch
     stream = torch.cuda.current_stream()
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=t["x"].device)
+    grads = {}
 
     def step(ev=None):
-        layer.schedule(ids)
         if ev is not None:
             ev[0].record(stream)
-        layer.forward(x, ids, gates, wg, wu, wd, y=y)
+        layer.schedule(t["ids"])
         if ev is not None:
             ev[1].record(stream)
+        layer.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"], y=y)
+        if ev is not None:
+            ev[2].record(stream)
+        if with_bwd:
+            grads.update(layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"],
+                                        t["wu"], t["wd"]))
+            if ev is not None:
+                ev[3].record(stream)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     st = layer.status()
     if st != 0:
         raise SystemExit(f"device status {st:#x} after warmup")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    nev = 4 if with_bwd else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    print("[bench] timed", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     st = layer.status()
     if st != 0:
         raise SystemExit(f"device status {st:#x} after timed steps")
+    res = {"ms_per_step": start.elapsed_time(end) / steps,
+           "sched_ms": [e[0].elapsed_time(e[1]) for e in evs],
+           "fwd_ms": [e[1].elapsed_time(e[2]) for e in evs]}
+    if with_bwd:
+        res["bwd_ms"] = [e[2].elapsed_time(e[3]) for e in evs]
+    return res
 
+
+def stats(v):
+    return {"mean": round(float(np.mean(v)), 4), "median": round(float(np.median(v)), 4),
+            "min": round(float(np.min(v)), 4)}
+
+
+def routed_rows(cfg, ids):
+    return int(((ids >= cfg.e0) & (ids < cfg.e0 + cfg.n_local)).sum())
+
+
+def sweep(args):
+    """Forward time over minibatch sizes and comm-CU counts on the config-3 shape, against
+    the two-waves lower bound for a 256 x 256 tile: each GEMM should see at least two full
+    waves of tiles, 2 * C_compute * 256 * 256 / (2 I) rows for GEMM1."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+    L.load()
+    dev = torch.device("cuda:0")
+    base = gen.CONFIGS[3]
+    d, t, _ = setup(base, False, False, dev)
+    R = routed_rows(base, d["ids"])
+    from mixture_experts_layer_mok_amd.layer import MoKLayer
+    from mixture_experts_layer_mok_amd.tuning import layer_two_wave_min_rows
+    cus = L.mok_device_cus()
+    for comm in (16, 32, 48, 64):
+        for M in (512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 6144, 8192):
+            cfg = base.replace(M=M, comm_cus=comm)
+            layer = MoKLayer(L.desc_from_config(cfg), device=dev)
+            r = time_layer(cfg, t, layer, args.steps, args.warmup, False)
+            fwd = float(np.median(r["fwd_ms"]))
+            m_min = layer_two_wave_min_rows(cus, comm, cfg.I)
+            print(json.dumps({"sweep": "minibatch", "M": M, "comm_cus": comm,
+                              "fwd_ms_median": round(fwd, 4),
+                              "fwd_tflops": round(6.0 * cfg.D * cfg.I * R / fwd / 1e9, 1),
+                              "two_wave_min_rows": round(m_min), "above_two_waves": M >= m_min}),
+                  flush=True)
+            del layer
+            torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU only; --gpus must be 1. "
+                          "Across GPUs it shards by expert, one process per GPU."}))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+
+    L.load()
+    if args.sweep:
+        sweep(args)
+        return
+    cfg = gen.CONFIGS[args.config]
+    over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}
+    cfg = cfg.replace(**over)
+    with_bwd = not args.fwd_only
+    dev = torch.device("cuda:0")
+    d, t, layer = setup(cfg, args.unfused, with_bwd, dev)
+    R = routed_rows(cfg, d["ids"])
+    flops_fwd = 6.0 * cfg.D * cfg.I * R
+    flops_bwd = 12.0 * cfg.D * cfg.I * R if with_bwd else 0.0
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    r = time_layer(cfg, t, layer, args.steps, args.warmup, with_bwd)
+    ms = r["ms_per_step"]
+    fwd_ms = float(np.mean(r["fwd_ms"]))
     achieved = flops_fwd / (fwd_ms * 1e-3) / 1e12
+    mode = "unfused" if args.unfused else "fused"
     out = {
-        "metric": "MoE layer forward TFLOPS (bf16)",
-        "value": round(flops_fwd / (ms_step * 1e-3) / 1e12, 3),
+        "metric": "MoE layer fwd+bwd TFLOPS (bf16)" if with_bwd else
+                  "MoE layer forward TFLOPS (bf16)",
+        "value": round((flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: T={cfg.T} D={cfg.D} I={cfg.I} E={cfg.E} "
-                               f"local={cfg.n_local} k={cfg.k}",
+        "data": "synthetic (seeded normal draws at the layer's real shape)",
+        "config": {"workload": f"{cfg.name}: pool T={cfg.T} x D={cfg.D}, I={cfg.I}, "
+                               f"E={cfg.E} (experts {cfg.e0}..{cfg.e0 + cfg.n_local - 1} local), "
+                               f"top-{cfg.k}" + (", forward+backward" if with_bwd else
+                                                 ", forward"),
                    "routed_rows": R, "minibatch_rows": cfg.M, "ring_slots": cfg.S,
-                   "comm_cus": cfg.comm_cus, "mode": "unfused" if args.unfused else "fused"},
-        "fwd_ms": round(fwd_ms, 4),
-        "schedule_plus_fwd_ms": round(ms_step, 4),
-        "routed_rows_per_s": round(R / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else "unfused",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                   "comm_cus": cfg.comm_cus, "mode": mode},
+        "schedule_ms": stats(r["sched_ms"]),
+        "fwd_ms": stats(r["fwd_ms"]),
+        "fwd_tflops": round(achieved, 2),
+        "routed_rows_per_s": round(R / (ms * 1e-3), 1),
+        "schedule_share": round(float(np.mean(r["sched_ms"])) / ms, 4),
     }
+    if with_bwd:
+        bwd_ms = float(np.mean(r["bwd_ms"]))
+        out["bwd_ms"] = stats(r["bwd_ms"])
+        out["bwd_tflops"] = round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2)
+    # the committed counters were taken on the default command (config 5, fused, M=2048,
+    # S=4, 32 comm CUs, forward saving a and b for the backward)
+    traffic = read_traffic() if (not args.unfused and with_bwd and args.config == 5
+                                 and cfg.M == 2048 and cfg.S == 4 and cfg.comm_cus == 32) else None
+    out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else
+                       "forward (unfused launches)", "achieved": round(achieved, 2),
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
     if not args.no_cpu_baseline:
         import oracle as O
-        Ts = min(args.cpu_tokens, cfg.T)
-        sub = slice(0, Ts)
-        Rs = int(((d["ids"][sub] >= cfg.e0) & (d["ids"][sub] < cfg.e0 + cfg.n_local)).sum())
+        log("timing the float64 oracle on the host")
         t0 = time.time()
-        O.forward(d["x"][sub], d["ids"][sub], d["gates"][sub], d["wg"], d["wu"], d["wd"],
-                  e0=cfg.e0, E=cfg.E, M=cfg.M)
+        O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0, E=cfg.E,
+                  M=cfg.M)
+        if with_bwd:
+            O.backward(d["dy"], d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"],
+                       e0=cfg.e0, E=cfg.E, M=cfg.M)
         dt = time.time() - t0
-        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-        out["cpu_baseline"] = {"value": round(6.0 * cfg.D * cfg.I * Rs / dt / 1e12, 5),
-                               "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                               "sample": f"float64 oracle forward on the first {Ts} tokens "
-                                         f"({Rs} routed rows), {dt:.2f} s"}
-    print(json.dumps(out))
+        cores = len(os.sched_getaffinity(0))
+        omp = os.environ.get("OMP_NUM_THREADS")
+        if omp and omp.isdigit():
+            cores = min(cores, int(omp))
+        out["cpu_baseline"] = {
+            "value": round((flops_fwd + flops_bwd) / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"the whole workload ({R} routed rows), "
+                      f"{'forward+backward' if with_bwd else 'forward'} once in float64 "
+                      f"NumPy: {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -40,23 +40,49 @@ MOK_HD inline int64_t a_offset(int p, int w, int l, int rows_valid, int64_t lda)
 //           output block holds 16 gate columns and their 16 up columns (GEMM1).
 enum BLayout { kSplit = 0, kPaired = 1 };
 
-// Matrix (0 = B0, 1 = B1) and row of the B chunk of load p, wave w, lane l.  For the
-// paired layout the half of the 32-row block, (r / 16) % 2, is (w / 2) % 2: wave-uniform.
-MOK_HD inline int b_matrix(int layout, int p, int w) {
-  return layout == kPaired ? ((w >> 1) & 1) : (p < 2 ? 0 : 1);
+// Matrix (0 = B0, 1 = B1) and row (clamped to N - 1) of B tile row r (0..255).
+MOK_HD inline int b_matrix_of_row(int layout, int r) {
+  return layout == kPaired ? ((r >> 4) & 1) : (r < 128 ? 0 : 1);
 }
-MOK_HD inline int b_row(int layout, int p, int w, int l, int nb0, int nb1, int N) {
-  const int r = dma_row(p, w, l);
+MOK_HD inline int b_row_of_row(int layout, int r, int nb0, int nb1, int N) {
   int rb;
   if (layout == kPaired) rb = nb0 + (r >> 5) * 16 + (r & 15);
   else rb = (r < 128) ? nb0 + r : nb1 + r - 128;
   return rb > N - 1 ? N - 1 : rb;
+}
+
+// Matrix and row of the B chunk of load p, wave w, lane l.  For the paired layout the
+// half of the 32-row block, (r / 16) % 2, is (w / 2) % 2: wave-uniform; for the split
+// layout the matrix is fixed per load p.
+MOK_HD inline int b_matrix(int layout, int p, int w) {
+  return layout == kPaired ? ((w >> 1) & 1) : (p < 2 ? 0 : 1);
+}
+MOK_HD inline int b_row(int layout, int p, int w, int l, int nb0, int nb1, int N) {
+  return b_row_of_row(layout, dma_row(p, w, l), nb0, nb1, N);
 }
 // Byte offset of the B chunk from the start of its weight matrix (rows clamped to N - 1).
 MOK_HD inline int64_t b_offset(int layout, int p, int w, int l, int nb0, int nb1, int N,
                                int64_t ldb) {
   return (int64_t(b_row(layout, p, w, l, nb0, nb1, N)) * ldb + dma_chunk(w, l) * 8) * 2;
 }
+
+// MXFP8 tiles: one K step is 128 code bytes per row (8 chunks: the same direct-to-LDS
+// geometry, with rows of ld / 2 two-byte units) plus one dword of 4 e8m0 scales per
+// row.  Lanes of waves 0-3 load the scale dword of A tile row (w % 4) * 64 + l, lanes
+// of waves 4-7 that of B tile row (w % 4) * 64 + l.  Scale rows are s_ld bytes apart
+// (a multiple of 4); the dword of step ks sits at byte 4 ks of its row.
+MOK_HD inline int mx_scale_row(int w, int l) { return (w & 3) * 64 + l; }
+MOK_HD inline int64_t mx_a_scale_offset(int w, int l, int rows_valid, int64_t s_ld) {
+  int r = mx_scale_row(w, l);
+  if (r > rows_valid - 1) r = rows_valid - 1;
+  return int64_t(r) * s_ld;
+}
+MOK_HD inline int64_t mx_b_scale_offset(int layout, int w, int l, int nb0, int nb1, int N,
+                                        int64_t s_ld) {
+  return int64_t(b_row_of_row(layout, mx_scale_row(w, l), nb0, nb1, N)) * s_ld;
+}
+// On a half step (K % 128 == 64, the last step) only chunks 0..3 of each row load.
+MOK_HD inline bool mx_chunk_in_half(int w, int l) { return dma_chunk(w, l) < 4; }
 
 }  // namespace geom
 }  // namespace mok

@@ -332,3 +332,14 @@ def test_gate_gradient_identity():
     direct = np.sum(d["dy"].astype(np.float64)[t] * parts["o"], axis=1)
     np.testing.assert_allclose(g["dg"].reshape(-1)[s.perm], direct, rtol=1e-10, atol=1e-13)
     assert np.all(g["dg"].reshape(-1)[s.pos < 0] == 0)
+
+
+def test_two_waves_rule_reproduces_printed_floor():
+    """The pages' 2368-token floor for the 7168/2048 shape follows from the two-waves rule
+    with 148 compute units and a 128 x 256 tile (tests/golden/two_waves.json)."""
+    from mixture_experts_layer_mok_amd.tuning import layer_two_wave_min_rows, two_wave_min_rows
+    g = json.load(open(os.path.join(GOLD, "two_waves.json")))
+    assert two_wave_min_rows(g["compute_units"], g["tile_m"], g["tile_n"],
+                             g["intermediate"]) == g["min_minibatch"]
+    # more compute units or a bigger tile raise the floor proportionally
+    assert layer_two_wave_min_rows(256, 32, 2048) == 2 * 224 * 256 * 256 / 4096
