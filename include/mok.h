@@ -119,12 +119,14 @@ mok_status_t mok_schedule_tables(const mok_desc_t* desc, const void* ws, size_t 
                                  int32_t* counts, int32_t* offsets, int32_t* perm,
                                  int32_t* pos, int32_t* hdr, void* stream);
 
-/* Quantise bf16 rows to MXFP8 ([L] section 02 names MXFP8; the block format is OCP MX:
- * e4m3 elements, one e8m0 scale per 32 elements).  src [rows, cols] bf16 (cols a
- * multiple of 32) -> codes [rows, cols] uint8, scales [rows, cols/32] uint8.  The
+/* Quantise bf16 rows to MXFP8 ([L] section 03 names the MXFP8 mode; the block format is
+ * OCP MX: e4m3 elements, one e8m0 scale per 32 elements).  src [rows, cols] bf16 (cols
+ * a multiple of 32) -> codes [rows, cols] uint8, scales [rows, cols/32] uint8.  The
  * shared exponent is the smallest n with amax * 2^-n <= 448 (clamped to [-127, 127];
- * an all-zero block gets n = -127), code = e4m3 round-to-nearest-even of v * 2^-n.
- * Used for the weights before a MXFP8 forward. */
+ * an all-zero block gets n = -127), code = e4m3 round-to-nearest-even of v * 2^-n,
+ * saturating at 448.  The forward's dispatch quantises X rows with the same routine.
+ * Used for the weights before a MXFP8 forward.  src and codes must be 16-byte aligned
+ * (MOK_E_SHAPE otherwise).  Asynchronous on stream; the caller owns every buffer. */
 mok_status_t mok_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, uint8_t* codes,
                              uint8_t* scales, void* stream);
 
@@ -133,9 +135,16 @@ mok_status_t mok_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, u
  *   y[t] = sum over slots j in ascending order with a local expert e = ids[t,j]-e0 of
  *          topk_w[t,j] * ( silu(x[t] W_gate[e]^T) * (x[t] W_up[e]^T) ) W_down[e]^T
  * accumulated in fp32, rounded once to bf16; tokens with no local slot get 0.
- * bf16 mode: weights are bf16 (s_* must be NULL).  MXFP8 mode: w_* point to e4m3 codes
- * and s_* to their e8m0 scales (from mok_quantize_mx); X is quantised during dispatch
- * and H inside the SwiGLU epilogue.  Requires a preceding mok_schedule on `ws`. */
+ * x [T, D] bf16; topk_ids [T, k] int32; topk_w [T, k] fp32; w_gate, w_up [E_loc, I, D];
+ * w_down [E_loc, D, I]; all row-major.
+ * bf16 mode: weights are bf16 (s_* must be NULL, MOK_E_SHAPE otherwise).
+ * MXFP8 mode ([L] section 03): w_* point to e4m3 codes of the same shapes and s_* to
+ * their e8m0 scales, s_gate and s_up [E_loc, I, D/32], s_down [E_loc, D, I/32] (from
+ * mok_quantize_mx); X rows are quantised during dispatch and H inside the SwiGLU
+ * epilogue (blocks of 32 along I); the products run on scaled MFMA with fp32
+ * accumulation.  x, y and the weights must be 16-byte aligned and the scales 4-byte
+ * aligned (MOK_E_SHAPE otherwise).  Requires a preceding mok_schedule on `ws`.
+ * Asynchronous on stream. */
 mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* topk_ids,
                          const float* topk_w, const void* w_gate, const void* w_up,
                          const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,

@@ -9,6 +9,8 @@ using namespace mok;
 
 namespace {
 
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 mok_status_t check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
   if (!ws) return MOK_E_NULL;
   if (ws_bytes < L.total) return MOK_E_WORKSPACE;
@@ -66,6 +68,7 @@ mok_status_t mok_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, u
                              uint8_t* scales, void* stream) {
   if (!src_bf16 || !codes || !scales) return MOK_E_NULL;
   if (rows < 0 || cols < 32 || cols % 32 != 0) return MOK_E_SHAPE;
+  if (!aligned(src_bf16, 16) || !aligned(codes, 16)) return MOK_E_SHAPE;
   return launch_quantize_mx(static_cast<const uint16_t*>(src_bf16), rows, cols, codes, scales,
                             static_cast<hipStream_t>(stream));
 }
@@ -80,9 +83,12 @@ mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* t
   mok_status_t s = make_layout(desc, &L);
   if (s != MOK_OK) return s;
   if ((s = check_ws(L, ws, ws_bytes)) != MOK_OK) return s;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
+      !aligned(w_down, 16))
+    return MOK_E_SHAPE;
   if (L.mx) {
     if (!s_gate || !s_up || !s_down) return MOK_E_NULL;
-    return MOK_E_UNSUPPORTED;
+    if (!aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4)) return MOK_E_SHAPE;
   } else if (s_gate || s_up || s_down) {
     return MOK_E_SHAPE;
   }
@@ -110,6 +116,9 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
   if (s != MOK_OK) return s;
   if ((s = check_ws(L, ws, ws_bytes)) != MOK_OK) return s;
   if (!L.save || L.mx) return MOK_E_UNSUPPORTED;  // needs a bf16 forward that saved
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
+      !aligned(w_down, 16) || !aligned(dx, 16))
+    return MOK_E_SHAPE;
   BwdArgs a;
   a.dy = static_cast<const uint16_t*>(dy);
   a.x = static_cast<const uint16_t*>(x);

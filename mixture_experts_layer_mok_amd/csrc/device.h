@@ -70,6 +70,13 @@ __device__ __forceinline__ void or_relaxed(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void st_dev_u16(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev_u8(uint8_t* p, uint8_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_dev_b128(void* p, v4u v) {
   uint64_t* q = static_cast<uint64_t*>(p);
   __hip_atomic_store(q, uint64_t(v.x) | (uint64_t(v.y) << 32), __ATOMIC_RELAXED,

@@ -25,6 +25,9 @@ struct Ptrs {
   uint8_t* full_xs;   // unfused MX scales
   uint8_t* full_h;    // unfused: [T*k, I] hidden rows
   uint8_t* full_hs;
+  uint8_t* wsg;       // MXFP8 weight scales repacked to the tile's stride (when needed)
+  uint8_t* wsu;
+  uint8_t* wsd;
   // backward
   uint16_t* bx;       // [T*k, D] dispatched X rows
   uint16_t* bdy;      // [T*k, D] dispatched dY rows
@@ -62,6 +65,9 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.full_xs = L.unfused ? b + L.off_full_xs : nullptr;
   P.full_h = L.unfused ? b + L.off_full_h : nullptr;
   P.full_hs = L.unfused ? b + L.off_full_hs : nullptr;
+  P.wsg = L.repack_wg ? b + L.off_wsg : nullptr;
+  P.wsu = L.repack_wg ? b + L.off_wsu : nullptr;
+  P.wsd = L.repack_wd ? b + L.off_wsd : nullptr;
   auto u16 = [&](size_t off) { return L.save ? reinterpret_cast<uint16_t*>(b + off) : nullptr; };
   P.bx = u16(L.off_bx);
   P.bdy = u16(L.off_bdy);

@@ -50,12 +50,18 @@ struct Layout {
   int64_t mt_max;    // m-tiles per minibatch, upper bound
   int64_t nN1, nN2;  // n-tiles of GEMM1 (over I) and GEMM2 (over D)
   bool mx, save, unfused;
+  // MXFP8: bytes per scale row of the layer's own X and H buffers (one dword per 128-wide
+  // K step), and of the weight scales the tiles read (the caller's K / 32 when K % 128
+  // == 0, else a repacked copy in the workspace with the padded stride)
+  int64_t xs_ld, hs_ld, wgs_ld, wds_ld;
+  bool repack_wg, repack_wd;
   // byte offsets into the workspace
   size_t off_hdr, off_counts, off_offsets, off_blk, off_perm, off_pos, off_mt_tab, off_mt_cnt,
       off_tile_base, off_mb_start, off_sync, sync_bytes, off_obuf, off_ring, slot_bytes;
   int64_t slot_rows;  // rows one slot holds: a minibatch's tiles may run past its window
   size_t slot_x, slot_xs, slot_h, slot_hs, slot_ab;  // offsets inside one slot
   size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
+  size_t off_wsg, off_wsu, off_wsd;  // repacked weight scales (MXFP8, when needed)
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t TKP;      // width of the transposed per-expert panels: T*k + 64*E_loc
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
@@ -96,6 +102,12 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->mt_max = (M + kBM - 1) / kBM + nl + 1;
   if (L->mt_max > L->TK / kBM + 1 + nl) L->mt_max = L->TK / kBM + 1 + nl;
   L->slot_rows = M + kBM;
+  L->xs_ld = (D + 127) / 128 * 4;
+  L->hs_ld = (I + 127) / 128 * 4;
+  L->repack_wg = L->mx && D % 128 != 0;
+  L->repack_wd = L->mx && I % 128 != 0;
+  L->wgs_ld = L->repack_wg ? L->xs_ld : D / 32;
+  L->wds_ld = L->repack_wd ? L->hs_ld : I / 32;
   L->nN1 = (I + kBN1 - 1) / kBN1;
   L->nN2 = (D + kBN2 - 1) / kBN2;
 
@@ -123,9 +135,9 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   size_t so = 0;
   const size_t SR = size_t(L->slot_rows);
   L->slot_x = so; so = align_up(so + SR * D * (L->mx ? 1 : 2), A);
-  L->slot_xs = so; so = align_up(so + (L->mx ? SR * (D / 32) : 0), A);
+  L->slot_xs = so; so = align_up(so + (L->mx ? SR * L->xs_ld : 0), A);
   L->slot_h = so; so = align_up(so + SR * I * (L->mx ? 1 : 2), A);
-  L->slot_hs = so; so = align_up(so + (L->mx ? SR * (I / 32) : 0), A);
+  L->slot_hs = so; so = align_up(so + (L->mx ? SR * L->hs_ld : 0), A);
   L->slot_ab = so; so = align_up(so + (L->save ? SR * 2 * I * 2 : 0), A);
   L->slot_bytes = so;
   L->off_ring = o; o = align_up(o + L->slot_bytes * S, A);
@@ -133,9 +145,17 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->off_full_x = L->off_full_xs = L->off_full_h = L->off_full_hs = 0;
   if (L->unfused) {
     L->off_full_x = o; o = align_up(o + size_t(L->TK) * D * (L->mx ? 1 : 2), A);
-    L->off_full_xs = o; o = align_up(o + (L->mx ? size_t(L->TK) * (D / 32) : 0), A);
+    L->off_full_xs = o; o = align_up(o + (L->mx ? size_t(L->TK) * L->xs_ld : 0), A);
     L->off_full_h = o; o = align_up(o + size_t(L->TK) * I * (L->mx ? 1 : 2), A);
-    L->off_full_hs = o; o = align_up(o + (L->mx ? size_t(L->TK) * (I / 32) : 0), A);
+    L->off_full_hs = o; o = align_up(o + (L->mx ? size_t(L->TK) * L->hs_ld : 0), A);
+  }
+  L->off_wsg = L->off_wsu = L->off_wsd = 0;
+  if (L->repack_wg) {
+    L->off_wsg = o; o = align_up(o + size_t(nl) * I * L->wgs_ld, A);
+    L->off_wsu = o; o = align_up(o + size_t(nl) * I * L->wgs_ld, A);
+  }
+  if (L->repack_wd) {
+    L->off_wsd = o; o = align_up(o + size_t(nl) * D * L->wds_ld, A);
   }
   // backward regions (present when the forward saves for backward).  Row buffers are
   // indexed by routed row (at most T*k rows); the transposed panels hold, per local

@@ -1,19 +1,23 @@
-// Forward of the MoE layer on one GPU's share (bf16).
+// Forward of the MoE layer on one GPU's share, bf16 or MXFP8.
 //
 // Steps (Leiphone article on MoK, sections 02-03; news brief, design decisions):
 //   dispatch  — pull: row r of minibatch mb is copied from the token pool,
 //               X[perm[r] / k], into ring slot mb % S (the owner lays rows out itself,
-//               already grouped by expert);
+//               already grouped by expert); in MXFP8 mode the row is quantised on the
+//               way (e4m3 codes, one e8m0 scale per 32 values along D);
 //   GEMM1     — per expert segment: a = X W_gate^T, b = X W_up^T sharing the A tile,
-//               SwiGLU h = silu(a) * b in the epilogue, H written to the slot;
+//               SwiGLU h = silu(a) * b in the epilogue, H written to the slot (MXFP8:
+//               quantised along I in the same epilogue);
 //   GEMM2     — o = H W_down^T, pushed straight to its pair's row of the result buffer
 //               (the destination of every result is known from the schedule);
 //   combine   — the final weighted sum: y[t] = sum_j gate[t,j] * o[t*k+j] over local
 //               slots in ascending j, fp32 (multiply, then add), rounded once to bf16.
 //
 // Fused form (one persistent cooperative kernel): the first comm_cus workgroups move
-// data (dispatch + combine), the rest run MFMA tiles.  Handoff goes through device
-// counters with agent-scope release/acquire (each MI355X XCD has its own L2):
+// data (dispatch + combine), the rest run MFMA tiles.  Handoff data (slot rows, H, the
+// result rows) is written and read at device scope (each MI355X XCD has its own L2),
+// and the counters are relaxed device-scope atomics bumped after a workgroup's stores
+// have completed:
 //   ready[mb]  comm workgroups that finished gathering their share of mb;
 //   hdone[mb][i]  GEMM1 tiles finished for m-tile i of mb (GEMM2 of that m-tile waits);
 //   done[mb]   GEMM2 tiles finished for mb — frees slot mb % S and allows combining
@@ -34,8 +38,39 @@ struct FwdParams {
   Ptrs P;
   FwdArgs a;
   int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
-  int64_t slot_bytes, slot_x, slot_h, slot_ab;
+  int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
+  // MXFP8: scale row strides of X / H rows and of the weight scales the tiles read, and
+  // those weight scales (the caller's, or repacked copies in the workspace)
+  int64_t xs_ld, hs_ld, wgs_ld, wds_ld;
+  const uint8_t* wsg;
+  const uint8_t* wsu;
+  const uint8_t* wsd;
 };
+
+// MX operands of GEMM1 for m-tile row block A (codes) / As (scales) of local expert e.
+__device__ __forceinline__ MxOperands mx_ops_gemm1(const FwdParams& p, const uint8_t* A,
+                                                   const uint8_t* As, int e) {
+  const int64_t wsz = int64_t(p.I) * p.D;
+  MxOperands o;
+  o.A = A; o.As = As; o.as_ld = p.xs_ld;
+  o.w0 = static_cast<const uint8_t*>(p.a.wg) + e * wsz;
+  o.w0s = p.wsg + int64_t(e) * p.I * p.wgs_ld;
+  o.w1 = static_cast<const uint8_t*>(p.a.wu) + e * wsz;
+  o.w1s = p.wsu + int64_t(e) * p.I * p.wgs_ld;
+  o.ws_ld = p.wgs_ld;
+  return o;
+}
+__device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uint8_t* A,
+                                                   const uint8_t* As, int e) {
+  const int64_t wsz = int64_t(p.I) * p.D;
+  MxOperands o;
+  o.A = A; o.As = As; o.as_ld = p.hs_ld;
+  o.w0 = static_cast<const uint8_t*>(p.a.wd) + e * wsz;
+  o.w0s = p.wsd + int64_t(e) * p.D * p.wds_ld;
+  o.w1 = o.w0; o.w1s = o.w0s;
+  o.ws_ld = p.wds_ld;
+  return o;
+}
 
 // ------------------------------------------------------------------------------------
 // combine
@@ -80,21 +115,37 @@ __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
 // ------------------------------------------------------------------------------------
 // Unfused kernels: the same steps over full-size buffers, one launch per step.
 // ------------------------------------------------------------------------------------
+template <bool MX>
 __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
   const int R = int(p.P.hdr[kHdrR]);
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
-  uint16_t* X = reinterpret_cast<uint16_t*>(p.P.full_x);
-  for (int r = gw; r < R; r += nw)
-    wave_copy_row<false>(X + int64_t(r) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+  for (int r = gw; r < R; r += nw) {
+    const uint16_t* src = p.a.x + int64_t(p.P.perm[r] / p.k) * p.D;
+    if (MX)
+      wave_quant_row<false>(p.P.full_x + int64_t(r) * p.D, p.P.full_xs + int64_t(r) * p.xs_ld,
+                            src, p.D);
+    else
+      wave_copy_row<false>(reinterpret_cast<uint16_t*>(p.P.full_x) + int64_t(r) * p.D, src, p.D);
+  }
 }
 
+template <bool MX>
 __global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
   const int nt = blockIdx.x % p.nN1;
   const int f = blockIdx.x / p.nN1;
   const int mb = f / p.mt_max, i = f % p.mt_max;
   if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return;
   const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+  if (MX) {
+    TileAcc acc;
+    const MxOperands o = mx_ops_gemm1(p, p.P.full_x + int64_t(e.x) * p.D,
+                                      p.P.full_xs + int64_t(e.x) * p.xs_ld, e.z);
+    run_tile_mx<false>(true, o, e.y, nt * kBN1, p.D, p.I, acc);
+    epi_swiglu_mx<false>(acc, e.y, nt * kBN1, p.I, p.P.full_h + int64_t(e.x) * p.I, p.I,
+                         p.P.full_hs + int64_t(e.x) * p.hs_ld, p.hs_ld);
+    return;
+  }
   const uint16_t* X = reinterpret_cast<const uint16_t*>(p.P.full_x);
   uint16_t* H = reinterpret_cast<uint16_t*>(p.P.full_h);
   const int64_t wsz = int64_t(p.I) * p.D;
@@ -105,12 +156,21 @@ __global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
   epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, H + int64_t(e.x) * p.I, p.I, nullptr);
 }
 
+template <bool MX>
 __global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
   const int nt = blockIdx.x % p.nN2;
   const int f = blockIdx.x / p.nN2;
   const int mb = f / p.mt_max, i = f % p.mt_max;
   if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return;
   const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
+  if (MX) {
+    TileAcc acc;
+    const MxOperands o = mx_ops_gemm2(p, p.P.full_h + int64_t(e.x) * p.I,
+                                      p.P.full_hs + int64_t(e.x) * p.hs_ld, e.z);
+    run_tile_mx<false>(false, o, e.y, nt * kBN2, p.D, p.I, acc);
+    epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
+    return;
+  }
   const uint16_t* H = reinterpret_cast<const uint16_t*>(p.P.full_h);
   const int64_t wsz = int64_t(p.I) * p.D;
   TileAcc acc;
@@ -141,6 +201,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(FwdParams p) {
   }
 }
 
+template <bool MX>
 __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uint32_t* done) {
   uint32_t* hdr = p.P.hdr;
   const int n_mb = int(hdr[kHdrNmb]);
@@ -164,11 +225,17 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
     if (mb >= p.S) {
       if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr)) return;
     }
-    uint16_t* slot_x = reinterpret_cast<uint16_t*>(p.P.ring + s * p.slot_bytes + p.slot_x);
+    uint8_t* slot = p.P.ring + s * p.slot_bytes;
     const int lo = p.P.mb_start[mb], hi = p.P.mb_start[mb + 1];
-    for (int r = lo + gw; r < hi; r += nw)
-      wave_copy_row<true>(slot_x + int64_t(r - lo) * p.D, p.a.x + int64_t(p.P.perm[r] / p.k) * p.D,
-                          p.D);
+    for (int r = lo + gw; r < hi; r += nw) {
+      const uint16_t* src = p.a.x + int64_t(p.P.perm[r] / p.k) * p.D;
+      if (MX)
+        wave_quant_row<true>(slot + p.slot_x + int64_t(r - lo) * p.D,
+                             slot + p.slot_xs + int64_t(r - lo) * p.xs_ld, src, p.D);
+      else
+        wave_copy_row<true>(reinterpret_cast<uint16_t*>(slot + p.slot_x) + int64_t(r - lo) * p.D,
+                            src, p.D);
+    }
     wg_signal_add(ready + mb, 1);
     if (mb >= p.S) combine_mb(mb - p.S);
   }
@@ -178,6 +245,7 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
   }
 }
 
+template <bool MX>
 __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
                              uint32_t* done, uint32_t* hdone) {
   uint32_t* hdr = p.P.hdr;
@@ -212,6 +280,25 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     }
     const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
     const int r0 = e.x - lo;
+    if (MX) {
+      const int n0 = nt * (g1 ? kBN1 : kBN2);
+      TileAcc acc;
+      if (g1) {
+        const MxOperands o = mx_ops_gemm1(p, slot + p.slot_x + int64_t(r0) * p.D,
+                                          slot + p.slot_xs + int64_t(r0) * p.xs_ld, e.z);
+        run_tile_mx<true>(true, o, e.y, n0, p.D, p.I, acc);
+        epi_swiglu_mx<true>(acc, e.y, n0, p.I, slot + p.slot_h + int64_t(r0) * p.I, p.I,
+                            slot + p.slot_hs + int64_t(r0) * p.hs_ld, p.hs_ld);
+        wg_signal_add(hd, 1);
+      } else {
+        const MxOperands o = mx_ops_gemm2(p, slot + p.slot_h + int64_t(r0) * p.I,
+                                          slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
+        run_tile_mx<true>(false, o, e.y, n0, p.D, p.I, acc);
+        epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+        wg_signal_add(done + mb, 1);
+      }
+      continue;
+    }
     const uint16_t* A = g1 ? slot_x + int64_t(r0) * p.D : slot_h + int64_t(r0) * p.I;
     const uint16_t* w0 = reinterpret_cast<const uint16_t*>(g1 ? p.a.wg : p.a.wd) + e.z * wsz;
     const uint16_t* w1 = reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz;
@@ -230,13 +317,28 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
   }
 }
 
+template <bool MX>
 __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   uint32_t* ready = p.P.sync;
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
   const int C = p.a.comm_cus;
-  if (int(blockIdx.x) < C) comm_role(p, blockIdx.x, C, ready, done);
-  else compute_role(p, C, ready, done, hdone);
+  if (int(blockIdx.x) < C) comm_role<MX>(p, blockIdx.x, C, ready, done);
+  else compute_role<MX>(p, C, ready, done, hdone);
+}
+
+// Weight scales with a row stride of K / 32 bytes, repacked to the tile's stride of one
+// dword per 128-wide K step (used when K % 128 == 64); the pad byte is 127 (scale 1)
+// and is never multiplied.
+__global__ __launch_bounds__(256) void k_mx_repack(const uint8_t* __restrict__ src, int64_t rows,
+                                                   int src_ld, uint8_t* __restrict__ dst,
+                                                   int dst_ld) {
+  const int64_t n = rows * dst_ld;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / dst_ld;
+    const int c = int(i - r * dst_ld);
+    dst[i] = c < src_ld ? src[r * src_ld + c] : uint8_t(127);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -250,41 +352,65 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.S = int(L.S); p.mt_max = int(L.mt_max); p.nN1 = int(L.nN1); p.nN2 = int(L.nN2);
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
-  p.slot_h = int64_t(L.slot_h); p.slot_ab = int64_t(L.slot_ab);
+  p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
+  p.slot_ab = int64_t(L.slot_ab);
+  p.xs_ld = L.xs_ld; p.hs_ld = L.hs_ld; p.wgs_ld = L.wgs_ld; p.wds_ld = L.wds_ld;
+  p.wsg = L.repack_wg ? P.wsg : a.sg;
+  p.wsu = L.repack_wg ? P.wsu : a.su;
+  p.wsd = L.repack_wd ? P.wsd : a.sd;
   return p;
 }
 
-int fused_grid_size() {
+static int fused_grid_size(const void* kernel) {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k_fwd_fused),
-                                                   kThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess)
     return 0;
   return cus * occ;
 }
 
 mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st) {
   FwdParams p = make_params(L, P, a);
+  if (L.repack_wg) {
+    const int64_t rows = L.nl * L.I;
+    const unsigned g = unsigned(std::min<int64_t>((rows * L.wgs_ld + 255) / 256, 4096));
+    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.sg, rows, int(L.D / 32), P.wsg,
+                       int(L.wgs_ld));
+    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.su, rows, int(L.D / 32), P.wsu,
+                       int(L.wgs_ld));
+  }
+  if (L.repack_wd) {
+    const int64_t rows = L.nl * L.D;
+    const unsigned g = unsigned(std::min<int64_t>((rows * L.wds_ld + 255) / 256, 4096));
+    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.sd, rows, int(L.I / 32), P.wsd,
+                       int(L.wds_ld));
+  }
   if (L.unfused) {
     const unsigned gw = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
-    hipLaunchKernelGGL(k_gather_all, dim3(gw), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_gemm1_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN1)), dim3(kThreads),
-                       0, st, p);
-    hipLaunchKernelGGL(k_gemm2_all, dim3(unsigned(L.n_mb_max * L.mt_max * L.nN2)), dim3(kThreads),
-                       0, st, p);
+    const dim3 g1(unsigned(L.n_mb_max * L.mt_max * L.nN1)), g2(unsigned(L.n_mb_max * L.mt_max * L.nN2));
+    if (L.mx) {
+      hipLaunchKernelGGL(k_gather_all<true>, dim3(gw), dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_gemm1_all<true>, g1, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL(k_gemm2_all<true>, g2, dim3(kThreads), 0, st, p);
+    } else {
+      hipLaunchKernelGGL(k_gather_all<false>, dim3(gw), dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_gemm1_all<false>, g1, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL(k_gemm2_all<false>, g2, dim3(kThreads), 0, st, p);
+    }
     hipLaunchKernelGGL(k_combine_all, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
                        dim3(256), 0, st, p);
     return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
   }
-  const int grid = fused_grid_size();
+  const void* kern = L.mx ? reinterpret_cast<const void*>(k_fwd_fused<true>)
+                          : reinterpret_cast<const void*>(k_fwd_fused<false>);
+  const int grid = fused_grid_size(kern);
   if (grid <= 0) return MOK_E_DEVICE;
   if (a.comm_cus >= grid) return MOK_E_SHAPE;
   hipLaunchKernelGGL(k_fwd_prep, dim3(64), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return MOK_E_LAUNCH;
   void* args[] = {&p};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_fused), dim3(grid),
-                                 dim3(kThreads), args, 0, st) != hipSuccess)
+  if (hipLaunchCooperativeKernel(kern, dim3(grid), dim3(kThreads), args, 0, st) != hipSuccess)
     return MOK_E_LAUNCH;
   return MOK_OK;
 }

@@ -39,40 +39,68 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
   return sign | code;
 }
 
-// One lane quantises one 32-element block of bf16: src points at the block, codes at
-// its 32 output bytes, returns the scale byte.
-__device__ __forceinline__ uint8_t mx_block_bf16(const uint16_t* __restrict__ src,
-                                                 uint8_t* __restrict__ codes) {
+// Maximum over each group of 4 (quad) or 16 (DPP row) consecutive lanes, with DPP lane
+// moves: quad_perm [1,0,3,2] and [2,3,0,1], then row_half_mirror and row_mirror, which
+// pair quad 0 with quad 1 and the two halves of a row.  Every lane of a group must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const float t = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+  return fmaxf(v, t);
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = dpp_max_step<0xB1>(v);  // quad_perm [1,0,3,2]
+  return dpp_max_step<0x4E>(v);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  return dpp_max_step<0x140>(v);  // row_mirror
+}
+
+// Eight e4m3 codes of v[0..7] * 2^-n, packed little-endian.
+__device__ __forceinline__ uint64_t e4m3_pack8(const float (&v)[8], int n) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= e4m3_rne(ldexpf(v[j], -n)) << (8 * j);
+    hi |= e4m3_rne(ldexpf(v[4 + j], -n)) << (8 * j);
+  }
+  return uint64_t(lo) | (uint64_t(hi) << 32);
+}
+
+// One wave quantises one row of D bf16 values (D a multiple of 32) into MX: codes[0..D)
+// and scales[0..D/32).  Lane l handles 8-element chunks c = l, l + 64, ...; the 4
+// lanes of a quad hold one 32-element block, whose largest magnitude they share over
+// DPP.  With kCoherent the outputs are written at device scope (handoff data).
+template <bool kCoherent>
+__device__ __forceinline__ void wave_quant_row(uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ src, int D) {
+  const int lane = threadIdx.x & 63;
+  const int nch = D >> 3;  // a multiple of 4: quads are whole or absent
   const v4u* s = reinterpret_cast<const v4u*>(src);
-  v4u v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = s[i];
-  float f[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+  for (int c = lane; c < nch; c += 64) {
+    const v4u u = s[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float v[8];
+    float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f[i * 8 + 2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
-      f[i * 8 + 2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
+      v[2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
+      v[2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    amax = quad_max(amax);
+    const int n = mx_shared_exp(amax);
+    const uint64_t packed = e4m3_pack8(v, n);
+    if (kCoherent) st_dev_u64(codes + int64_t(c) * 8, packed);
+    else *reinterpret_cast<uint64_t*>(codes + int64_t(c) * 8) = packed;
+    if ((lane & 3) == 0) {
+      if (kCoherent) st_dev_u8(scales + (c >> 2), uint8_t(n + 127));
+      else scales[c >> 2] = uint8_t(n + 127);
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  const int n = mx_shared_exp(amax);
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t wd = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wd |= e4m3_rne(ldexpf(f[i * 4 + j], -n)) << (8 * j);
-    out[i] = wd;
-  }
-  v4u* d = reinterpret_cast<v4u*>(codes);
-  d[0] = v4u{out[0], out[1], out[2], out[3]};
-  d[1] = v4u{out[4], out[5], out[6], out[7]};
-  return uint8_t(n + 127);
 }
 
 }  // namespace mok

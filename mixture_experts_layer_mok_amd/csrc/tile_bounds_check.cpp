@@ -2,9 +2,15 @@
 // operand, for given hidden (D) and intermediate (I) sizes, over every tile shape the
 // kernels launch: GEMM1 (A = [rows, D], B0 = W_gate, B1 = W_up: [I, D], columns n0..n0+127
 // of both), GEMM2 (A = [rows, I], B0 = B1 = W_down: [D, I], columns n0..n0+255), any
-// row count 1..256, and that the paired layout covers each gate/up row exactly once.  Built with the host compiler only; exits non-zero on a violation.
+// row count 1..256, and that the paired layout covers each gate/up row exactly once.
+// The MXFP8 tile (1-byte codes, 128-byte K steps, a last half step when K % 128 == 64,
+// one scale dword per row and step) is checked the same way: every code load stays
+// inside its own row's K bytes, every scale load inside its row of scales, and every
+// valid offset below 2^31 (the range of its buffer resource; setting bit 31 makes a load
+// out of range).  Built with the host compiler only; exits non-zero on a violation.
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <initializer_list>
 
 #include "tile_geom.h"
@@ -29,6 +35,38 @@ static int check(const char* what, int layout, int K, int64_t lda, int64_t ldb, 
   return bad;
 }
 
+static int check_mx(const char* what, int layout, int K, int64_t lda, int64_t as_ld, int rows,
+                    int64_t ldb, int64_t bs_ld, int N, int n0, int nb1) {
+  const int nk = (K + 127) / 128;
+  const bool half_last = K % 128 != 0;
+  int bad = 0;
+  for (int ks = 0; ks < nk; ++ks) {
+    const bool half = half_last && ks == nk - 1;
+    for (int w = 0; w < mok::geom::kWaves; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int64_t adj = (half && !mok::geom::mx_chunk_in_half(w, l)) ? -64 : 0;
+        for (int p = 0; p < mok::geom::kLoads; ++p) {
+          const int ra = std::min(mok::geom::dma_row(p, w, l), rows - 1);
+          const int64_t oa = mok::geom::a_offset(p, w, l, rows, lda / 2) + adj + 128 * ks;
+          if (oa < ra * lda || oa + 16 > ra * lda + K || oa + 16 > (int64_t(1) << 31)) ++bad;
+          const int rb = mok::geom::b_row(layout, p, w, l, n0, nb1, N);
+          const int64_t ob = mok::geom::b_offset(layout, p, w, l, n0, nb1, N, ldb / 2) + adj +
+                             128 * ks;
+          if (rb < 0 || rb >= N || ob < rb * ldb || ob + 16 > rb * ldb + K ||
+              ob + 16 > (int64_t(1) << 31))
+            ++bad;
+        }
+        if (4 * ks + 4 > as_ld || 4 * ks + 4 > bs_ld || as_ld % 4 || bs_ld % 4) ++bad;
+        const int64_t sa = mok::geom::mx_a_scale_offset(w, l, rows, as_ld) + 4 * ks;
+        if (sa < 0 || sa + 4 > int64_t(rows) * as_ld) ++bad;
+        const int64_t sb = mok::geom::mx_b_scale_offset(layout, w, l, n0, nb1, N, bs_ld) + 4 * ks;
+        if (sb < 0 || sb + 4 > int64_t(N) * bs_ld) ++bad;
+      }
+  }
+  if (bad) std::printf("%s: %d bad offsets (K=%d N=%d n0=%d rows=%d)\n", what, bad, K, N, n0, rows);
+  return bad;
+}
+
 int main(int argc, char** argv) {
   if (argc != 3) {
     std::fprintf(stderr, "usage: %s D I\n", argv[0]);
@@ -47,6 +85,17 @@ int main(int argc, char** argv) {
       bad += check("dh", mok::geom::kSplit, D, D, D, I, n0, n0 + 128, rows);
     for (int n0 = 0; n0 < D; n0 += kBN2)
       bad += check("dx", mok::geom::kSplit, 2 * I, 2 * I, 2 * I, D, n0, n0 + 128, rows);
+    // MXFP8 forward: padded scale rows for X / H, the caller's K / 32 weight scales when
+    // K % 128 == 0 and a padded repack otherwise
+    {
+      const int64_t xs_ld = (D + 127) / 128 * 4, hs_ld = (I + 127) / 128 * 4;
+      const int64_t wgs_ld = D % 128 ? xs_ld : D / 32, wds_ld = I % 128 ? hs_ld : I / 32;
+      for (int n0 = 0; n0 < I; n0 += kBN1)
+        bad += check_mx("gemm1-mx", mok::geom::kPaired, D, D, xs_ld, rows, D, wgs_ld, I, n0, n0);
+      for (int n0 = 0; n0 < D; n0 += kBN2)
+        bad += check_mx("gemm2-mx", mok::geom::kSplit, I, I, hs_ld, rows, I, wds_ld, D, n0,
+                        n0 + 128);
+    }
     const int TKP = 4096;
     for (int K : {64, 1024, 4096})
       for (int n0 = 0; n0 < I; n0 += kBN2)

@@ -2,7 +2,9 @@
 // copies and reductions, the grouped-GEMM tile runner and its epilogues.
 #pragma once
 #include "gemm_bf16.h"
+#include "gemm_mx.h"
 #include "launch.h"
+#include "mx.h"
 
 namespace mok {
 
@@ -124,6 +126,83 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// Epilogue of the MXFP8 GEMM1: SwiGLU as in epi_swiglu, then H is MX-quantised along I.
+// A 32-column MX block [n0 + 32 wn, +32) is exactly MFMA blocks j = 0, 1 of wave column
+// wn: for one row, the 16 gate lanes of a DPP row hold its 32 h values (two per lane),
+// so the block maximum is a 16-lane DPP reduction.  Writes codes Hc[row * ldh + col] and
+// scales Hs[row * hs_ld + col / 32].  I is a multiple of 32, so a block is wholly inside
+// or outside [0, I).
+template <bool kCoherent>
+__device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int n0, int I,
+                                              uint8_t* Hc, int64_t ldh, uint8_t* Hs,
+                                              int64_t hs_ld) {
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int wn = (tid >> 6) & 3;
+  const bool gate_lane = (lane & 16) == 0;
+  const int cb = n0 + 32 * wn;
+  if (cb >= I) return;  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float x0 = acc.c[i][0][v], x1 = acc.c[i][1][v];
+      const float y0 = __shfl_xor(x0, 16), y1 = __shfl_xor(x1, 16);
+      const float h0 = silu_f(x0) * y0, h1 = silu_f(x1) * y1;
+      const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+      const int n = mx_shared_exp(amax);
+      const int row = acc_row(tid, i, v);
+      if (row < rows && gate_lane) {
+        const uint8_t c0 = uint8_t(e4m3_rne(ldexpf(h0, -n)));
+        const uint8_t c1 = uint8_t(e4m3_rne(ldexpf(h1, -n)));
+        uint8_t* hr = Hc + int64_t(row) * ldh + cb + (lane & 15);
+        if (kCoherent) {
+          st_dev_u8(hr, c0);
+          st_dev_u8(hr + 16, c1);
+        } else {
+          hr[0] = c0;
+          hr[16] = c1;
+        }
+        if ((lane & 15) == 0) {
+          uint8_t* sp = Hs + int64_t(row) * hs_ld + (cb >> 5);
+          if (kCoherent) st_dev_u8(sp, uint8_t(n + 127));
+          else *sp = uint8_t(n + 127);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one block row at a time: few live registers
+  }
+}
+
+// MXFP8 operands of one tile of either GEMM:
+//   GEMM1: A = dispatched X codes [rows, D] (scales xs_ld bytes per row), B = W_gate /
+//          W_up codes, rows n0.., K = D;
+//   GEMM2: A = H codes [rows, I] (scales hs_ld per row), B = W_down codes rows
+//          n0..n0+255, K = I.
+struct MxOperands {
+  const uint8_t* A;
+  const uint8_t* As;
+  int64_t as_ld;
+  const uint8_t* w0;
+  const uint8_t* w0s;
+  const uint8_t* w1;
+  const uint8_t* w1s;
+  int64_t ws_ld;
+};
+
+template <bool kCoherent>
+__device__ __forceinline__ void run_tile_mx(bool gemm1, const MxOperands& o, int rows, int n0,
+                                            int D, int I, TileAcc& acc) {
+  MxSrc src;
+  if (gemm1)
+    mx_src_init(src, geom::kPaired, o.A, o.As, D, o.as_ld, rows, o.w0, o.w0s, o.w1, o.w1s, D,
+                o.ws_ld, n0, n0, I, D);
+  else
+    mx_src_init(src, geom::kSplit, o.A, o.As, I, o.as_ld, rows, o.w0, o.w0s, o.w0, o.w0s, I,
+                o.ws_ld, n0, n0 + 128, D, I);
+  mx_gemm<kCoherent>(src, gemm1 ? D : I, acc);
 }
 
 // Operands of one tile of either GEMM (one K loop serves both).

@@ -91,6 +91,14 @@ def test_entry_points_fail_before_touching_memory():
     ok, need_mx = _ws_code(dmx)
     assert lib.mok_moe_fwd(ctypes.byref(dmx), *args, None, None, None, FAKE, FAKE, need_mx,
                            None) == L.MOK_E_NULL
+    # misaligned operands are refused before anything is enqueued
+    assert lib.mok_moe_fwd(dp, FAKE + 2, *args[1:], None, None, None, FAKE, FAKE, need,
+                           None) == L.MOK_E_SHAPE
+    assert lib.mok_moe_fwd(dp, *args, None, None, None, FAKE + 8, FAKE, need, None) == \
+        L.MOK_E_SHAPE
+    assert lib.mok_moe_fwd(ctypes.byref(dmx), *args, FAKE + 1, FAKE, FAKE, FAKE, FAKE, need_mx,
+                           None) == L.MOK_E_SHAPE
+    assert lib.mok_quantize_mx(FAKE + 4, 4, 64, FAKE, FAKE, None) == L.MOK_E_SHAPE
     assert lib.mok_quantize_mx(FAKE, 4, 48, FAKE, FAKE, None) == L.MOK_E_SHAPE
     assert lib.mok_quantize_mx(None, 4, 64, FAKE, FAKE, None) == L.MOK_E_NULL
     assert lib.mok_read_device_status(None, None, None) == L.MOK_E_NULL
