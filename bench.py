@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
@@ -118,6 +119,11 @@ def setup(cfg, unfused, save, device):
         t[n] = bf16_tensor(d[n + "_bits"], device)
     flags = (L.MOK_FLAG_UNFUSED if unfused else 0) | (L.MOK_FLAG_SAVE_FOR_BWD if save else 0)
     layer = MoKLayer(L.desc_from_config(cfg, flags=flags), device=device)
+    if cfg.precision == L.MOK_PREC_MXFP8:
+        # weights are quantised once, before the layer (not part of a step)
+        for n in ("wg", "wu", "wd"):
+            t[n], t["s" + n[1]] = layer.quantize_weights(t[n])
+        torch.cuda.synchronize()
     return d, t, layer
 
 
@@ -134,7 +140,8 @@ def time_layer(cfg, t, layer, steps, warmup, with_bwd):
         layer.schedule(t["ids"])
         if ev is not None:
             ev[1].record(stream)
-        layer.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"], y=y)
+        layer.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"],
+                      scales=(t.get("sg"), t.get("su"), t.get("sd")), y=y)
         if ev is not None:
             ev[2].record(stream)
         if with_bwd:
@@ -179,7 +186,8 @@ def routed_rows(cfg, ids):
 
 
 def sweep(args):
-    """Forward time over minibatch sizes and comm-CU counts on the config-3 shape, against
+    """Forward time over minibatch sizes and comm-CU counts on the config-3 (bf16) or
+    config-4 (MXFP8, Zipf routing) workload, against
     the two-waves lower bound for a 256 x 256 tile: each GEMM should see at least two full
     waves of tiles, 2 * C_compute * 256 * 256 / (2 I) rows for GEMM1."""
     import torch
@@ -188,26 +196,53 @@ def sweep(args):
     from mixture_experts_layer_mok_amd import gen
     L.load()
     dev = torch.device("cuda:0")
-    base = gen.CONFIGS[3]
+    base = gen.CONFIGS[args.config if args.config in (3, 4) else 3]
     d, t, _ = setup(base, False, False, dev)
     R = routed_rows(base, d["ids"])
     from mixture_experts_layer_mok_amd.layer import MoKLayer
     from mixture_experts_layer_mok_amd.tuning import layer_two_wave_min_rows
     cus = L.mok_device_cus()
-    for comm in (16, 32, 48, 64):
-        for M in (512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 6144, 8192):
+    mx = base.precision == L.MOK_PREC_MXFP8
+    comms = (32, 64, 96, 128) if mx else (16, 32, 48, 64)
+    Ms = (1024, 2048, 4096, 8192) if mx else (512, 1024, 1536, 2048, 2560, 3072, 3584, 4096,
+                                              6144, 8192)
+    for comm in comms:
+        for M in Ms:
             cfg = base.replace(M=M, comm_cus=comm)
             layer = MoKLayer(L.desc_from_config(cfg), device=dev)
             r = time_layer(cfg, t, layer, args.steps, args.warmup, False)
             fwd = float(np.median(r["fwd_ms"]))
             m_min = layer_two_wave_min_rows(cus, comm, cfg.I)
-            print(json.dumps({"sweep": "minibatch", "M": M, "comm_cus": comm,
+            print(json.dumps({"sweep": "minibatch", "config": base.name, "M": M, "comm_cus": comm,
                               "fwd_ms_median": round(fwd, 4),
                               "fwd_tflops": round(6.0 * cfg.D * cfg.I * R / fwd / 1e9, 1),
                               "two_wave_min_rows": round(m_min), "above_two_waves": M >= m_min}),
                   flush=True)
             del layer
             torch.cuda.empty_cache()
+
+
+def mx_forward_figure(args):
+    """The MXFP8 forward on the Zipf-skewed config-4 workload (the pages' MXFP8 mode),
+    timed like the main line; reported beside the bf16 step."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import gen
+    cfg = gen.CONFIGS[4]
+    dev = torch.device("cuda:0")
+    d, t, layer = setup(cfg, False, False, dev)
+    R = routed_rows(cfg, d["ids"])
+    log(f"timing the MXFP8 forward ({R} routed rows)")
+    r = time_layer(cfg, t, layer, args.steps, args.warmup, False)
+    fwd = float(np.mean(r["fwd_ms"]))
+    tf = 6.0 * cfg.D * cfg.I * R / (fwd * 1e-3) / 1e12
+    res = {"workload": f"{cfg.name}: Zipf(1.2) routing, {R} routed rows",
+           "schedule_ms": stats(r["sched_ms"]), "fwd_ms": stats(r["fwd_ms"]),
+           "fwd_tflops": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+           "routed_rows_per_s": round(R / (r["ms_per_step"] * 1e-3), 1)}
+    del layer, t
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -231,7 +266,8 @@ def main():
     cfg = gen.CONFIGS[args.config]
     over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}
     cfg = cfg.replace(**over)
-    with_bwd = not args.fwd_only
+    mx = cfg.precision == L.MOK_PREC_MXFP8
+    with_bwd = not args.fwd_only and not mx  # the MXFP8 backward is not built
     dev = torch.device("cuda:0")
     d, t, layer = setup(cfg, args.unfused, with_bwd, dev)
     R = routed_rows(cfg, d["ids"])
@@ -243,9 +279,11 @@ def main():
     fwd_ms = float(np.mean(r["fwd_ms"]))
     achieved = flops_fwd / (fwd_ms * 1e-3) / 1e12
     mode = "unfused" if args.unfused else "fused"
+    prec = "mxfp8" if mx else "bf16"
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     out = {
-        "metric": "MoE layer fwd+bwd TFLOPS (bf16)" if with_bwd else
-                  "MoE layer forward TFLOPS (bf16)",
+        "metric": f"MoE layer fwd+bwd TFLOPS ({prec})" if with_bwd else
+                  f"MoE layer forward TFLOPS ({prec})",
         "value": round((flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -255,7 +293,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3+e8m0 (fp32 accumulate)" if mx else "bf16",
         "data": "synthetic (seeded normal draws at the layer's real shape)",
         "config": {"workload": f"{cfg.name}: pool T={cfg.T} x D={cfg.D}, I={cfg.I}, "
                                f"E={cfg.E} (experts {cfg.e0}..{cfg.e0 + cfg.n_local - 1} local), "
@@ -279,8 +317,10 @@ def main():
                                  and cfg.M == 2048 and cfg.S == 4 and cfg.comm_cus == 32) else None
     out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else
                        "forward (unfused launches)", "achieved": round(achieved, 2),
-                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+                       "peak": peak, "unit": "TFLOP/s",
+                       "frac": round(achieved / peak, 4), "traffic": traffic}
+    if not mx and not args.no_mx and args.config == 5:
+        out["mxfp8_fwd"] = mx_forward_figure(args)
     if not args.no_cpu_baseline:
         import oracle as O
         log("timing the float64 oracle on the host")

@@ -15,8 +15,12 @@
 // that every MFMA operand is K-contiguous, and each dW tile has one owner and one K
 // order: no atomics, bitwise reproducible.
 //
-// This file holds the path as separate kernels; the gate/up pre-activations are
-// recomputed from the dispatched rows (replay of GEMM1).
+// This file holds the path as separate kernels.  The gate/up pre-activations a, b come
+// from the forward where it still holds them and are recomputed otherwise (replay of
+// GEMM1), following the reverse ring traversal: after a fused forward the ring slots
+// hold the last S minibatches (their a, b are copied out), and only minibatches whose
+// slot was recycled, mb < n_mb - S, are replayed.  An unfused forward that saves for
+// the backward writes a, b of every row, and nothing is replayed.
 #include <algorithm>
 
 #include "tile_ops.h"
@@ -26,8 +30,10 @@ namespace mok {
 struct BwdParams {
   Ptrs P;
   BwdArgs a;
-  int T, D, I, k, nl, mt_max, nDt, nIt, nNdh, n_mb_max;
+  int T, D, I, k, nl, mt_max, nDt, nIt, nNdh, n_mb_max, S;
   int64_t TKP;
+  int64_t slot_bytes, slot_ab;
+  int ab_saved;  // 1: the forward wrote a, b of every row (unfused); 0: ring only (fused)
 };
 
 // ------------------------------------------------------------------------------------
@@ -167,10 +173,31 @@ __device__ __forceinline__ bool tile_of(const BwdParams& p, int f, int4& e) {
 }
 
 // Replay of GEMM1: gate/up pre-activations of every routed row into bab [R, 2I].
+// a, b of the minibatches still resident in the ring after a fused forward: slot mb % S
+// holds rows mb_start[mb] .. mb_start[mb + 1] of mb >= n_mb - S.  One wave per row.
+__global__ __launch_bounds__(256) void k_bwd_ab_resident(BwdParams p) {
+  const int n_mb = int(p.P.hdr[kHdrNmb]);
+  const int mb0 = n_mb > p.S ? n_mb - p.S : 0;
+  const int lo = n_mb > 0 ? p.P.mb_start[mb0] : 0, hi = int(p.P.hdr[kHdrR]);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  int mb = mb0;
+  for (int r = lo + gw; r < hi; r += nw) {
+    while (mb + 1 < n_mb && p.P.mb_start[mb + 1] <= r) ++mb;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.P.ring + (mb % p.S) * p.slot_bytes +
+                                                            p.slot_ab) +
+                          int64_t(r - p.P.mb_start[mb]) * 2 * p.I;
+    wave_copy_row<false>(p.P.bab + int64_t(r) * 2 * p.I, src, 2 * p.I);
+  }
+}
+
+// Replay of GEMM1 for the m-tiles of minibatches whose a, b are no longer held.
 __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
   int4 e;
   const int nN1 = (p.I + kBN1 - 1) / kBN1;
-  if (!tile_of(p, blockIdx.x / nN1, e)) return;
+  const int f = blockIdx.x / nN1;
+  if (!tile_of(p, f, e)) return;
+  if (p.ab_saved || f / p.mt_max >= int(p.P.hdr[kHdrNmb]) - p.S) return;
   const int nt = blockIdx.x % nN1;
   const int64_t wsz = int64_t(p.I) * p.D;
   TileAcc acc;
@@ -301,6 +328,10 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.nIt = int((L.I + kBN2 - 1) / kBN2);
   p.nNdh = int(L.nNdh);
   p.TKP = int64_t(L.TKP);
+  p.S = int(L.S);
+  p.slot_bytes = int64_t(L.slot_bytes);
+  p.slot_ab = int64_t(L.slot_ab);
+  p.ab_saved = L.unfused ? 1 : 0;
   const unsigned rows_grid = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
   const unsigned ftiles = unsigned(L.n_mb_max * L.mt_max);
   const unsigned nN1 = unsigned((L.I + kBN1 - 1) / kBN1);
@@ -312,6 +343,8 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
                      st, p);
   hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
                      p);
+  if (!L.unfused)
+    hipLaunchKernelGGL(k_bwd_ab_resident, dim3(rows_grid), dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_bwd_gemm1, dim3(ftiles * nN1), dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dh, dim3(ftiles * unsigned(p.nNdh)), dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dx, dim3(ftiles * unsigned(p.nDt)), dim3(kThreads), 0, st, p);

@@ -22,10 +22,14 @@
 //   hdone[mb][i]  GEMM1 tiles finished for m-tile i of mb (GEMM2 of that m-tile waits);
 //   done[mb]   GEMM2 tiles finished for mb — frees slot mb % S and allows combining
 //              the tokens whose last local row lies in mb.
-// Compute workgroups take tiles from an atomic ticket in minibatch order (GEMM1 tiles
-// of mb, then its GEMM2 tiles), so every wait is on work with a smaller ticket or on a
-// comm step that only depends on such work: no cycle, given all workgroups are
-// co-resident (cooperative launch).  A token is combined by the comm workgroup that
+// Compute workgroups take tiles from an atomic ticket.  Tickets run in blocks
+// j = 0, 1, ...: block j holds the GEMM1 tiles of minibatch j followed by the GEMM2
+// tiles of minibatch j - L, with a lookahead L = 1 when the ring has two slots or more
+// (L = 0 otherwise), so a GEMM2 tile's H was normally finished a whole block earlier.
+// Every wait is on work with a smaller ticket (GEMM2 of mb on GEMM1 of mb) or on a
+// comm step that only depends on such work (the gather of mb on GEMM2 of mb - S, in
+// block mb - S + L < mb): no cycle, given all workgroups are co-resident (cooperative
+// launch).  A token is combined by the comm workgroup that
 // owns its highest local row, right after that row's minibatch is done, so most of the
 // combine overlaps later minibatches' GEMMs.
 #include <algorithm>
@@ -75,40 +79,71 @@ __device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uin
 // ------------------------------------------------------------------------------------
 // combine
 // ------------------------------------------------------------------------------------
-// y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.
+// y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.  Each lane
+// owns 16-byte chunks of the row; two chunks and up to four slots are loaded before any
+// is accumulated (the sum itself runs in ascending j per element).
 template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
+  constexpr int kJ = 4;
   const int lane = threadIdx.x & 63;
   const int D = p.D, k = p.k;
+  const int nch = D >> 3;
   const int64_t q0 = int64_t(t) * k;
   const int32_t my_pos = lane < k ? p.P.pos[q0 + lane] : -1;
   const float my_g = lane < k ? p.a.gates[q0 + lane] : 0.f;
   const uint64_t has = __ballot(my_pos >= 0);
   v4u* yrow = reinterpret_cast<v4u*>(p.a.y + int64_t(t) * D);
-  for (int c = lane; c < (D >> 3); c += 64) {
-    float acc[8];
+  for (int c0 = lane; c0 < nch; c0 += 128) {
+    const bool two = c0 + 64 < nch;
+    float acc[2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     uint64_t m = has;
     while (m) {
-      const int j = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const float g = __shfl(my_g, j);
-      const v4u* src = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + j) * D) + c;
-      const v4u v = kCoherent ? ld_dev_b128(src) : *src;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      int js[kJ];
+      v4u v[kJ][2];
+      int n = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = __fadd_rn(acc[2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
-        acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
+      for (int u = 0; u < kJ; ++u) {
+        js[u] = -1;
+        if (m) {
+          js[u] = __ffsll((unsigned long long)m) - 1;
+          m &= m - 1;
+          n = u + 1;
+          const v4u* src = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + js[u]) * D) + c0;
+          v[u][0] = kCoherent ? ld_dev_b128(src) : *src;
+          if (two) v[u][1] = kCoherent ? ld_dev_b128(src + 64) : src[64];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kJ; ++u) {
+        if (u >= n) break;
+        const float g = __shfl(my_g, js[u]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w[4] = {v[u][h].x, v[u][h].y, v[u][h].z, v[u][h].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[h][2 * e] =
+                __fadd_rn(acc[h][2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
+            acc[h][2 * e + 1] =
+                __fadd_rn(acc[h][2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
+          }
+        }
       }
     }
-    v4u out;
-    out.x = pack_bf16x2(acc[0], acc[1]);
-    out.y = pack_bf16x2(acc[2], acc[3]);
-    out.z = pack_bf16x2(acc[4], acc[5]);
-    out.w = pack_bf16x2(acc[6], acc[7]);
-    yrow[c] = out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      v4u out;
+      out.x = pack_bf16x2(acc[h][0], acc[h][1]);
+      out.y = pack_bf16x2(acc[h][2], acc[h][3]);
+      out.z = pack_bf16x2(acc[h][4], acc[h][5]);
+      out.w = pack_bf16x2(acc[h][6], acc[h][7]);
+      yrow[c0 + 64 * h] = out;
+    }
   }
 }
 
@@ -153,7 +188,9 @@ __global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
   run_tile<false>(true, X + int64_t(e.x) * p.D, e.y,
                   reinterpret_cast<const uint16_t*>(p.a.wg) + e.z * wsz,
                   reinterpret_cast<const uint16_t*>(p.a.wu) + e.z * wsz, nt * kBN1, p.D, p.I, acc);
-  epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, H + int64_t(e.x) * p.I, p.I, nullptr);
+  // saving for the backward: a, b of every row go straight to its row buffer
+  epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, H + int64_t(e.x) * p.I, p.I,
+                    p.save ? p.P.bab + int64_t(e.x) * 2 * p.I : nullptr);
 }
 
 template <bool MX>
@@ -253,22 +290,35 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
   const int n_mb = int(hdr[kHdrNmb]);
   const int64_t wsz = int64_t(p.I) * p.D;
   __shared__ uint32_t s_ticket;
-  int mb = 0;
+  const int L = p.S >= 2 ? 1 : 0;
+  const uint32_t per_mt = uint32_t(p.nN1 + p.nN2);
+  // m-tiles in minibatches [0, i), and the first ticket of block j
+  auto mt_before = [&](int i) {
+    i = i < 0 ? 0 : (i > n_mb ? n_mb : i);
+    return uint32_t(p.P.tile_base[i]) / per_mt;
+  };
+  auto block_start = [&](int j) {
+    return uint32_t(p.nN1) * mt_before(j) + uint32_t(p.nN2) * mt_before(j - L);
+  };
+  int j = 0;
   while (true) {
     if (threadIdx.x == 0) s_ticket = fetch_add_relaxed(hdr + kHdrFwdTicket, 1u);
     __syncthreads();
     const uint32_t tk = s_ticket;
     __syncthreads();
     if (tk >= total || aborted(hdr)) break;
-    while (mb + 1 < n_mb && uint32_t(p.P.tile_base[mb + 1]) <= tk) ++mb;
-    const int q = int(tk - uint32_t(p.P.tile_base[mb]));
+    while (j + 1 < n_mb + L && block_start(j + 1) <= tk) ++j;
+    const uint32_t q0 = tk - block_start(j);
+    const uint32_t g1n = j < n_mb ? uint32_t(p.P.mt_cnt[j] * p.nN1) : 0u;
+    const bool g1 = q0 < g1n;
+    const int mb = g1 ? j : j - L;
+    const int q = int(g1 ? q0 : q0 - g1n + uint32_t(p.P.mt_cnt[mb] * p.nN1));
     const int nmt = p.P.mt_cnt[mb];
     const int s = mb % p.S;
     uint8_t* slot = p.P.ring + s * p.slot_bytes;
     uint16_t* slot_x = reinterpret_cast<uint16_t*>(slot + p.slot_x);
     uint16_t* slot_h = reinterpret_cast<uint16_t*>(slot + p.slot_h);
     const int lo = p.P.mb_start[mb];
-    const bool g1 = q < nmt * p.nN1;
     const int qq = g1 ? q : q - nmt * p.nN1;
     const int nn = g1 ? p.nN1 : p.nN2;
     const int i = qq / nn, nt = qq % nn;

@@ -70,35 +70,47 @@ __device__ __forceinline__ uint64_t e4m3_pack8(const float (&v)[8], int n) {
 }
 
 // One wave quantises one row of D bf16 values (D a multiple of 32) into MX: codes[0..D)
-// and scales[0..D/32).  Lane l handles 8-element chunks c = l, l + 64, ...; the 4
-// lanes of a quad hold one 32-element block, whose largest magnitude they share over
-// DPP.  With kCoherent the outputs are written at device scope (handoff data).
+// and scales[0..D/32).  Lane l handles 8-element chunks c = l, l + 64, ..., loading 8 of
+// them before quantising any; the 4 lanes of a quad hold one 32-element block, whose
+// largest magnitude they share over DPP (a quad is wholly inside or outside the row,
+// since D / 8 is a multiple of 4).  With kCoherent the outputs are written at device
+// scope (handoff data).
 template <bool kCoherent>
 __device__ __forceinline__ void wave_quant_row(uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                const uint16_t* __restrict__ src, int D) {
+  constexpr int kB = 8;
   const int lane = threadIdx.x & 63;
-  const int nch = D >> 3;  // a multiple of 4: quads are whole or absent
+  const int nch = D >> 3;
   const v4u* s = reinterpret_cast<const v4u*>(src);
-  for (int c = lane; c < nch; c += 64) {
-    const v4u u = s[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    float v[8];
-    float amax = 0.f;
+  for (int c0 = lane; c0 < nch; c0 += 64 * kB) {
+    v4u raw[kB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
-      v[2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
-      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
-    }
-    amax = quad_max(amax);
-    const int n = mx_shared_exp(amax);
-    const uint64_t packed = e4m3_pack8(v, n);
-    if (kCoherent) st_dev_u64(codes + int64_t(c) * 8, packed);
-    else *reinterpret_cast<uint64_t*>(codes + int64_t(c) * 8) = packed;
-    if ((lane & 3) == 0) {
-      if (kCoherent) st_dev_u8(scales + (c >> 2), uint8_t(n + 127));
-      else scales[c >> 2] = uint8_t(n + 127);
+    for (int u = 0; u < kB; ++u)
+      if (c0 + 64 * u < nch) raw[u] = s[c0 + 64 * u];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < nch) {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        float v[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
+          v[2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
+          amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+        }
+        amax = quad_max(amax);
+        const int n = mx_shared_exp(amax);
+        const uint64_t packed = e4m3_pack8(v, n);
+        if (kCoherent) st_dev_u64(codes + int64_t(c) * 8, packed);
+        else *reinterpret_cast<uint64_t*>(codes + int64_t(c) * 8) = packed;
+        if ((lane & 3) == 0) {
+          if (kCoherent) st_dev_u8(scales + (c >> 2), uint8_t(n + 127));
+          else scales[c >> 2] = uint8_t(n + 127);
+        }
+      }
     }
   }
 }

@@ -11,6 +11,12 @@ namespace mok {
 // ------------------------------------------------------------------------------------
 // wave-level data movement
 // ------------------------------------------------------------------------------------
+// Rows are moved by one wave each, 16 bytes per lane, with kRowBatch loads per lane in
+// flight before the first store (a row of D = 7168 bf16 is 14 chunks per lane): the
+// data movers run on a few CUs, so their bandwidth is set by the bytes each wave keeps
+// in flight.
+constexpr int kRowBatch = 8;
+
 template <bool kCoherent>
 __device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
                                               const uint16_t* __restrict__ src, int D) {
@@ -18,19 +24,19 @@ __device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
   const int nch = D >> 3;
   const v4u* s = reinterpret_cast<const v4u*>(src);
   v4u* d = reinterpret_cast<v4u*>(dst);
-  int c = lane;
-  for (; c + 192 < nch; c += 256) {
-    const v4u v0 = s[c], v1 = s[c + 64], v2 = s[c + 128], v3 = s[c + 192];
-    if (kCoherent) {
-      st_dev_b128(d + c, v0); st_dev_b128(d + c + 64, v1);
-      st_dev_b128(d + c + 128, v2); st_dev_b128(d + c + 192, v3);
-    } else {
-      d[c] = v0; d[c + 64] = v1; d[c + 128] = v2; d[c + 192] = v3;
+  for (int c0 = lane; c0 < nch; c0 += 64 * kRowBatch) {
+    v4u v[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u)
+      if (c0 + 64 * u < nch) v[u] = s[c0 + 64 * u];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < nch) {
+        if (kCoherent) st_dev_b128(d + c, v[u]);
+        else d[c] = v[u];
+      }
     }
-  }
-  for (; c < nch; c += 64) {
-    if (kCoherent) st_dev_b128(d + c, s[c]);
-    else d[c] = s[c];
   }
 }
 
@@ -61,8 +67,10 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
 // column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
 // Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
-// [rows, 2I]: gate in [0, I), up in [I, 2I).  With kCoherent, H is written at device scope (handoff data of
-// the fused kernel).
+// [rows, 2I]: gate in [0, I), up in [I, 2I).  With kCoherent both are written at device
+// scope: in the fused kernel a ring slot is rewritten by workgroups on other XCDs within
+// one launch, and a plain store would leave a dirty line in one XCD's L2 that could be
+// written back after a newer one from another XCD.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
                                            uint16_t* H, int64_t ldh, uint16_t* AB) {
@@ -87,7 +95,11 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
             if (kCoherent) st_dev_u16(H + off, h);
             else H[off] = h;
           }
-          if (AB) AB[row * 2 * I + (gate_lane ? col : I + col)] = f32_to_bf16(x);
+          if (AB) {
+            uint16_t* ab = AB + row * 2 * I + (gate_lane ? col : I + col);
+            if (kCoherent) st_dev_u16(ab, f32_to_bf16(x));
+            else *ab = f32_to_bf16(x);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // one block at a time: few live registers

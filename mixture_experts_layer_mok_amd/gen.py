@@ -64,8 +64,10 @@ CONFIGS = {
                    comm_cus=32),
     3: LayerConfig("c3-share-fwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8, M=2048,
                    S=4, comm_cus=32),
+    # the skewed load puts ~86k rows on this GPU: the data movers need twice the CUs
+    # (minibatch x comm-CU sweep of the MXFP8 forward)
     4: LayerConfig("c4-share-zipf-fwd-mxfp8", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
-                   M=2048, S=4, comm_cus=32, precision=PREC_MXFP8, zipf_s=1.2),
+                   M=2048, S=4, comm_cus=64, precision=PREC_MXFP8, zipf_s=1.2),
     5: LayerConfig("c5-share-fwd-bwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
                    M=2048, S=4, comm_cus=32),
 }

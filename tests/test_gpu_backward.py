@@ -94,3 +94,20 @@ def test_backward_config5_full_and_deterministic():
     _, g2, _ = run_fwd_bwd(cfg, dev)
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("cfg", SMALL[1:3], ids=lambda c: c.name)
+def test_backward_after_fused_and_unfused_forward_agree(cfg):
+    """The backward takes a, b from the forward where it still holds them (ring slots
+    after a fused forward, every row after an unfused one) and replays GEMM1 elsewhere;
+    replayed and held values come from the same tile arithmetic, so the gradients are
+    bitwise equal, and equal again with a one-slot ring (everything but the last
+    minibatch replayed)."""
+    d = gen.make_inputs(cfg, seed=77, with_dy=True)
+    dev = DevInputs(d)
+    _, g_f, _ = run_fwd_bwd(cfg, dev)
+    _, g_u, _ = run_fwd_bwd(cfg, dev, flags=L.MOK_FLAG_SAVE_FOR_BWD | L.MOK_FLAG_UNFUSED)
+    _, g_1, _ = run_fwd_bwd(cfg, dev, S=1)
+    for name in g_f:
+        assert torch.equal(g_f[name], g_u[name]), name
+        assert torch.equal(g_f[name], g_1[name]), name
