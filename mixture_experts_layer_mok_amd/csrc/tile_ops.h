@@ -240,74 +240,104 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 // padded panel end pe are written, zeros past the valid rows), and the partial sum of
 // u h over this tile's columns for each row into dgpart[row][nt] (lanes first, then
 // the four column waves in order: a fixed summation order).
+//
+// The panel stores go through LDS: per 32 x 32 block a wave writes its values as
+// [column][row] (pitch 80 bytes: 16-byte aligned rows, few bank conflicts) into a
+// private 7.5 KB area of the free operand stages, then every lane stores 32
+// consecutive bytes of one panel row (16 rows of one column), instead of 8 bytes per
+// column scattered over 32 panel rows.
 __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int pc0, int pe,
                                        int n0, int I, int64_t TKP, const uint16_t* bab,
                                        const float* gates, const int32_t* perm, uint16_t* bdab,
                                        uint16_t* ht, uint16_t* dat, uint16_t* dbt, float* dgpart,
                                        int nt, int nNdh) {
+  constexpr int kPitch = 80, kPanelBytes = 32 * kPitch;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
+  const int w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
   float* red = reinterpret_cast<float*>(g_lds_a);  // [4][256] row partials per column wave
+  const uint32_t tbuf = lds_addr(g_lds_b) + uint32_t(w) * 3 * kPanelBytes;
+  uint16_t* const panels[3] = {ht, dat, dbt};
   const int64_t twoI = 2 * int64_t(I);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float s[4][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int rr[4];
-      float gq[4], s[4];
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        rr[t] = acc_row(tid, i, 4 * q + t);  // four consecutive rows
-        gq[t] = rr[t] < rows ? gates[perm[row0 + rr[t]]] : 0.f;
-        s[t] = 0.f;
-      }
+      for (int t = 0; t < 4; ++t) s[q][t] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (col < I) {
-          uint32_t hv[2] = {0u, 0u}, dav[2] = {0u, 0u}, dbv[2] = {0u, 0u};
+    for (int j = 0; j < 2; ++j) {
+      const int cb = n0 + wn * 64 + j * 32;  // I % 64 == 0: the block is all in or all out
+      if (cb >= I) continue;
+      const int col = cb + (lane & 31);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (rr[t] < rows) {
-              const float u = acc.c[i][j][4 * q + t];
-              const uint16_t* abr = bab + int64_t(row0 + rr[t]) * twoI;
-              const float a = bf16_to_f32(abr[col]);
-              const float b = bf16_to_f32(abr[I + col]);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-              const float sl = a * sg;
-              const float h = sl * b;
-              s[t] += u * h;
-              const float dh = gq[t] * u;
-              const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
-              const float db = dh * sl;
-              uint16_t* dr = bdab + int64_t(row0 + rr[t]) * twoI;
-              const uint16_t dab = f32_to_bf16(da), dbb = f32_to_bf16(db);
-              dr[col] = dab;
-              dr[I + col] = dbb;
-              hv[t >> 1] |= uint32_t(f32_to_bf16(h)) << (16 * (t & 1));
-              dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
-              dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
-            }
+      for (int q = 0; q < 4; ++q) {
+        uint32_t hv[2] = {0u, 0u}, dav[2] = {0u, 0u}, dbv[2] = {0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int rr = acc_row(tid, i, 4 * q + t);  // four consecutive rows
+          if (rr < rows) {
+            const float g = gates[perm[row0 + rr]];
+            const float u = acc.c[i][j][4 * q + t];
+            const uint16_t* abr = bab + int64_t(row0 + rr) * twoI;
+            const float a = bf16_to_f32(abr[col]);
+            const float b = bf16_to_f32(abr[I + col]);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+            const float sl = a * sg;
+            const float h = sl * b;
+            s[q][t] += u * h;
+            const float dh = g * u;
+            const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
+            const float db = dh * sl;
+            uint16_t* dr = bdab + int64_t(row0 + rr) * twoI;
+            const uint16_t dab = f32_to_bf16(da), dbb = f32_to_bf16(db);
+            dr[col] = dab;
+            dr[I + col] = dbb;
+            hv[t >> 1] |= uint32_t(f32_to_bf16(h)) << (16 * (t & 1));
+            dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
+            dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
           }
-          const int pc = pc0 + rr[0];  // multiple of 4: one 8-byte store per panel
-          if (pc < pe) {
-            const int64_t off = int64_t(col) * TKP + pc;
-            *reinterpret_cast<uint2*>(ht + off) = make_uint2(hv[0], hv[1]);
-            *reinterpret_cast<uint2*>(dat + off) = make_uint2(dav[0], dav[1]);
-            *reinterpret_cast<uint2*>(dbt + off) = make_uint2(dbv[0], dbv[1]);
+        }
+        // rows 8 q + 4 (lane / 32) .. +3 of column lane % 32 of this block
+        const uint32_t wa = tbuf + uint32_t(lane & 31) * kPitch + 16 * q + 8 * (lane >> 5);
+        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) v2u lds_v2u;
+        *reinterpret_cast<lds_v2u*>(uintptr_t(wa)) = v2u{hv[0], hv[1]};
+        *reinterpret_cast<lds_v2u*>(uintptr_t(wa + kPanelBytes)) = v2u{dav[0], dav[1]};
+        *reinterpret_cast<lds_v2u*>(uintptr_t(wa + 2 * kPanelBytes)) = v2u{dbv[0], dbv[1]};
+      }
+      // the wave's LDS writes are visible to its own later reads once they completed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      {
+        const int c = lane >> 1, hh = lane & 1;  // column, half (16 rows)
+        const int pcs = pc0 + wm * 128 + i * 32 + 16 * hh;
+        const uint32_t ra = tbuf + uint32_t(c) * kPitch + 32 * hh;
+        if (pcs < pe) {
+#pragma unroll
+          for (int pnl = 0; pnl < 3; ++pnl) {
+            const v4u lo = *reinterpret_cast<lds_cv4u*>(uintptr_t(ra + pnl * kPanelBytes));
+            const v4u hi = *reinterpret_cast<lds_cv4u*>(uintptr_t(ra + pnl * kPanelBytes + 16));
+            v4u* dst = reinterpret_cast<v4u*>(panels[pnl] + int64_t(cb + c) * TKP + pcs);
+            dst[0] = lo;
+            dst[1] = hi;
           }
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float v = s[t];
+        float v = s[q][t];
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
-        if ((lane & 31) == 0 && rr[t] < rows) red[wn * 256 + rr[t]] = v;
+        const int rr = acc_row(tid, i, 4 * q + t);
+        if ((lane & 31) == 0 && rr < rows) red[wn * 256 + rr] = v;
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   for (int r = tid; r < rows; r += kThreads)
