@@ -41,8 +41,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_fused_c5_traffic.txt")
-KERNEL_SOURCES = ("moe_fwd.hip", "tile_ops.h", "gemm_bf16.h", "tile_geom.h", "device.h",
-                  "layout.h")
+KERNEL_SOURCES = ("moe_fwd.hip", "tile_ops.h", "gemm_bf16.h", "gemm_mx.h", "mx.h", "tile_geom.h",
+                  "device.h", "layout.h", "launch.h")
 
 
 def parse():
