@@ -312,9 +312,9 @@ def main():
         out["bwd_ms"] = stats(r["bwd_ms"])
         out["bwd_tflops"] = round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2)
     # the committed counters were taken on the default command (config 5, fused, M=2048,
-    # S=4, 32 comm CUs, forward saving a and b for the backward)
+    # S=8, 32 comm CUs, forward saving a and b for the backward)
     traffic = read_traffic() if (not args.unfused and with_bwd and args.config == 5
-                                 and cfg.M == 2048 and cfg.S == 4 and cfg.comm_cus == 32) else None
+                                 and cfg.M == 2048 and cfg.S == 8 and cfg.comm_cus == 32) else None
     out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else
                        "forward (unfused launches)", "achieved": round(achieved, 2),
                        "peak": peak, "unit": "TFLOP/s",

@@ -132,6 +132,26 @@ __device__ __forceinline__ void tile_src_init(TileSrc& s, int layout, const uint
   }
 }
 
+// As tile_src_init, with the A rows gathered: tile row r (clamped to rows_valid - 1) is
+// row rowmap[r] / k of X [*, ldx] (rowmap = the schedule's perm from the tile's first
+// routed row: pair index t*k + j, token t).  Offsets are taken from X's base, so X must
+// hold fewer than 2^31 elements (checked on the host).
+__device__ __forceinline__ void tile_src_init_gather(TileSrc& s, int layout, const uint16_t* X,
+                                                     int64_t ldx, const int32_t* rowmap, int k,
+                                                     int rows_valid, const uint16_t* B0,
+                                                     const uint16_t* B1, int64_t ldb, int nb0,
+                                                     int nb1, int N) {
+  tile_src_init(s, layout, X, ldx, rows_valid, B0, B1, ldb, nb0, nb1, N);
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p) {
+    int r = geom::dma_row(p, w, l);
+    if (r > rows_valid - 1) r = rows_valid - 1;
+    const int64_t src = rowmap[r] / k;
+    s.oa[p] = uint32_t((src * ldx + geom::dma_chunk(w, l) * 8) * 2);
+  }
+}
+
 template <bool COH, int STAGE>
 __device__ __forceinline__ void tile_issue(const TileSrc& s, int k0) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform

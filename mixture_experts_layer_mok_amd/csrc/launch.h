@@ -29,8 +29,6 @@ struct Ptrs {
   uint8_t* wsu;
   uint8_t* wsd;
   // backward
-  uint16_t* bx;       // [T*k, D] dispatched X rows
-  uint16_t* bdy;      // [T*k, D] dispatched dY rows
   uint16_t* bab;      // [T*k, 2I] gate / up pre-activations
   uint16_t* bdab;     // [T*k, 2I] their gradients
   uint16_t* dxbuf;    // [T*k, D] per-pair dX contributions (pair-indexed)
@@ -69,8 +67,6 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.wsu = L.repack_wg ? b + L.off_wsu : nullptr;
   P.wsd = L.repack_wd ? b + L.off_wsd : nullptr;
   auto u16 = [&](size_t off) { return L.save ? reinterpret_cast<uint16_t*>(b + off) : nullptr; };
-  P.bx = u16(L.off_bx);
-  P.bdy = u16(L.off_bdy);
   P.bab = u16(L.off_bab);
   P.bdab = u16(L.off_bdab);
   P.dxbuf = u16(L.off_dxbuf);

@@ -65,8 +65,8 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t TKP;      // width of the transposed per-expert panels: T*k + 64*E_loc
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
-  size_t off_bx, off_bdy, off_bab, off_bdab, off_dxbuf, off_dgpart, off_wdt, off_wgut, off_xt,
-      off_gdyt, off_ht, off_dat, off_dbt, off_roff;
+  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_wdt, off_wgut, off_xt, off_gdyt, off_ht,
+      off_dat, off_dbt, off_roff;
   size_t total;
 };
 
@@ -162,16 +162,16 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   // expert, its rows as columns, padded with zeros to a multiple of 64.
   L->TKP = align_up(size_t(L->TK), 64) + 64 * nl;
   L->nNdh = (I + kBN2 - 1) / kBN2;
-  L->off_bx = L->off_bdy = L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = 0;
+  L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = 0;
   L->off_wdt = L->off_wgut = L->off_xt = L->off_gdyt = L->off_ht = L->off_dat = L->off_dbt = 0;
   L->off_roff = 0;
   if (L->save) {
     // panel and transposed-weight offsets of the backward GEMM tiles stay below 2^32 bytes
-    if ((D > I ? D : I) * L->TKP >= (int64_t(1) << 31) || 2 * I * D >= (int64_t(1) << 31))
+    // ... and the backward GEMMs read X and dY rows in place (offsets from their bases)
+    if ((D > I ? D : I) * L->TKP >= (int64_t(1) << 31) || 2 * I * D >= (int64_t(1) << 31) ||
+        T * D >= (int64_t(1) << 31))
       return MOK_E_SHAPE;
     const size_t TK = size_t(L->TK), TKP = size_t(L->TKP);
-    L->off_bx = o; o = align_up(o + TK * D * 2, A);
-    L->off_bdy = o; o = align_up(o + TK * D * 2, A);
     L->off_bab = o; o = align_up(o + TK * 2 * I * 2, A);
     L->off_bdab = o; o = align_up(o + TK * 2 * I * 2, A);
     L->off_dxbuf = o; o = align_up(o + TK * D * 2, A);

@@ -51,14 +51,6 @@ __global__ __launch_bounds__(64) void k_bwd_prep(BwdParams p) {
   }
 }
 
-// dst[r] = src[perm[r] / k] for routed rows r < R (one wave per row).
-__global__ __launch_bounds__(256) void k_bwd_gather(BwdParams p, const uint16_t* src, uint16_t* dst) {
-  const int R = int(p.P.hdr[kHdrR]);
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  for (int r = gw; r < R; r += nw)
-    wave_copy_row<false>(dst + int64_t(r) * p.D, src + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
-}
 
 // 64 x 64 transpose through LDS: dst[c][r] = src[r][c] for a [rows, cols] block of a
 // batch item.  Each thread moves 16 bytes on both sides.
@@ -201,8 +193,10 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
   const int nt = blockIdx.x % nN1;
   const int64_t wsz = int64_t(p.I) * p.D;
   TileAcc acc;
-  run_tile<false>(true, p.P.bx + int64_t(e.x) * p.D, e.y, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz,
-                  nt * kBN1, p.D, p.I, acc);
+  TileSrc src;
+  tile_src_init_gather(src, geom::kPaired, p.a.x, p.D, p.P.perm + e.x, p.k, e.y,
+                       p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.D, nt * kBN1, nt * kBN1, p.I);
+  tile_gemm<false>(src, p.D, acc);
   epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, nullptr, p.I, p.P.bab + int64_t(e.x) * 2 * p.I);
 }
 
@@ -215,8 +209,8 @@ __global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
   const int64_t wsz = int64_t(p.I) * p.D;
   const uint16_t* wdt = p.P.wdt + e.z * wsz;
   TileSrc src;
-  tile_src_init(src, geom::kSplit, p.P.bdy + int64_t(e.x) * p.D, p.D, e.y, wdt, wdt, p.D, n0,
-                n0 + 128, p.I);
+  tile_src_init_gather(src, geom::kSplit, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y, wdt, wdt, p.D,
+                       n0, n0 + 128, p.I);
   TileAcc acc;
   tile_gemm<false>(src, p.D, acc);
   const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
@@ -337,8 +331,6 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   const unsigned nN1 = unsigned((L.I + kBN1 - 1) / kBN1);
   const unsigned dmax = unsigned((std::max(L.D, L.I) + 63) / 64);
   hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_gather, dim3(rows_grid), dim3(256), 0, st, p, a.x, P.bx);
-  hipLaunchKernelGGL(k_bwd_gather, dim3(rows_grid), dim3(256), 0, st, p, a.dy, P.bdy);
   hipLaunchKernelGGL(k_bwd_transpose_weights, dim3(dmax, dmax, unsigned(3 * L.nl)), dim3(256), 0,
                      st, p);
   hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
