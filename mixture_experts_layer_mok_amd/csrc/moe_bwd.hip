@@ -18,8 +18,8 @@
 // This file holds the path as separate kernels.  The gate/up pre-activations a, b come
 // from the forward where it still holds them and are recomputed otherwise (replay of
 // GEMM1), following the reverse ring traversal: after a fused forward the ring slots
-// hold the last S minibatches (their a, b are copied out), and only minibatches whose
-// slot was recycled, mb < n_mb - S, are replayed.  An unfused forward that saves for
+// hold the last S minibatches (the dH epilogue reads their a, b there), and only
+// minibatches whose slot was recycled, mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for
 // the backward writes a, b of every row, and nothing is replayed.
 #include <algorithm>
 
@@ -34,7 +34,18 @@ struct BwdParams {
   int64_t TKP;
   int64_t slot_bytes, slot_ab;
   int ab_saved;  // 1: the forward wrote a, b of every row (unfused); 0: ring only (fused)
+  int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
 };
+
+// a, b of the rows of m-tile e in minibatch mb: in the ring slot while the minibatch is
+// still resident after a fused forward, else in the row buffer (replayed, or written by
+// an unfused forward).
+__device__ __forceinline__ const uint16_t* ab_rows(const BwdParams& p, const int4& e, int mb) {
+  if (!p.ab_saved && mb >= int(p.P.hdr[kHdrNmb]) - p.S)
+    return reinterpret_cast<const uint16_t*>(p.P.ring + (mb % p.S) * p.slot_bytes + p.slot_ab) +
+           int64_t(e.x - p.P.mb_start[mb]) * 2 * p.I;
+  return p.P.bab + int64_t(e.x) * 2 * p.I;
+}
 
 // ------------------------------------------------------------------------------------
 // preparation
@@ -157,80 +168,89 @@ __global__ __launch_bounds__(256) void k_bwd_panels(BwdParams p) {
 // ------------------------------------------------------------------------------------
 // GEMM kernels (one m-tile of the schedule's table per workgroup row)
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ bool tile_of(const BwdParams& p, int f, int4& e) {
-  const int mb = f / p.mt_max, i = f % p.mt_max;
-  if (mb >= int(p.P.hdr[kHdrNmb]) || i >= p.P.mt_cnt[mb]) return false;
-  e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
-  return true;
+// m-tile g (0 .. m-tiles - 1, in row order over all minibatches): its table entry and
+// minibatch (binary search over the m-tile prefix, tile_base[mb] / per_mt).
+__device__ __forceinline__ void mtile_at(const BwdParams& p, int g, int4& e, int& mb) {
+  const int n_mb = int(p.P.hdr[kHdrNmb]);
+  int lo = 0, hi = n_mb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.P.tile_base[mid] / p.per_mt <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  mb = lo;
+  e = p.P.mt_tab[int64_t(lo) * p.mt_max + (g - p.P.tile_base[lo] / p.per_mt)];
 }
 
-// Replay of GEMM1: gate/up pre-activations of every routed row into bab [R, 2I].
-// a, b of the minibatches still resident in the ring after a fused forward: slot mb % S
-// holds rows mb_start[mb] .. mb_start[mb + 1] of mb >= n_mb - S.  One wave per row.
-__global__ __launch_bounds__(256) void k_bwd_ab_resident(BwdParams p) {
-  const int n_mb = int(p.P.hdr[kHdrNmb]);
-  const int mb0 = n_mb > p.S ? n_mb - p.S : 0;
-  const int lo = n_mb > 0 ? p.P.mb_start[mb0] : 0, hi = int(p.P.hdr[kHdrR]);
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  int mb = mb0;
-  for (int r = lo + gw; r < hi; r += nw) {
-    while (mb + 1 < n_mb && p.P.mb_start[mb + 1] <= r) ++mb;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.P.ring + (mb % p.S) * p.slot_bytes +
-                                                            p.slot_ab) +
-                          int64_t(r - p.P.mb_start[mb]) * 2 * p.I;
-    wave_copy_row<false>(p.P.bab + int64_t(r) * 2 * p.I, src, 2 * p.I);
-  }
-}
+// The row GEMMs of the backward run on a grid of one workgroup per CU that walks the
+// (m-tile, column tile) pairs, row tiles slowest: the grid's size does not depend on
+// the worst-case tile table, and no workgroup starts only to find its slot empty.  The
+// K loop ends with a barrier and every epilogue that touches LDS ends with one, so the
+// next tile's loads may start at once.
 
 // Replay of GEMM1 for the m-tiles of minibatches whose a, b are no longer held.
 __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
-  int4 e;
+  if (p.ab_saved) return;
   const int nN1 = (p.I + kBN1 - 1) / kBN1;
-  const int f = blockIdx.x / nN1;
-  if (!tile_of(p, f, e)) return;
-  if (p.ab_saved || f / p.mt_max >= int(p.P.hdr[kHdrNmb]) - p.S) return;
-  const int nt = blockIdx.x % nN1;
+  const int n_mb = int(p.P.hdr[kHdrNmb]);
+  // the m-tiles of minibatches [0, n_mb - S) come first in row order
+  const int mb_end = n_mb - p.S;
+  if (mb_end <= 0) return;
+  const int nq = (p.P.tile_base[mb_end] / p.per_mt) * nN1;
   const int64_t wsz = int64_t(p.I) * p.D;
-  TileAcc acc;
-  TileSrc src;
-  tile_src_init_gather(src, geom::kPaired, p.a.x, p.D, p.P.perm + e.x, p.k, e.y,
-                       p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.D, nt * kBN1, nt * kBN1, p.I);
-  tile_gemm<false>(src, p.D, acc);
-  epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, nullptr, p.I, p.P.bab + int64_t(e.x) * 2 * p.I);
+  for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+    int4 e;
+    int mb;
+    mtile_at(p, q / nN1, e, mb);
+    const int nt = q % nN1;
+    TileAcc acc;
+    TileSrc src;
+    tile_src_init_gather(src, geom::kPaired, p.a.x, p.D, p.P.perm + e.x, p.k, e.y,
+                         p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.D, nt * kBN1, nt * kBN1, p.I);
+    tile_gemm<false>(src, p.D, acc);
+    epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, nullptr, p.I, p.P.bab + int64_t(e.x) * 2 * p.I);
+  }
 }
 
 // dH GEMM: u = dY rows x W_down[e] (wdt rows), fused SwiGLU backward and dG partials.
 __global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
-  int4 e;
-  if (!tile_of(p, blockIdx.x / p.nNdh, e)) return;
-  const int nt = blockIdx.x % p.nNdh;
-  const int n0 = nt * kBN2;
+  const int nq = int(p.P.hdr[kHdrMtiles]) * p.nNdh;
   const int64_t wsz = int64_t(p.I) * p.D;
-  const uint16_t* wdt = p.P.wdt + e.z * wsz;
-  TileSrc src;
-  tile_src_init_gather(src, geom::kSplit, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y, wdt, wdt, p.D,
-                       n0, n0 + 128, p.I);
-  TileAcc acc;
-  tile_gemm<false>(src, p.D, acc);
-  const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
-  epi_dh(acc, e.y, e.x, pc0, p.P.roff[e.z + 1], n0, p.I, p.TKP, p.P.bab, p.a.gates, p.P.perm,
-         p.P.bdab, p.P.ht, p.P.dat, p.P.dbt, p.P.dgpart, nt, p.nNdh);
+  for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+    int4 e;
+    int mb;
+    mtile_at(p, q / p.nNdh, e, mb);
+    const int nt = q % p.nNdh;
+    const int n0 = nt * kBN2;
+    const uint16_t* wdt = p.P.wdt + e.z * wsz;
+    TileSrc src;
+    tile_src_init_gather(src, geom::kSplit, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y, wdt, wdt,
+                         p.D, n0, n0 + 128, p.I);
+    TileAcc acc;
+    tile_gemm<false>(src, p.D, acc);
+    const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
+    epi_dh(acc, e.y, e.x, pc0, p.P.roff[e.z + 1], n0, p.I, p.TKP, ab_rows(p, e, mb), p.a.gates,
+           p.P.perm, p.P.bdab, p.P.ht, p.P.dat, p.P.dbt, p.P.dgpart, nt, p.nNdh);
+  }
 }
 
 // dX GEMM: dx rows = [da | db] x [W_gate; W_up][e] (wgut rows), pushed to their pairs.
 __global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
-  int4 e;
-  if (!tile_of(p, blockIdx.x / p.nDt, e)) return;
-  const int n0 = (blockIdx.x % p.nDt) * kBN2;
+  const int nq = int(p.P.hdr[kHdrMtiles]) * p.nDt;
   const int64_t K = 2 * int64_t(p.I);
-  const uint16_t* wg = p.P.wgut + e.z * K * p.D;
-  TileSrc src;
-  tile_src_init(src, geom::kSplit, p.P.bdab + int64_t(e.x) * K, K, e.y, wg, wg, K, n0, n0 + 128,
-                p.D);
-  TileAcc acc;
-  tile_gemm<false>(src, int(K), acc);
-  epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+  for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+    int4 e;
+    int mb;
+    mtile_at(p, q / p.nDt, e, mb);
+    const int n0 = (q % p.nDt) * kBN2;
+    const uint16_t* wg = p.P.wgut + e.z * K * p.D;
+    TileSrc src;
+    tile_src_init(src, geom::kSplit, p.P.bdab + int64_t(e.x) * K, K, e.y, wg, wg, K, n0,
+                  n0 + 128, p.D);
+    TileAcc acc;
+    tile_gemm<false>(src, int(K), acc);
+    epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+  }
 }
 
 // dW GEMMs over the expert panels.  Per expert: dW_down tiles (D x I), then dW_gate and
@@ -326,20 +346,22 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.slot_bytes = int64_t(L.slot_bytes);
   p.slot_ab = int64_t(L.slot_ab);
   p.ab_saved = L.unfused ? 1 : 0;
-  const unsigned rows_grid = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
-  const unsigned ftiles = unsigned(L.n_mb_max * L.mt_max);
-  const unsigned nN1 = unsigned((L.I + kBN1 - 1) / kBN1);
+  p.per_mt = int(L.nN1 + L.nN2);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return MOK_E_DEVICE;
+  const dim3 tiles_grid = dim3(unsigned(cus));  // one 512-thread tile workgroup fits a CU
   const unsigned dmax = unsigned((std::max(L.D, L.I) + 63) / 64);
   hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, st, p);
   hipLaunchKernelGGL(k_bwd_transpose_weights, dim3(dmax, dmax, unsigned(3 * L.nl)), dim3(256), 0,
                      st, p);
   hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
                      p);
-  if (!L.unfused)
-    hipLaunchKernelGGL(k_bwd_ab_resident, dim3(rows_grid), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_gemm1, dim3(ftiles * nN1), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dh, dim3(ftiles * unsigned(p.nNdh)), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dx, dim3(ftiles * unsigned(p.nDt)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dh, tiles_grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dx, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dw, dim3(unsigned(L.nl * 3 * p.nDt * p.nIt)), dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dg, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536))),
                      dim3(256), 0, st, p);

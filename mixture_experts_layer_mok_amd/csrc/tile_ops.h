@@ -235,6 +235,8 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 // n0 + [0, 256) (split B layout: B tile row b is column n0 + b) of u = dY W_down.  Per
 // element, with a, b the saved gate/up pre-activations, g the row's gate weight,
 // s = sigmoid(a):  h = a s b;  dh = g u;  da = dh b s (1 + a (1 - s));  db = dh a s.
+// a, b of tile row r are ab_tile[r * 2I + col] and ab_tile[r * 2I + I + col] (the tile's
+// rows in the ring slot or in the row buffer).
 // Writes da, db row-major into bdab [R, 2I] and, transposed, h / da / db into the
 // per-expert panels (row r of the tile is panel column pc0 + r; columns up to the
 // padded panel end pe are written, zeros past the valid rows), and the partial sum of
@@ -247,7 +249,7 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 // consecutive bytes of one panel row (16 rows of one column), instead of 8 bytes per
 // column scattered over 32 panel rows.
 __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int pc0, int pe,
-                                       int n0, int I, int64_t TKP, const uint16_t* bab,
+                                       int n0, int I, int64_t TKP, const uint16_t* ab_tile,
                                        const float* gates, const int32_t* perm, uint16_t* bdab,
                                        uint16_t* ht, uint16_t* dat, uint16_t* dbt, float* dgpart,
                                        int nt, int nNdh) {
@@ -281,7 +283,7 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
           if (rr < rows) {
             const float g = gates[perm[row0 + rr]];
             const float u = acc.c[i][j][4 * q + t];
-            const uint16_t* abr = bab + int64_t(row0 + rr) * twoI;
+            const uint16_t* abr = ab_tile + int64_t(rr) * twoI;
             const float a = bf16_to_f32(abr[col]);
             const float b = bf16_to_f32(abr[I + col]);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
