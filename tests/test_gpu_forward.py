@@ -154,3 +154,31 @@ def test_forward_config3_sampled_and_deterministic(c3_inputs):
         assert torch.equal(y, y_o)
     y_u, _ = run_forward(cfg, dev, flags=L.MOK_FLAG_UNFUSED)
     assert torch.equal(y, y_u)
+
+
+@pytest.mark.parametrize("precision", [0, 1], ids=["bf16", "mxfp8"])
+def test_forward_reuses_workspace_with_new_inputs(precision):
+    """Successive forwards on one workspace with different inputs: each must equal a fresh
+    unfused run bit for bit, with as many ring slots as minibatches and with fewer (slots
+    rewritten within a launch): no data of an earlier call or minibatch may survive."""
+    from mixture_experts_layer_mok_amd.layer import MoKLayer
+    cfg = gen.small_config("reuse", T=1024, D=256, I=256, E=8, k=2, M=256, S=8, comm_cus=16)
+    for S in (8, 2):
+        layer = MoKLayer(L.desc_from_config(cfg, S=S, precision=precision))
+        for seed in (31, 32, 33):
+            d = gen.make_inputs(cfg, seed=seed)
+            dev = DevInputs(d)
+            scales = (None, None, None)
+            wg, wu, wd = dev.wg, dev.wu, dev.wd
+            if precision:
+                (wg, sg), (wu, su), (wd, sd) = (layer.quantize_weights(w) for w in (wg, wu, wd))
+                scales = (sg, su, sd)
+            layer.schedule(dev.ids)
+            y = layer.forward(dev.x, dev.ids, dev.gates, wg, wu, wd, scales=scales)
+            ref_layer = MoKLayer(L.desc_from_config(cfg, S=S, precision=precision,
+                                                    flags=L.MOK_FLAG_UNFUSED))
+            ref_layer.schedule(dev.ids)
+            yr = ref_layer.forward(dev.x, dev.ids, dev.gates, wg, wu, wd, scales=scales)
+            torch.cuda.synchronize()
+            assert layer.status() == 0
+            assert torch.equal(y, yr), (S, seed)
