@@ -69,6 +69,10 @@ typedef enum {
                                        the resident minibatches for mok_moe_bwd          */
 #define MOK_FLAG_UNFUSED 0x2u       /* run the same steps as separate kernels over
                                        full-size buffers (comparison / phase timing)     */
+#define MOK_FLAG_SHORT_WAITS 0x4u   /* bounded waits of the fused forward expire after 1 us
+                                       instead of 2 s: the run sets MOK_DEV_TIMEOUT and
+                                       exits early with y undefined (tests the timeout
+                                       path; never for production use)                   */
 
 /* sticky device status bits (mok_read_device_status) */
 #define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */

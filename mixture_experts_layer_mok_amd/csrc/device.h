@@ -55,6 +55,7 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(v4u a, v4u b, f32x16_t c) {
 // and every loop of the persistent kernels exits once the abort word is set.
 // ------------------------------------------------------------------------------------
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s of the 100 MHz constant clock
+constexpr uint64_t kShortWaitTicks = 100ull;   // 1 us: MOK_FLAG_SHORT_WAITS
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -92,7 +93,8 @@ __device__ __forceinline__ v4u ld_dev_b128(const void* p) {
 }
 
 // Whole workgroup: wait until *p >= target.  Returns false when aborted/timed out.
-__device__ __forceinline__ bool wg_wait_geq(const uint32_t* p, uint32_t target, uint32_t* hdr) {
+__device__ __forceinline__ bool wg_wait_geq(const uint32_t* p, uint32_t target, uint32_t* hdr,
+                                            uint64_t limit) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
     int ok = 1;
@@ -100,7 +102,7 @@ __device__ __forceinline__ bool wg_wait_geq(const uint32_t* p, uint32_t target, 
       const uint64_t t0 = wall_clock64();
       while (ld_relaxed(p) < target) {
         if (ld_relaxed(hdr + kHdrAbort)) { ok = 0; break; }
-        if (wall_clock64() - t0 > kWaitTicks) {
+        if (wall_clock64() - t0 > limit) {
           or_relaxed(hdr + kHdrStatus, MOK_DEV_TIMEOUT);
           __hip_atomic_store(hdr + kHdrAbort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;

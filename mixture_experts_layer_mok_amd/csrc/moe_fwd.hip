@@ -42,6 +42,7 @@ struct FwdParams {
   Ptrs P;
   FwdArgs a;
   int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
+  uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
   // MXFP8: scale row strides of X / H rows and of the weight scales the tiles read, and
   // those weight scales (the caller's, or repacked copies in the workspace)
@@ -260,7 +261,7 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
   for (int mb = 0; mb < n_mb; ++mb) {
     const int s = mb % p.S;
     if (mb >= p.S) {
-      if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr)) return;
+      if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr, p.wait_ticks)) return;
     }
     uint8_t* slot = p.P.ring + s * p.slot_bytes;
     const int lo = p.P.mb_start[mb], hi = p.P.mb_start[mb + 1];
@@ -277,7 +278,7 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
     if (mb >= p.S) combine_mb(mb - p.S);
   }
   for (int cm = max(0, n_mb - p.S); cm < n_mb; ++cm) {
-    if (!wg_wait_geq(done + cm, mb_tiles2(cm), hdr)) return;
+    if (!wg_wait_geq(done + cm, mb_tiles2(cm), hdr, p.wait_ticks)) return;
     combine_mb(cm);
   }
 }
@@ -324,9 +325,9 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     const int i = qq / nn, nt = qq % nn;
     uint32_t* hd = hdone + int64_t(mb) * p.mt_max + i;
     if (g1) {
-      if (!wg_wait_geq(ready + mb, uint32_t(C), hdr)) break;
+      if (!wg_wait_geq(ready + mb, uint32_t(C), hdr, p.wait_ticks)) break;
     } else {
-      if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr)) break;
+      if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr, p.wait_ticks)) break;
     }
     const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
     const int r0 = e.x - lo;
@@ -401,6 +402,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.T = int(L.T); p.D = int(L.D); p.I = int(L.I); p.k = int(L.k); p.M = int(L.M);
   p.S = int(L.S); p.mt_max = int(L.mt_max); p.nN1 = int(L.nN1); p.nN2 = int(L.nN2);
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
+  p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
   p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
   p.slot_ab = int64_t(L.slot_ab);

@@ -64,8 +64,10 @@ def test_workspace_size_null_and_growth():
     c1, b1 = _ws_code(_desc(S=4))
     c2, b2 = _ws_code(_desc(flags=L.MOK_FLAG_UNFUSED))
     c3, b3 = _ws_code(_desc(flags=L.MOK_FLAG_SAVE_FOR_BWD))
-    assert c0 == c1 == c2 == c3 == L.MOK_OK
+    c4, b4 = _ws_code(_desc(flags=L.MOK_FLAG_SHORT_WAITS))
+    assert c0 == c1 == c2 == c3 == c4 == L.MOK_OK
     assert b0 < b1 and b0 < b2 and b0 < b3 and b0 % 256 == 0
+    assert b4 == b0  # the wait limit needs no memory
     # the result buffer alone is T*k*D bf16
     assert b0 > 128 * 2 * 128 * 2
 

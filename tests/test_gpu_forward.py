@@ -11,6 +11,7 @@ import torch
 import oracle as O
 from mixture_experts_layer_mok_amd import _lib as L
 from mixture_experts_layer_mok_amd import gen
+from mixture_experts_layer_mok_amd.layer import MoKLayer
 from tests.gpu_util import DevInputs, rel_fro, run_forward, say, y_values
 
 pytestmark = pytest.mark.gpu
@@ -161,7 +162,6 @@ def test_forward_reuses_workspace_with_new_inputs(precision):
     """Successive forwards on one workspace with different inputs: each must equal a fresh
     unfused run bit for bit, with as many ring slots as minibatches and with fewer (slots
     rewritten within a launch): no data of an earlier call or minibatch may survive."""
-    from mixture_experts_layer_mok_amd.layer import MoKLayer
     cfg = gen.small_config("reuse", T=1024, D=256, I=256, E=8, k=2, M=256, S=8, comm_cus=16)
     for S in (8, 2):
         layer = MoKLayer(L.desc_from_config(cfg, S=S, precision=precision))
@@ -182,3 +182,35 @@ def test_forward_reuses_workspace_with_new_inputs(precision):
             torch.cuda.synchronize()
             assert layer.status() == 0
             assert torch.equal(y, yr), (S, seed)
+
+
+@pytest.mark.parametrize("precision", [L.MOK_PREC_BF16, L.MOK_PREC_MXFP8], ids=["bf16", "mxfp8"])
+def test_forward_wait_timeout_exits_and_recovers(precision):
+    """With MOK_FLAG_SHORT_WAITS every bounded wait of the fused forward expires after
+    1 us, so a run with more minibatches than ring slots must time out: the kernel
+    still exits (the synchronize returns), the status word carries MOK_DEV_TIMEOUT, and
+    the next schedule and forward on the same workspace are correct again."""
+    cfg = gen.small_config("timeout", T=512, D=256, I=256, E=4, k=2, M=64, S=1, comm_cus=8)
+    d = gen.make_inputs(cfg, seed=12)
+    dev = DevInputs(d)
+    mx = precision == L.MOK_PREC_MXFP8
+    desc = L.desc_from_config(cfg, flags=L.MOK_FLAG_SHORT_WAITS, precision=precision)
+    layer = MoKLayer(desc)
+    ws = (layer.quantize_weights(dev.wg), layer.quantize_weights(dev.wu),
+          layer.quantize_weights(dev.wd)) if mx else None
+    w = (ws[0][0], ws[1][0], ws[2][0]) if mx else (dev.wg, dev.wu, dev.wd)
+    sc = (ws[0][1], ws[1][1], ws[2][1]) if mx else (None, None, None)
+    say(f"[timeout] {'mxfp8' if mx else 'bf16'} short waits")
+    layer.schedule(dev.ids)
+    layer.forward(dev.x, dev.ids, dev.gates, *w, scales=sc)
+    torch.cuda.synchronize()
+    assert layer.status() & L.MOK_DEV_TIMEOUT
+    say("[timeout] recovery run")
+    layer.desc = L.desc_from_config(cfg, precision=precision)
+    layer.schedule(dev.ids)
+    y = layer.forward(dev.x, dev.ids, dev.gates, *w, scales=sc)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    ref = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0, E=cfg.E,
+                    M=cfg.M, mxfp8=mx)
+    assert rel_fro(y_values(y), ref) < (5e-2 if mx else TOL_BF16)
