@@ -85,6 +85,40 @@ __device__ __forceinline__ void st_dev_b128(void* p, v4u v) {
   __hip_atomic_store(q + 1, uint64_t(v.z) | (uint64_t(v.w) << 32), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// Row access through a buffer resource: the hardware checks every access against the
+// row's length, so loads past the end read zero and stores past it are dropped, which
+// lets a row loop run without per-chunk branches.  The base is made wave-uniform.
+// kCpolDev (sc1) makes an access device scope, as the handoff protocol above requires.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kCpolPlain = 0;
+constexpr int kCpolDev = 16;
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t x = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
+  void* b = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, 0, int(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
+}
+template <int CPOL>
+__device__ __forceinline__ v4u buf_ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL);
+}
+template <int CPOL>
+__device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CPOL);
+}
+template <int CPOL>
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint64_t v) {
+  typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(v2u_t{uint32_t(v), uint32_t(v >> 32)}, r, off, 0, CPOL);
+}
+template <int CPOL>
+__device__ __forceinline__ void buf_st1(rsrc_t r, uint32_t off, uint8_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, CPOL);
+}
+
 __device__ __forceinline__ v4u ld_dev_b128(const void* p) {
   const uint64_t* q = static_cast<const uint64_t*>(p);
   const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -34,8 +34,7 @@ enum HdrWord : int {
   kHdrFwdTicket = 4,   // fused forward: next tile ticket
   kHdrAbort = 5,       // set when a bounded wait expires; every loop exits
   kHdrFwdTiles = 6,    // fused forward: total tiles
-  kHdrBwdTicket = 7,   // fused backward: next tile ticket
-  kHdrBwdTiles = 8,
+  kHdrDrainTicket = 7, // fused forward: next drain work chunk
   kHdrWords = 64
 };
 

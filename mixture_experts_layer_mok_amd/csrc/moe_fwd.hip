@@ -80,71 +80,88 @@ __device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uin
 // ------------------------------------------------------------------------------------
 // combine
 // ------------------------------------------------------------------------------------
-// y[t] = sum_j gate * o[t*k+j] over slots with a local row, ascending j.  Each lane
-// owns 16-byte chunks of the row; two chunks and up to four slots are loaded before any
-// is accumulated (the sum itself runs in ascending j per element).
+// y[t] = sum_j gate_j * o[t*k+j] over the slots j with a local row, in ascending j per
+// element (acc = 0, then acc += gate_j * o_j, each step rounded to fp32).  One wave per
+// token; lane l owns the 16-byte chunks l, l + 64, ... of the row.  A token with a single
+// local slot (the usual case of an even expert share) is scaled in passes of kRowBatch
+// chunks per lane; otherwise the wave loads kCombChunks chunks of two slots at a time.
+// Either way 16 loads per lane are in flight.
+constexpr int kCombChunks = 8;
+
+__device__ __forceinline__ void acc_gated(float (&acc)[8], v4u v, float g) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] = __fadd_rn(acc[2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
+    acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
+  }
+}
+__device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
+  return v4u{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+}
+
 template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
-  constexpr int kJ = 4;
-  const int lane = threadIdx.x & 63;
+  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  const uint32_t lane = threadIdx.x & 63;
   const int D = p.D, k = p.k;
-  const int nch = D >> 3;
+  const uint32_t bytes = uint32_t(D) * 2;
   const int64_t q0 = int64_t(t) * k;
-  const int32_t my_pos = lane < k ? p.P.pos[q0 + lane] : -1;
-  const float my_g = lane < k ? p.a.gates[q0 + lane] : 0.f;
+  const int32_t my_pos = int(lane) < k ? p.P.pos[q0 + lane] : -1;
+  const float my_g = int(lane) < k ? p.a.gates[q0 + lane] : 0.f;
   const uint64_t has = __ballot(my_pos >= 0);
-  v4u* yrow = reinterpret_cast<v4u*>(p.a.y + int64_t(t) * D);
-  for (int c0 = lane; c0 < nch; c0 += 128) {
-    const bool two = c0 + 64 < nch;
-    float acc[2][8];
+  const rsrc_t ry = row_rsrc(p.a.y + int64_t(t) * D, bytes);
+  if (__popcll(has) == 1) {
+    const int j = __ffsll((unsigned long long)has) - 1;
+    const float g = __shfl(my_g, j);
+    const rsrc_t ro = row_rsrc(p.P.obuf + (q0 + j) * D, bytes);
+    for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kRowBatch) {
+      v4u v[kRowBatch];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int u = 0; u < kRowBatch; ++u) v[u] = buf_ld16<kPol>(ro, b0 + (lane + 64 * u) * 16);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+      for (int u = 0; u < kRowBatch; ++u) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        acc_gated(acc, v[u], g);
+        buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * u) * 16, pack_acc(acc));
+      }
+    }
+    return;
+  }
+  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kCombChunks) {
+    float acc[kCombChunks][8];
+#pragma unroll
+    for (int c = 0; c < kCombChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
     uint64_t m = has;
     while (m) {
-      int js[kJ];
-      v4u v[kJ][2];
-      int n = 0;
+      const int j0 = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int j1 = m ? __ffsll((unsigned long long)m) - 1 : -1;
+      if (m) m &= m - 1;
+      const rsrc_t r0 = row_rsrc(p.P.obuf + (q0 + j0) * D, bytes);
+      // a missing second slot gets a zero-length range: its loads read nothing
+      const rsrc_t r1 = row_rsrc(p.P.obuf + (q0 + (j1 >= 0 ? j1 : j0)) * D, j1 >= 0 ? bytes : 0u);
+      v4u v0[kCombChunks], v1[kCombChunks];
 #pragma unroll
-      for (int u = 0; u < kJ; ++u) {
-        js[u] = -1;
-        if (m) {
-          js[u] = __ffsll((unsigned long long)m) - 1;
-          m &= m - 1;
-          n = u + 1;
-          const v4u* src = reinterpret_cast<const v4u*>(p.P.obuf + (q0 + js[u]) * D) + c0;
-          v[u][0] = kCoherent ? ld_dev_b128(src) : *src;
-          if (two) v[u][1] = kCoherent ? ld_dev_b128(src + 64) : src[64];
-        }
+      for (int c = 0; c < kCombChunks; ++c) {
+        v0[c] = buf_ld16<kPol>(r0, b0 + (lane + 64 * c) * 16);
+        v1[c] = buf_ld16<kPol>(r1, b0 + (lane + 64 * c) * 16);
       }
+      const float g0 = __shfl(my_g, j0);
 #pragma unroll
-      for (int u = 0; u < kJ; ++u) {
-        if (u >= n) break;
-        const float g = __shfl(my_g, js[u]);
+      for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v0[c], g0);
+      if (j1 >= 0) {
+        const float g1 = __shfl(my_g, j1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t w[4] = {v[u][h].x, v[u][h].y, v[u][h].z, v[u][h].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[h][2 * e] =
-                __fadd_rn(acc[h][2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
-            acc[h][2 * e + 1] =
-                __fadd_rn(acc[h][2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
-          }
-        }
+        for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v1[c], g1);
       }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h == 1 && !two) break;
-      v4u out;
-      out.x = pack_bf16x2(acc[h][0], acc[h][1]);
-      out.y = pack_bf16x2(acc[h][2], acc[h][3]);
-      out.z = pack_bf16x2(acc[h][4], acc[h][5]);
-      out.w = pack_bf16x2(acc[h][6], acc[h][7]);
-      yrow[c0 + 64 * h] = out;
-    }
+    for (int c = 0; c < kCombChunks; ++c)
+      buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
   }
 }
 
@@ -235,51 +252,182 @@ __global__ __launch_bounds__(256) void k_fwd_prep(FwdParams p) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p.P.sync[i] = 0;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     p.P.hdr[kHdrFwdTicket] = 0;
+    p.P.hdr[kHdrDrainTicket] = 0;
     p.P.hdr[kHdrAbort] = 0;
   }
 }
 
+// Rows of minibatch mb into its ring slot (slot mb mod S), row r by wave (r - lo) mod nw
+// == gw; MXFP8 rows are quantised on the way.  When a row fits in one pass (D <= 8192),
+// the loads of the wave's next row are issued before the current row is stored: vector
+// memory operations retire in issue order, so waiting for a load issued after a store
+// would also wait for that store to reach memory.  Two row buffers alternate, so no
+// register copy forces an early wait.
+template <bool MX>
+__device__ __forceinline__ void gather_mb(const FwdParams& p, int mb, int gw, int nw) {
+  gw = __builtin_amdgcn_readfirstlane(gw);
+  uint8_t* slot = p.P.ring + (mb % p.S) * p.slot_bytes;
+  const int lo = p.P.mb_start[mb], hi = p.P.mb_start[mb + 1];
+  const uint32_t bytes = uint32_t(p.D) * 2;
+  auto src_row = [&](int r) { return p.a.x + int64_t(p.P.perm[r] / p.k) * p.D; };
+  if (bytes > 64u * 16u * kRowBatch) {
+    for (int r = lo + gw; r < hi; r += nw) {
+      if (MX)
+        wave_quant_row<true>(slot + p.slot_x + int64_t(r - lo) * p.D,
+                             slot + p.slot_xs + int64_t(r - lo) * p.xs_ld, src_row(r), p.D);
+      else
+        wave_copy_row<true>(reinterpret_cast<uint16_t*>(slot + p.slot_x) + int64_t(r - lo) * p.D,
+                            src_row(r), p.D);
+    }
+    return;
+  }
+  static_assert(kRowBatch == kQuantBatch, "one pass holds the same chunks in both paths");
+  const int r0 = lo + gw;
+  if (r0 >= hi) return;
+  const int nrows = (hi - r0 + nw - 1) / nw;  // the wave's rows: r0 + i * nw, i < nrows
+  const uint32_t lane = threadIdx.x & 63;
+  // perm of the wave's rows, 64 at a time (lane j holds row i0 + j): one vector load
+  // per 64 rows, whose wait also covers the stores issued before it
+  int32_t pv = 0;
+  auto token_of = [&](int i) {
+    if ((i & 63) == 0) {
+      const int j = i + int(lane);
+      pv = j < nrows ? p.P.perm[r0 + j * nw] : 0;
+    }
+    return __builtin_amdgcn_readlane(pv, i & 63) / p.k;
+  };
+  // loads of the wave's row i into buf (an empty range when i >= nrows: nothing is read)
+  auto issue = [&](v4u (&buf)[kRowBatch], int i) {
+    const bool live = i < nrows;
+    const rsrc_t rs = row_rsrc(live ? p.a.x + int64_t(token_of(i)) * p.D : p.a.x,
+                               live ? bytes : 0u);
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) buf[u] = buf_ld16<kCpolPlain>(rs, (lane + 64 * u) * 16);
+  };
+  auto put = [&](const v4u (&buf)[kRowBatch], int i) {
+    const int64_t q = int64_t(r0 - lo) + int64_t(i) * nw;  // row within the slot
+    if (MX) {
+      const rsrc_t rc = row_rsrc(slot + p.slot_x + q * p.D, uint32_t(p.D));
+      const rsrc_t rsc = row_rsrc(slot + p.slot_xs + q * p.xs_ld, uint32_t(p.D) >> 5);
+      quant_store_pass<kCpolDev>(buf, rc, rsc, 0);
+    } else {
+      const rsrc_t rd = row_rsrc(slot + p.slot_x + q * bytes, bytes);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) buf_st16<kCpolDev>(rd, (lane + 64 * u) * 16, buf[u]);
+    }
+  };
+  // two row buffers in turn, so that two rows' loads are in flight
+  v4u a[kRowBatch], b[kRowBatch];
+  issue(a, 0);
+  for (int i = 0;;) {
+    issue(b, i + 1);
+    put(a, i);
+    if (++i >= nrows) break;
+    issue(a, i + 1);
+    put(b, i);
+    if (++i >= nrows) break;
+  }
+}
+
+// Comm workgroups: gather minibatches 1.. into the ring (minibatch 0 is gathered by every
+// workgroup before the roles split), reusing a slot once the GEMM2 tiles of the minibatch
+// it held are done, and combine the tokens of that older minibatch.  The last S
+// minibatches are combined in the drain.
 template <bool MX>
 __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint32_t* ready, uint32_t* done) {
   uint32_t* hdr = p.P.hdr;
   const int n_mb = int(hdr[kHdrNmb]);
   const int w = threadIdx.x >> 6;
   const int gw = c * (kThreads / 64) + w, nw = C * (kThreads / 64);
-  // tokens without a local slot: y = 0
-  for (int t = gw; t < p.T; t += nw)
-    if (token_last_row(p.P.pos, t, p.k) < 0) wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
-
-  auto combine_mb = [&](int cm) {
-    const int lo = p.P.mb_start[cm], hi = p.P.mb_start[cm + 1];
-    for (int r = lo + gw; r < hi; r += nw) {
-      const int t = p.P.perm[r] / p.k;
-      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
-    }
-  };
   auto mb_tiles2 = [&](int mb) { return uint32_t(p.P.mt_cnt[mb] * p.nN2); };
-
-  for (int mb = 0; mb < n_mb; ++mb) {
-    const int s = mb % p.S;
+  for (int mb = 1; mb < n_mb; ++mb) {
     if (mb >= p.S) {
       if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr, p.wait_ticks)) return;
     }
-    uint8_t* slot = p.P.ring + s * p.slot_bytes;
-    const int lo = p.P.mb_start[mb], hi = p.P.mb_start[mb + 1];
-    for (int r = lo + gw; r < hi; r += nw) {
-      const uint16_t* src = p.a.x + int64_t(p.P.perm[r] / p.k) * p.D;
-      if (MX)
-        wave_quant_row<true>(slot + p.slot_x + int64_t(r - lo) * p.D,
-                             slot + p.slot_xs + int64_t(r - lo) * p.xs_ld, src, p.D);
-      else
-        wave_copy_row<true>(reinterpret_cast<uint16_t*>(slot + p.slot_x) + int64_t(r - lo) * p.D,
-                            src, p.D);
-    }
+    gather_mb<MX>(p, mb, gw, nw);
     wg_signal_add(ready + mb, 1);
-    if (mb >= p.S) combine_mb(mb - p.S);
+    if (mb >= p.S) {
+      const int cm = mb - p.S;
+      const int lo = p.P.mb_start[cm], hi = p.P.mb_start[cm + 1];
+      for (int r = lo + gw; r < hi; r += nw) {
+        const int t = p.P.perm[r] / p.k;
+        if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
+      }
+    }
   }
-  for (int cm = max(0, n_mb - p.S); cm < n_mb; ++cm) {
-    if (!wg_wait_geq(done + cm, mb_tiles2(cm), hdr, p.wait_ticks)) return;
-    combine_mb(cm);
+}
+
+// Waits until the GEMM2 tiles of minibatches [from, to] are all done.  Wave 0 checks 64
+// counters per load; only the unfinished ones are waited for.
+__device__ __forceinline__ bool wait_done_range(const FwdParams& p, const uint32_t* done,
+                                                int from, int to) {
+  __shared__ uint64_t s_pending;
+  for (int c0 = from; c0 <= to; c0 += 64) {
+    if (threadIdx.x < 64) {
+      const int c = c0 + int(threadIdx.x);
+      const bool pend = c <= to && ld_relaxed(done + c) < uint32_t(p.P.mt_cnt[c] * p.nN2);
+      const uint64_t b = __ballot(pend);
+      if (threadIdx.x == 0) s_pending = b;
+    }
+    __syncthreads();
+    uint64_t m = s_pending;
+    __syncthreads();
+    while (m) {
+      const int c = c0 + __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      if (!wg_wait_geq(done + c, uint32_t(p.P.mt_cnt[c] * p.nN2), p.P.hdr, p.wait_ticks))
+        return false;
+    }
+  }
+  return true;
+}
+
+// Drain, run by every workgroup once its role is done, so that the compute CUs help with
+// the data movement left at the end.  Work comes in chunks from a ticket: first the
+// token chunks (y = 0 for tokens without a local row), then, minibatch by minibatch, the
+// row chunks of the last S minibatches.  A row chunk of minibatch cm combines the tokens
+// whose last row it holds; their other rows lie in minibatches before cm, whose GEMM2
+// tiles may finish after cm's, so it waits for the tiles of every minibatch up to cm.
+constexpr int kDrainTokens = 64;
+constexpr int kDrainRows = 8;  // one row per wave: the final combine spreads over every CU
+
+__device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) {
+  uint32_t* hdr = p.P.hdr;
+  const int n_mb = int(hdr[kHdrNmb]);
+  const int w = threadIdx.x >> 6;
+  constexpr int W = kThreads / 64;
+  const uint32_t nz = uint32_t((p.T + kDrainTokens - 1) / kDrainTokens);
+  auto chunks = [&](int mb) {
+    return uint32_t((p.P.mb_start[mb + 1] - p.P.mb_start[mb] + kDrainRows - 1) / kDrainRows);
+  };
+  __shared__ uint32_t s_tk;
+  int cm = max(0, n_mb - p.S);
+  uint32_t cbase = nz;  // first ticket of minibatch cm's row chunks (tickets only grow)
+  int waited = 0;       // minibatches [0, waited) are known to be done
+  while (true) {
+    if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrDrainTicket, 1u);
+    __syncthreads();
+    const uint32_t tk = s_tk;
+    __syncthreads();
+    if (aborted(hdr)) return;
+    if (tk < nz) {
+      const int t1 = min(p.T, int(tk + 1) * kDrainTokens);
+      for (int t = int(tk) * kDrainTokens + w; t < t1; t += W)
+        if (token_last_row(p.P.pos, t, p.k) < 0) wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
+      continue;
+    }
+    while (cm < n_mb && tk >= cbase + chunks(cm)) cbase += chunks(cm++);
+    if (cm >= n_mb) return;
+    if (waited <= cm) {
+      if (!wait_done_range(p, done, waited, cm)) return;
+      waited = cm + 1;
+    }
+    const int lo = p.P.mb_start[cm] + int(tk - cbase) * kDrainRows;
+    const int hi = min(p.P.mb_start[cm + 1], lo + kDrainRows);
+    for (int r = lo + w; r < hi; r += W) {
+      const int t = p.P.perm[r] / p.k;
+      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
+    }
   }
 }
 
@@ -325,7 +473,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     const int i = qq / nn, nt = qq % nn;
     uint32_t* hd = hdone + int64_t(mb) * p.mt_max + i;
     if (g1) {
-      if (!wg_wait_geq(ready + mb, uint32_t(C), hdr, p.wait_ticks)) break;
+      if (!wg_wait_geq(ready + mb, mb == 0 ? gridDim.x : uint32_t(C), hdr, p.wait_ticks)) break;
     } else {
       if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr, p.wait_ticks)) break;
     }
@@ -374,8 +522,15 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
   const int C = p.a.comm_cus;
+  // fill: every workgroup gathers part of minibatch 0
+  if (p.P.hdr[kHdrNmb] > 0) {
+    gather_mb<MX>(p, 0, blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6),
+                  gridDim.x * (kThreads / 64));
+    wg_signal_add(ready, 1);
+  }
   if (int(blockIdx.x) < C) comm_role<MX>(p, blockIdx.x, C, ready, done);
   else compute_role<MX>(p, C, ready, done, hdone);
+  drain(p, done);
 }
 
 // Weight scales with a row stride of K / 32 bytes, repacked to the tile's stride of one

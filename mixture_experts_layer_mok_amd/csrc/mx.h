@@ -1,9 +1,9 @@
 // MXFP8 encoding on the device: OCP MX blocks of 32 elements with an e8m0 shared scale
 // and e4m3 elements (bias 7, largest finite 448, no infinities).  The shared exponent
 // is the smallest n with amax * 2^-n <= 448 (clamped to [-127, 127], -127 for an
-// all-zero block); each element is v * 2^-n rounded to nearest even, saturating.
-// Implemented on float32 bit patterns; every step after reading the float32 value is
-// exact.
+// all-zero block); each element is v * 2^-n rounded to nearest even.  The exponent is
+// read from float32 bit patterns and the scaling by 2^-n is exact, so only the final
+// conversion rounds.
 #pragma once
 #include "device.h"
 
@@ -19,24 +19,12 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
   return max(-127, min(127, n));
 }
 
-// e4m3 code of x (already scaled), round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;        // |x| >= 448
-  if (a < 0x3C800000u) {                             // |x| < 2^-6: multiples of 2^-9
-    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | uint32_t(q);                       // q == 8 is the smallest normal
-  }
-  const uint32_t e = (a >> 23) - 127u + 7u;         // 1..15
-  const uint32_t m = a & 0x7FFFFFu;
-  uint32_t q = m >> 20;
-  const uint32_t rem = m & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-  uint32_t code = (e << 3) + q;                      // a mantissa carry bumps the exponent
-  if (code > 0x7Eu) code = 0x7Eu;
-  return sign | code;
+// e4m3 codes of two already-scaled values (byte 0: a, byte 1: b) from gfx950's
+// conversion instruction: OCP e4m3, round to nearest even, subnormals kept.  The shared
+// exponent bounds every scaled magnitude by 448, the largest finite code, so no value
+// reaches the instruction's overflow handling.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
 
 // Maximum over each group of 4 (quad) or 16 (DPP row) consecutive lanes, with DPP lane
@@ -60,58 +48,62 @@ __device__ __forceinline__ float row16_max(float v) {
 
 // Eight e4m3 codes of v[0..7] * 2^-n, packed little-endian.
 __device__ __forceinline__ uint64_t e4m3_pack8(const float (&v)[8], int n) {
-  uint32_t lo = 0, hi = 0;
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -n), ldexpf(v[1], -n), 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -n), ldexpf(v[3], -n), lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -n), ldexpf(v[5], -n), 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -n), ldexpf(v[7], -n), hi, true);
+  return uint64_t(uint32_t(lo)) | (uint64_t(uint32_t(hi)) << 32);
+}
+
+// MX quantisation of one pass of a row: lane l holds 8-element chunks c = b + l + 64u
+// (u < kQuantBatch) in raw; the 4 lanes of a quad hold one 32-element block, whose
+// largest magnitude they share over DPP.  Codes and scales go through row-length buffer
+// resources (codes: D bytes, scales: D / 32 bytes), so chunks past the row's end are
+// quantised from zeros and their stores dropped: every lane stays active for the DPP
+// steps.
+constexpr int kQuantBatch = 16;
+
+template <int kPol>
+__device__ __forceinline__ void quant_store_pass(const v4u (&raw)[kQuantBatch], rsrc_t rc,
+                                                 rsrc_t rsc, uint32_t b) {
+  const uint32_t lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lo |= e4m3_rne(ldexpf(v[j], -n)) << (8 * j);
-    hi |= e4m3_rne(ldexpf(v[4 + j], -n)) << (8 * j);
+  for (int u = 0; u < kQuantBatch; ++u) {
+    const uint32_t c = b + lane + 64 * u;
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
+      v[2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    amax = quad_max(amax);
+    const int n = mx_shared_exp(amax);
+    buf_st8<kPol>(rc, c * 8, e4m3_pack8(v, n));
+    if ((lane & 3) == 0) buf_st1<kPol>(rsc, c >> 2, uint8_t(n + 127));
   }
-  return uint64_t(lo) | (uint64_t(hi) << 32);
 }
 
 // One wave quantises one row of D bf16 values (D a multiple of 32) into MX: codes[0..D)
-// and scales[0..D/32).  Lane l handles 8-element chunks c = l, l + 64, ..., loading 8 of
-// them before quantising any; the 4 lanes of a quad hold one 32-element block, whose
-// largest magnitude they share over DPP (a quad is wholly inside or outside the row,
-// since D / 8 is a multiple of 4).  With kCoherent the outputs are written at device
-// scope (handoff data).
+// and scales[0..D/32), kQuantBatch chunks per lane loaded before any is quantised.  With
+// kCoherent the outputs are written at device scope (handoff data).
 template <bool kCoherent>
 __device__ __forceinline__ void wave_quant_row(uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                const uint16_t* __restrict__ src, int D) {
-  constexpr int kB = 8;
-  const int lane = threadIdx.x & 63;
-  const int nch = D >> 3;
-  const v4u* s = reinterpret_cast<const v4u*>(src);
-  for (int c0 = lane; c0 < nch; c0 += 64 * kB) {
-    v4u raw[kB];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t nch = uint32_t(D) >> 3;
+  const rsrc_t rs = row_rsrc(src, uint32_t(D) * 2);
+  const rsrc_t rc = row_rsrc(codes, uint32_t(D));
+  const rsrc_t rsc = row_rsrc(scales, uint32_t(D) >> 5);
+  for (uint32_t b = 0; b < nch; b += 64 * kQuantBatch) {
+    v4u raw[kQuantBatch];
 #pragma unroll
-    for (int u = 0; u < kB; ++u)
-      if (c0 + 64 * u < nch) raw[u] = s[c0 + 64 * u];
-#pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const int c = c0 + 64 * u;
-      if (c < nch) {
-        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-        float v[8];
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = bf16_to_f32(uint16_t(w[j] & 0xFFFF));
-          v[2 * j + 1] = bf16_to_f32(uint16_t(w[j] >> 16));
-          amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
-        }
-        amax = quad_max(amax);
-        const int n = mx_shared_exp(amax);
-        const uint64_t packed = e4m3_pack8(v, n);
-        if (kCoherent) st_dev_u64(codes + int64_t(c) * 8, packed);
-        else *reinterpret_cast<uint64_t*>(codes + int64_t(c) * 8) = packed;
-        if ((lane & 3) == 0) {
-          if (kCoherent) st_dev_u8(scales + (c >> 2), uint8_t(n + 127));
-          else scales[c >> 2] = uint8_t(n + 127);
-        }
-      }
-    }
+    for (int u = 0; u < kQuantBatch; ++u)
+      raw[u] = buf_ld16<kCpolPlain>(rs, (b + lane + 64 * u) * 16);
+    quant_store_pass<kCoherent ? kCpolDev : kCpolPlain>(raw, rc, rsc, b);
   }
 }
 

@@ -12,31 +12,25 @@ namespace mok {
 // wave-level data movement
 // ------------------------------------------------------------------------------------
 // Rows are moved by one wave each, 16 bytes per lane, with kRowBatch loads per lane in
-// flight before the first store (a row of D = 7168 bf16 is 14 chunks per lane): the
-// data movers run on a few CUs, so their bandwidth is set by the bytes each wave keeps
-// in flight.
-constexpr int kRowBatch = 8;
+// flight before the first store (a row of D = 7168 bf16 is 14 chunks per lane, so one
+// pass): the data movers run on a few CUs, so their bandwidth is set by the bytes each
+// wave keeps in flight.  Accesses go through row-length buffer resources, so the chunks
+// of a pass that lie past the row's end cost an issue slot but no memory traffic.
+constexpr int kRowBatch = 16;
 
 template <bool kCoherent>
 __device__ __forceinline__ void wave_copy_row(uint16_t* __restrict__ dst,
                                               const uint16_t* __restrict__ src, int D) {
-  const int lane = threadIdx.x & 63;
-  const int nch = D >> 3;
-  const v4u* s = reinterpret_cast<const v4u*>(src);
-  v4u* d = reinterpret_cast<v4u*>(dst);
-  for (int c0 = lane; c0 < nch; c0 += 64 * kRowBatch) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t bytes = uint32_t(D) * 2;
+  const rsrc_t rs = row_rsrc(src, bytes), rd = row_rsrc(dst, bytes);
+  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kRowBatch) {
     v4u v[kRowBatch];
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u)
-      if (c0 + 64 * u < nch) v[u] = s[c0 + 64 * u];
+    for (int u = 0; u < kRowBatch; ++u) v[u] = buf_ld16<kCpolPlain>(rs, b0 + (lane + 64 * u) * 16);
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) {
-      const int c = c0 + 64 * u;
-      if (c < nch) {
-        if (kCoherent) st_dev_b128(d + c, v[u]);
-        else d[c] = v[u];
-      }
-    }
+    for (int u = 0; u < kRowBatch; ++u)
+      buf_st16<kCoherent ? kCpolDev : kCpolPlain>(rd, b0 + (lane + 64 * u) * 16, v[u]);
   }
 }
 
@@ -54,9 +48,11 @@ __device__ __forceinline__ int token_last_row(const int32_t* pos, int t, int k) 
 }
 
 __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
-  const int lane = threadIdx.x & 63;
-  v4u* d = reinterpret_cast<v4u*>(dst);
-  for (int c = lane; c < (D >> 3); c += 64) d[c] = v4u{0u, 0u, 0u, 0u};
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t bytes = uint32_t(D) * 2;
+  const rsrc_t rd = row_rsrc(dst, bytes);
+  for (uint32_t b = lane * 16; b < bytes; b += 64 * 16)
+    buf_st16<kCpolPlain>(rd, b, v4u{0u, 0u, 0u, 0u});
 }
 
 // ------------------------------------------------------------------------------------
@@ -167,8 +163,8 @@ __device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int 
       const int n = mx_shared_exp(amax);
       const int row = acc_row(tid, i, v);
       if (row < rows && gate_lane) {
-        const uint8_t c0 = uint8_t(e4m3_rne(ldexpf(h0, -n)));
-        const uint8_t c1 = uint8_t(e4m3_rne(ldexpf(h1, -n)));
+        const uint32_t cc = e4m3x2(ldexpf(h0, -n), ldexpf(h1, -n));
+        const uint8_t c0 = uint8_t(cc), c1 = uint8_t(cc >> 8);
         uint8_t* hr = Hc + int64_t(row) * ldh + cb + (lane & 15);
         if (kCoherent) {
           st_dev_u8(hr, c0);
@@ -259,9 +255,14 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
   const int w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
   float* red = reinterpret_cast<float*>(g_lds_a);  // [4][256] row partials per column wave
+  float* gate_of = red + 4 * 256;                  // [256] gate weight of each tile row
   const uint32_t tbuf = lds_addr(g_lds_b) + uint32_t(w) * 3 * kPanelBytes;
   uint16_t* const panels[3] = {ht, dat, dbt};
   const int64_t twoI = 2 * int64_t(I);
+  if (tid < 256) gate_of[tid] = tid < rows ? gates[perm[row0 + tid]] : 0.f;
+  const rsrc_t ab_res = row_rsrc(ab_tile, uint32_t(rows) * uint32_t(twoI) * 2u);
+  const rsrc_t dab_res = row_rsrc(bdab + int64_t(row0) * twoI, uint32_t(rows) * uint32_t(twoI) * 2u);
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float s[4][4];
@@ -274,33 +275,48 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
       const int cb = n0 + wn * 64 + j * 32;  // I % 64 == 0: the block is all in or all out
       if (cb >= I) continue;
       const int col = cb + (lane & 31);
+      // a and b of the lane's 16 rows (acc_row(i, 4q + t) = acc_row(i, 0) + 8q + t), all
+      // loads issued before the first use; rows past the tile lie outside the resource
+      // and read zero
+      uint16_t av[16], bv[16];
+      const uint32_t voff = (uint32_t(acc_row(tid, i, 0)) * uint32_t(twoI) + col) * 2u;
+      {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t so = uint32_t(8 * (v >> 2) + (v & 3)) * uint32_t(twoI) * 2u;
+          av[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so, 0);
+          bv[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so + uint32_t(I) * 2u, 0);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t hv[2] = {0u, 0u}, dav[2] = {0u, 0u}, dbv[2] = {0u, 0u};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int rr = acc_row(tid, i, 4 * q + t);  // four consecutive rows
-          if (rr < rows) {
-            const float g = gates[perm[row0 + rr]];
-            const float u = acc.c[i][j][4 * q + t];
-            const uint16_t* abr = ab_tile + int64_t(rr) * twoI;
-            const float a = bf16_to_f32(abr[col]);
-            const float b = bf16_to_f32(abr[I + col]);
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-            const float sl = a * sg;
-            const float h = sl * b;
-            s[q][t] += u * h;
-            const float dh = g * u;
-            const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
-            const float db = dh * sl;
-            uint16_t* dr = bdab + int64_t(row0 + rr) * twoI;
-            const uint16_t dab = f32_to_bf16(da), dbb = f32_to_bf16(db);
-            dr[col] = dab;
-            dr[I + col] = dbb;
-            hv[t >> 1] |= uint32_t(f32_to_bf16(h)) << (16 * (t & 1));
-            dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
-            dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
+          const bool ok = rr < rows;
+          const float g = gate_of[rr];
+          const float u = acc.c[i][j][4 * q + t];
+          const float a = bf16_to_f32(av[4 * q + t]);
+          const float b = bf16_to_f32(bv[4 * q + t]);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+          const float sl = a * sg;
+          const float h = sl * b;
+          s[q][t] += ok ? u * h : 0.f;
+          const float dh = g * u;
+          const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
+          const float db = dh * sl;
+          const uint16_t dab = ok ? f32_to_bf16(da) : uint16_t(0);
+          const uint16_t dbb = ok ? f32_to_bf16(db) : uint16_t(0);
+          const uint16_t hb = ok ? f32_to_bf16(h) : uint16_t(0);
+          {  // rows past the tile lie outside the resource: the stores are dropped
+            const uint32_t so = uint32_t(8 * q + t) * uint32_t(twoI) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b16(dab, dab_res, voff, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(dbb, dab_res, voff, so + uint32_t(I) * 2u, 0);
           }
+          hv[t >> 1] |= uint32_t(hb) << (16 * (t & 1));
+          dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
+          dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
         }
         // rows 8 q + 4 (lane / 32) .. +3 of column lane % 32 of this block
         const uint32_t wa = tbuf + uint32_t(lane & 31) * kPitch + 16 * q + 8 * (lane >> 5);
