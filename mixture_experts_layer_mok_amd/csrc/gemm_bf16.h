@@ -282,6 +282,268 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------------------------------------------------
+// Tiles with K-major operands
+// ------------------------------------------------------------------------------------
+// The backward contracts over dimensions that are not contiguous in memory: over the
+// rows of the weights (dX, dH: the B columns are contiguous along a weight row) and over
+// the routed rows (dW: both operands).  Such an operand is staged K-major (tile_geom.h:
+// 64 K rows of 256 columns per stage, swizzled in 4-chunk groups) and its MFMA fragments
+// are read with ds_read_b64_tr_b16.  That instruction transposes 16-bit elements within
+// each group of 16 lanes: lane i of a group receives element i % 4 of the 8-byte chunks
+// addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (measured on MI355X).
+// So if lane s of a group addresses K row kb + s / 4 at column cb + 4 (s % 4), lane i
+// receives K rows kb .. kb + 3 of column cb + i: half of an MFMA operand; a second read
+// at K + 4 gives the other half.  Per read, the 16 lanes of a group touch 4 K rows
+// whose swizzle groups differ, so the 64 lanes hit every bank exactly twice.
+//
+// Operand kinds:
+//   kKC  K-contiguous rows (the tile above; rows may be gathered);
+//   kKW  K-major weight matrix [K rows][ld]: tile column n is column n of every row;
+//        K rows past ksplit come from a second matrix (dX stacks W_gate over W_up);
+//   kKR  K-major routed rows: K index q is routed row rbeg + q, whose data is row
+//        perm[r] / ktop of a token matrix (gathered) or row r of a row matrix; rows at
+//        or past rend read zero (bit 31 of the offset, against a 2 GB resource).
+enum KmKind { kKC = 0, kKW = 1, kKR = 2 };
+constexpr uint32_t kKmOutOfRange = 0x80000000u;
+constexpr int kKmRowBytes = 512;  // one staged K row: 256 bf16
+
+struct KmOp {
+  i32x4_t r0, r1;
+  uint32_t off[geom::kLoads];  // kKC / kKW: per-lane byte offsets; kKR: column bytes
+  uint32_t ld2;                // kKW: bytes per K row; kKR: bytes per source row
+  int ksplit;                  // kKW
+  const int32_t* perm;         // kKR: gathered source rows (null: row r itself)
+  int ktop, rbeg, rend;        // kKR
+  int32_t nxt[geom::kLoads];   // kKR with perm: source rows of the next step to issue
+};
+
+__device__ __forceinline__ i32x4_t make_rsrc_2g_km(const void* base) {
+  i32x4_t r = make_rsrc(base);
+  r.z = int(kKmOutOfRange);
+  return r;
+}
+
+// K-contiguous rows [rows_valid, lda] from A (kKC), as tile_src_init's A operand.
+__device__ __forceinline__ void km_init_kc(KmOp& o, const uint16_t* A, int64_t lda,
+                                           int rows_valid) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  o.r0 = make_rsrc(A);
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p)
+    o.off[p] = uint32_t(geom::a_offset(p, w, l, rows_valid, lda));
+}
+
+// As km_init_kc with the rows gathered: tile row r (clamped to rows_valid - 1) is row
+// rowmap[r] / k of X (fewer than 2^31 elements, checked on the host).
+__device__ __forceinline__ void km_init_kc_gather(KmOp& o, const uint16_t* X, int64_t ldx,
+                                                  const int32_t* rowmap, int k, int rows_valid) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  o.r0 = make_rsrc(X);
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p) {
+    int r = geom::dma_row(p, w, l);
+    if (r > rows_valid - 1) r = rows_valid - 1;
+    o.off[p] = uint32_t((int64_t(rowmap[r] / k) * ldx + geom::dma_chunk(w, l) * 8) * 2);
+  }
+}
+
+// K-major weights: rows [0, ksplit) of W0, then rows of W1; tile columns n0 .. n0+255
+// of N (ld elements per row).
+__device__ __forceinline__ void km_init_weights(KmOp& o, const uint16_t* W0, const uint16_t* W1,
+                                                int ksplit, int64_t ld, int n0, int N) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  o.r0 = make_rsrc(W0);
+  o.r1 = make_rsrc(W1);
+  o.ld2 = uint32_t(ld * 2);
+  o.ksplit = ksplit;
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p)
+    o.off[p] = uint32_t((int64_t(geom::km_row(p, w, l)) * ld + geom::km_col(w, l, n0, N)) * 2);
+}
+
+// K-major routed rows [rbeg, rend): source row perm[r] / ktop (perm != null) or r of
+// M, ld elements per row; tile columns n0 .. n0+255 of N (col0 added to every column).
+__device__ __forceinline__ void km_init_rows(KmOp& o, const uint16_t* M, int64_t ld, int col0,
+                                             int n0, int N, const int32_t* perm, int ktop,
+                                             int rbeg, int rend) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  o.r0 = make_rsrc_2g_km(M);
+  o.ld2 = uint32_t(ld * 2);
+  o.perm = perm;
+  o.ktop = ktop;
+  o.rbeg = rbeg;
+  o.rend = rend;
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p) {
+    o.off[p] = uint32_t((col0 + geom::km_col(w, l, n0, N)) * 2);
+    const int r = rbeg + geom::km_row(p, w, l);
+    o.nxt[p] = perm ? perm[r < rend ? r : rend - 1] / ktop : 0;
+  }
+}
+
+template <int KIND, int STAGE>
+__device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (KIND == kKC) {
+#pragma unroll
+    for (int p = 0; p < geom::kLoads; ++p)
+      dma16<false>(o.r0, o.off[p], uint32_t(k0) * 2, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+  } else if (KIND == kKW) {
+    const bool second = k0 >= o.ksplit;
+    const uint32_t so = uint32_t(second ? k0 - o.ksplit : k0) * o.ld2;
+#pragma unroll
+    for (int p = 0; p < geom::kLoads; ++p)
+      dma16<false>(second ? o.r1 : o.r0, o.off[p], so,
+                   lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+  } else {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int p = 0; p < geom::kLoads; ++p) {
+      const int r = o.rbeg + k0 + geom::km_row(p, w, l);
+      const uint32_t src = o.perm ? uint32_t(o.nxt[p]) : uint32_t(r);
+      const uint32_t voff = r < o.rend ? src * o.ld2 + o.off[p] : kKmOutOfRange;
+      dma16<false>(o.r0, voff, 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+    }
+    if (o.perm) {  // source rows of the next step, one step ahead of their use
+#pragma unroll
+      for (int p = 0; p < geom::kLoads; ++p) {
+        const int r = o.rbeg + k0 + kBK + geom::km_row(p, w, l);
+        o.nxt[p] = o.perm[r < o.rend ? r : o.rend - 1] / o.ktop;
+      }
+    }
+  }
+}
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+// 8 K-consecutive bf16 of a K-major operand: two transposing reads, K rows +0..3, +4..7.
+__device__ __forceinline__ v4u km_frag(uint32_t addr) {
+  const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4s*>(uintptr_t(addr)));
+  const v4s_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4s*>(uintptr_t(addr + 4 * kKmRowBytes)));
+  typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+  const v2u_t a = __builtin_bit_cast(v2u_t, lo), b = __builtin_bit_cast(v2u_t, hi);
+  return v4u{a.x, a.y, b.x, b.y};
+}
+
+// Per-lane LDS byte address of the K-major fragment of 32-column block `blk` (columns
+// cw + 32 blk ..) for slice 0, read 0 of stage 0; slice ks adds 16 K rows, read 1 adds 4.
+__device__ __forceinline__ uint32_t km_frag_addr(uint32_t base, int cw, int blk) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, s = lane & 15;
+  const int col = cw + 32 * blk + 16 * (g & 1) + 4 * (s & 3);
+  const int kk = 8 * (g >> 1) + (s >> 2);
+  const int pos = (col >> 3) ^ (4 * (kk & 3));
+  return base + uint32_t(kk * kKmRowBytes + pos * 16 + (col & 7) * 2);
+}
+
+struct KmFragAddr {
+  uint32_t a[4], b[2];  // kKC A: per slice; K-major A: per block i; B: per block j
+};
+
+template <int AK>
+__device__ __forceinline__ void km_frag_addr_init(KmFragAddr& fa) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  if (AK == kKC) {
+    const int r32 = lane & 31;
+    const uint32_t a0 = lds_addr(g_lds_a) + uint32_t(wm * 128 + r32) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      fa.a[ks] = a0 + uint32_t(((ks * 2 + (lane >> 5)) ^ lds_swz(r32)) * 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa.a[i] = km_frag_addr(lds_addr(g_lds_a), wm * 128, i);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fa.b[j] = km_frag_addr(lds_addr(g_lds_b), wn * 64, j);
+}
+
+template <int AK, int S>
+__device__ __forceinline__ void km_frag_load(TileFrag& f, const KmFragAddr& fa, int ks) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (AK == kKC)
+      f.a[i] = *reinterpret_cast<lds_cv4u*>(uintptr_t(fa.a[ks] + S * kStageBytes + i * 32 * 128));
+    else
+      f.a[i] = km_frag(fa.a[i] + S * kStageBytes + ks * 16 * kKmRowBytes);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[j] = km_frag(fa.b[j] + S * kStageBytes + ks * 16 * kKmRowBytes);
+}
+
+template <int AK, int BK, int S>
+__device__ __forceinline__ void km_issue_step(KmOp& a, KmOp& b, int k0) {
+  km_issue<AK, S>(a, k0, g_lds_a);
+  km_issue<BK, S>(b, k0, g_lds_b);
+}
+
+// One K step kb in stage S, as tile_step.
+template <int AK, int BK, int S>
+__device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, int kb, int nk,
+                                        TileFrag& f0, TileFrag& f1, TileAcc& acc) {
+  constexpr int SN = S ^ 1;
+  km_frag_load<AK, S>(f1, fa, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  km_frag_load<AK, S>(f0, fa, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  km_frag_load<AK, S>(f1, fa, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kb + 1 < nk) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + 2 < nk) km_issue_step<AK, BK, S>(a, b, (kb + 2) * kBK);
+    km_frag_load<AK, SN>(f0, fa, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  frag_mma(f1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K loop of nk steps over operands a (kind AK: kKC or kKR) and b (kind BK: kKW or kKR).
+// C = A B^T as for tile_gemm, with A's tile row m / B's tile row n read as column m / n
+// of a K-major operand.  Ends with a barrier.
+template <int AK, int BK>
+__device__ __forceinline__ void tile_gemm_km(KmOp& a, KmOp& b, int nk, TileAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
+  if (nk <= 0) return;
+  asm volatile("" ::: "memory");
+  km_issue_step<AK, BK, 0>(a, b, 0);
+  if (nk > 1) {
+    km_issue_step<AK, BK, 1>(a, b, kBK);
+    wait_vmcnt<2 * geom::kLoads>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  KmFragAddr fa;
+  km_frag_addr_init<AK>(fa);
+  TileFrag f0, f1;
+  km_frag_load<AK, 0>(f0, fa, 0);
+  for (int kb = 0; kb < nk; kb += 2) {
+    km_step<AK, BK, 0>(a, b, fa, kb, nk, f0, f1, acc);
+    if (kb + 1 < nk) km_step<AK, BK, 1>(a, b, fa, kb + 1, nk, f0, f1, acc);
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // A value the compiler must treat as produced here: epilogue address arithmetic derived
 // from it cannot be hoisted above the K loop, where it would hold registers.
 __device__ __forceinline__ int opaque(int x) {

@@ -33,8 +33,6 @@ struct Ptrs {
   uint16_t* bdab;     // [T*k, 2I] their gradients
   uint16_t* dxbuf;    // [T*k, D] per-pair dX contributions (pair-indexed)
   float* dgpart;      // [T*k, nNdh] router-weight gradient partials per dH n-tile
-  uint16_t* wdt;      // [E_loc, I, D] W_down transposed
-  uint16_t* wgut;     // [E_loc, D, 2I] [W_gate | W_up] transposed
   uint16_t* xt;       // [D, TKP] panels of X columns per expert
   uint16_t* gdyt;     // [D, TKP] panels of gate * dY
   uint16_t* ht;       // [I, TKP] panels of h
@@ -71,8 +69,6 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.bdab = u16(L.off_bdab);
   P.dxbuf = u16(L.off_dxbuf);
   P.dgpart = L.save ? reinterpret_cast<float*>(b + L.off_dgpart) : nullptr;
-  P.wdt = u16(L.off_wdt);
-  P.wgut = u16(L.off_wgut);
   P.xt = u16(L.off_xt);
   P.gdyt = u16(L.off_gdyt);
   P.ht = u16(L.off_ht);

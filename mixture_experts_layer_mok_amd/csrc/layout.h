@@ -64,8 +64,8 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t TKP;      // width of the transposed per-expert panels: T*k + 64*E_loc
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
-  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_wdt, off_wgut, off_xt, off_gdyt, off_ht,
-      off_dat, off_dbt, off_roff;
+  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_xt, off_gdyt, off_ht, off_dat, off_dbt,
+      off_roff;
   size_t total;
 };
 
@@ -164,10 +164,10 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->TKP = align_up(size_t(L->TK), 64) + 64 * nl;
   L->nNdh = (I + kBN2 - 1) / kBN2;
   L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = 0;
-  L->off_wdt = L->off_wgut = L->off_xt = L->off_gdyt = L->off_ht = L->off_dat = L->off_dbt = 0;
+  L->off_xt = L->off_gdyt = L->off_ht = L->off_dat = L->off_dbt = 0;
   L->off_roff = 0;
   if (L->save) {
-    // panel and transposed-weight offsets of the backward GEMM tiles stay below 2^32 bytes
+    // panel and weight offsets of the backward GEMM tiles stay below 2^32 bytes
     // ... and the backward GEMMs read X and dY rows in place (offsets from their bases)
     if ((D > I ? D : I) * L->TKP >= (int64_t(1) << 31) || 2 * I * D >= (int64_t(1) << 31) ||
         T * D >= (int64_t(1) << 31))
@@ -177,8 +177,6 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_bdab = o; o = align_up(o + TK * 2 * I * 2, A);
     L->off_dxbuf = o; o = align_up(o + TK * D * 2, A);
     L->off_dgpart = o; o = align_up(o + TK * L->nNdh * 4, A);
-    L->off_wdt = o; o = align_up(o + size_t(nl) * I * D * 2, A);
-    L->off_wgut = o; o = align_up(o + size_t(nl) * D * 2 * I * 2, A);
     L->off_xt = o; o = align_up(o + size_t(D) * TKP * 2, A);
     L->off_gdyt = o; o = align_up(o + size_t(D) * TKP * 2, A);
     L->off_ht = o; o = align_up(o + size_t(I) * TKP * 2, A);

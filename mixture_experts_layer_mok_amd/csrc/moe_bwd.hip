@@ -63,54 +63,6 @@ __global__ __launch_bounds__(64) void k_bwd_prep(BwdParams p) {
 }
 
 
-// 64 x 64 transpose through LDS: dst[c][r] = src[r][c] for a [rows, cols] block of a
-// batch item.  Each thread moves 16 bytes on both sides.
-__device__ __forceinline__ void transpose_tile(const uint16_t* src, int64_t lds_src, int rows,
-                                               int cols, uint16_t* dst, int64_t ldd, int r0,
-                                               int c0, uint16_t (*tile)[72]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + t;  // 512 chunks of 8 elements
-    const int r = idx >> 3, c8 = (idx & 7) * 8;
-    v4u v = v4u{0u, 0u, 0u, 0u};
-    if (r0 + r < rows && c0 + c8 < cols)
-      v = *reinterpret_cast<const v4u*>(src + int64_t(r0 + r) * lds_src + c0 + c8);
-    *reinterpret_cast<v4u*>(&tile[r][c8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + t;
-    const int c = idx >> 3, r8 = (idx & 7) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = uint32_t(tile[r8 + 2 * e][c]) | (uint32_t(tile[r8 + 2 * e + 1][c]) << 16);
-    if (c0 + c < cols && r0 + r8 < rows)
-      *reinterpret_cast<v4u*>(dst + int64_t(c0 + c) * ldd + r0 + r8) = v4u{w[0], w[1], w[2], w[3]};
-  }
-  __syncthreads();
-}
-
-// W_down[e] [D, I] -> wdt[e] [I, D];  W_gate[e], W_up[e] [I, D] -> wgut[e] [D, 2I].
-// grid: (max(D, I)/64 column blocks, max(D, I)/64 row blocks, 3 * E_loc)
-__global__ __launch_bounds__(256) void k_bwd_transpose_weights(BwdParams p) {
-  __shared__ uint16_t tile[64][72];
-  const int which = blockIdx.z % 3, e = blockIdx.z / 3;
-  const int64_t wsz = int64_t(p.I) * p.D;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  if (which == 0) {
-    if (r0 >= p.D || c0 >= p.I) return;
-    transpose_tile(p.a.wd + e * wsz, p.I, p.D, p.I, p.P.wdt + e * wsz, p.D, r0, c0, tile);
-  } else {
-    if (r0 >= p.I || c0 >= p.D) return;
-    const uint16_t* src = (which == 1 ? p.a.wg : p.a.wu) + e * wsz;
-    uint16_t* dst = p.P.wgut + e * 2 * wsz + (which == 1 ? 0 : p.I);
-    transpose_tile(src, p.D, p.I, p.D, dst, 2 * int64_t(p.I), r0, c0, tile);
-  }
-}
-
 // Expert panels of X and of gate * dY: column roff[e] + q holds routed row offsets[e] + q
 // of expert e (zero for q >= count[e]).  grid: (TKP / 64, D / 64).
 __global__ __launch_bounds__(256) void k_bwd_panels(BwdParams p) {
@@ -212,7 +164,8 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
   }
 }
 
-// dH GEMM: u = dY rows x W_down[e] (wdt rows), fused SwiGLU backward and dG partials.
+// dH GEMM: u = dY rows x W_down[e] (K = D over the rows of W_down, read K-major), fused
+// SwiGLU backward and dG partials.
 __global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
   const int nq = int(p.P.hdr[kHdrMtiles]) * p.nNdh;
   const int64_t wsz = int64_t(p.I) * p.D;
@@ -222,33 +175,34 @@ __global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
     mtile_at(p, q / p.nNdh, e, mb);
     const int nt = q % p.nNdh;
     const int n0 = nt * kBN2;
-    const uint16_t* wdt = p.P.wdt + e.z * wsz;
-    TileSrc src;
-    tile_src_init_gather(src, geom::kSplit, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y, wdt, wdt,
-                         p.D, n0, n0 + 128, p.I);
+    const uint16_t* wd = p.a.wd + e.z * wsz;
+    KmOp a, b;
+    km_init_kc_gather(a, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y);
+    km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
     TileAcc acc;
-    tile_gemm<false>(src, p.D, acc);
+    tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
     const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
     epi_dh(acc, e.y, e.x, pc0, p.P.roff[e.z + 1], n0, p.I, p.TKP, ab_rows(p, e, mb), p.a.gates,
            p.P.perm, p.P.bdab, p.P.ht, p.P.dat, p.P.dbt, p.P.dgpart, nt, p.nNdh);
   }
 }
 
-// dX GEMM: dx rows = [da | db] x [W_gate; W_up][e] (wgut rows), pushed to their pairs.
+// dX GEMM: dx rows = [da | db] x [W_gate; W_up][e] (K = 2I over the rows of W_gate, then
+// W_up, read K-major), pushed to their pairs.
 __global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
   const int nq = int(p.P.hdr[kHdrMtiles]) * p.nDt;
   const int64_t K = 2 * int64_t(p.I);
+  const int64_t wsz = int64_t(p.I) * p.D;
   for (int q = blockIdx.x; q < nq; q += gridDim.x) {
     int4 e;
     int mb;
     mtile_at(p, q / p.nDt, e, mb);
     const int n0 = (q % p.nDt) * kBN2;
-    const uint16_t* wg = p.P.wgut + e.z * K * p.D;
-    TileSrc src;
-    tile_src_init(src, geom::kSplit, p.P.bdab + int64_t(e.x) * K, K, e.y, wg, wg, K, n0,
-                  n0 + 128, p.D);
+    KmOp a, b;
+    km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
+    km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
     TileAcc acc;
-    tile_gemm<false>(src, int(K), acc);
+    tile_gemm_km<kKC, kKW>(a, b, int(K / kBK), acc);
     epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
   }
 }
@@ -353,10 +307,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
       cus <= 0)
     return MOK_E_DEVICE;
   const dim3 tiles_grid = dim3(unsigned(cus));  // one 512-thread tile workgroup fits a CU
-  const unsigned dmax = unsigned((std::max(L.D, L.I) + 63) / 64);
   hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_transpose_weights, dim3(dmax, dmax, unsigned(3 * L.nl)), dim3(256), 0,
-                     st, p);
   hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
                      p);
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);

@@ -35,6 +35,24 @@ static int check(const char* what, int layout, int K, int64_t lda, int64_t ldb, 
   return bad;
 }
 
+// K-major weight operand: a matrix of Kmat rows of N columns (ld = N); the tile reads
+// columns n0 .. n0 + 255 (clamped below N) of K rows k0 + 0..63 for every step k0.
+static int check_km_weights(const char* what, int Kmat, int N, int n0) {
+  const int64_t bytes = int64_t(Kmat) * N * 2;
+  int bad = 0;
+  for (int k0 = 0; k0 < Kmat; k0 += kBK)
+    for (int p = 0; p < mok::geom::kLoads; ++p)
+      for (int w = 0; w < mok::geom::kWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int c = mok::geom::km_col(w, l, n0, N);
+          const int64_t off =
+              (int64_t(mok::geom::km_row(p, w, l)) * N + c) * 2 + int64_t(k0) * N * 2;
+          if (c < 0 || c + 8 > N || off < 0 || off + 16 > bytes || off >= (int64_t(1) << 32)) ++bad;
+        }
+  if (bad) std::printf("%s: %d bad offsets (Kmat=%d N=%d n0=%d)\n", what, bad, Kmat, N, n0);
+  return bad;
+}
+
 static int check_mx(const char* what, int layout, int K, int64_t lda, int64_t as_ld, int rows,
                     int64_t ldb, int64_t bs_ld, int N, int n0, int nb1) {
   const int nk = (K + 127) / 128;
@@ -79,8 +97,9 @@ int main(int argc, char** argv) {
       bad += check("gemm1", mok::geom::kPaired, D, D, D, I, n0, n0, rows);
     for (int n0 = 0; n0 < D; n0 += kBN2)
       bad += check("gemm2", mok::geom::kSplit, I, I, I, D, n0, n0 + 128, rows);
-    // backward: dH (A = dY rows, B = W_down^T [I, D]), dX (A = [da|db] rows, B =
-    // [W_gate|W_up]^T [D, 2I]), dW (A, B = expert panels of width TKP, K <= panel width)
+    // backward: dH's A = dY rows (K = D), dX's A = [da|db] rows (K = 2I); their B
+    // operands are K-major weights (below); dW (A, B = expert panels of width TKP, K <=
+    // panel width)
     for (int n0 = 0; n0 < I; n0 += kBN2)
       bad += check("dh", mok::geom::kSplit, D, D, D, I, n0, n0 + 128, rows);
     for (int n0 = 0; n0 < D; n0 += kBN2)
@@ -100,6 +119,23 @@ int main(int argc, char** argv) {
     for (int K : {64, 1024, 4096})
       for (int n0 = 0; n0 < I; n0 += kBN2)
         bad += check("dw", mok::geom::kSplit, K, TKP, TKP, I, n0, n0 + 128, rows);
+  }
+  // K-major weights: dH reads W_down [D rows, I columns], dX W_gate / W_up [I rows, D
+  // columns] (K = 2I: the steps of each matrix stay inside it)
+  for (int n0 = 0; n0 < I; n0 += kBN2) bad += check_km_weights("dh-wd", D, I, n0);
+  for (int n0 = 0; n0 < D; n0 += kBN2) bad += check_km_weights("dx-wgu", I, D, n0);
+  // K-major stage: each stage row gets its 32 chunks once, logical chunks a permutation
+  for (int kk = 0; kk < 64; ++kk) {
+    unsigned seen = 0;
+    int loads = 0;
+    for (int p = 0; p < mok::geom::kLoads; ++p)
+      for (int w = 0; w < mok::geom::kWaves; ++w)
+        for (int l = 0; l < 64; ++l)
+          if (mok::geom::km_row(p, w, l) == kk) {
+            ++loads;
+            seen |= 1u << mok::geom::km_chunk(w, l);
+          }
+    if (loads != 32 || seen != 0xFFFFFFFFu) ++bad;
   }
   // paired layout: tile rows of block b cover intermediate columns n0 + 16 b .. +15 of
   // both matrices, each exactly once (unclamped case)

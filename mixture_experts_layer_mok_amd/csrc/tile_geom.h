@@ -66,6 +66,20 @@ MOK_HD inline int64_t b_offset(int layout, int p, int w, int l, int nb0, int nb1
   return (int64_t(b_row(layout, p, w, l, nb0, nb1, N)) * ldb + dma_chunk(w, l) * 8) * 2;
 }
 
+// K-major operands (the backward reads weights and routed-row matrices as stored, with
+// K running over their rows): a stage holds 64 K rows of 256 tile columns, 32 chunks of
+// 16 bytes per row, logical chunk c of stage row kk at position c ^ (4 (kk & 3)).  Load p
+// of wave w, lane l fills stage row (8p + w) * 2 + l / 32 at position l % 32; kk & 3
+// depends on w and l only.
+MOK_HD inline int km_row(int p, int w, int l) { return (p * 8 + w) * 2 + (l >> 5); }
+MOK_HD inline int km_chunk(int w, int l) { return (l & 31) ^ (4 * (((w << 1) + (l >> 5)) & 3)); }
+// First tile column of that chunk, clamped so that its 8 columns stay below N (columns
+// past N are never stored).
+MOK_HD inline int km_col(int w, int l, int n0, int N) {
+  const int c = n0 + 8 * km_chunk(w, l);
+  return c > N - 8 ? N - 8 : c;
+}
+
 // MXFP8 tiles: one K step is 128 code bytes per row (8 chunks: the same direct-to-LDS
 // geometry, with rows of ld / 2 two-byte units) plus one dword of 4 e8m0 scales per
 // row.  Lanes of waves 0-3 load the scale dword of A tile row (w % 4) * 64 + l, lanes
