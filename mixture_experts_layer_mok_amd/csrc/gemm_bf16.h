@@ -302,8 +302,9 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //   kKW  K-major weight matrix [K rows][ld]: tile column n is column n of every row;
 //        K rows past ksplit come from a second matrix (dX stacks W_gate over W_up);
 //   kKR  K-major routed rows: K index q is routed row rbeg + q, whose data is row
-//        perm[r] / ktop of a token matrix (gathered) or row r of a row matrix; rows at
-//        or past rend read zero (bit 31 of the offset, against a 2 GB resource).
+//        tok[r] of a token matrix (gathered; tok = the token of each routed row) or row
+//        r of a row matrix; rows at or past rend read zero (bit 31 of the offset,
+//        against a 2 GB resource).
 enum KmKind { kKC = 0, kKW = 1, kKR = 2 };
 constexpr uint32_t kKmOutOfRange = 0x80000000u;
 constexpr int kKmRowBytes = 512;  // one staged K row: 256 bf16
@@ -313,9 +314,9 @@ struct KmOp {
   uint32_t off[geom::kLoads];  // kKC / kKW: per-lane byte offsets; kKR: column bytes
   uint32_t ld2;                // kKW: bytes per K row; kKR: bytes per source row
   int ksplit;                  // kKW
-  const int32_t* perm;         // kKR: gathered source rows (null: row r itself)
-  int ktop, rbeg, rend;        // kKR
-  int32_t nxt[geom::kLoads];   // kKR with perm: source rows of the next step to issue
+  const int32_t* tok;          // kKR: source row of each routed row (null: row r itself)
+  int rbeg, rend;              // kKR
+  int32_t nxt[geom::kLoads];   // kKR with tok: source rows of the next step to issue
 };
 
 __device__ __forceinline__ i32x4_t make_rsrc_2g_km(const void* base) {
@@ -362,28 +363,27 @@ __device__ __forceinline__ void km_init_weights(KmOp& o, const uint16_t* W0, con
     o.off[p] = uint32_t((int64_t(geom::km_row(p, w, l)) * ld + geom::km_col(w, l, n0, N)) * 2);
 }
 
-// K-major routed rows [rbeg, rend): source row perm[r] / ktop (perm != null) or r of
-// M, ld elements per row; tile columns n0 .. n0+255 of N (col0 added to every column).
+// K-major routed rows [rbeg, rend): source row tok[r] (tok != null) or r of M, ld
+// elements per row; tile columns n0 .. n0+255 of N (col0 added to every column).
 __device__ __forceinline__ void km_init_rows(KmOp& o, const uint16_t* M, int64_t ld, int col0,
-                                             int n0, int N, const int32_t* perm, int ktop,
-                                             int rbeg, int rend) {
+                                             int n0, int N, const int32_t* tok, int rbeg,
+                                             int rend) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   o.r0 = make_rsrc_2g_km(M);
   o.ld2 = uint32_t(ld * 2);
-  o.perm = perm;
-  o.ktop = ktop;
+  o.tok = tok;
   o.rbeg = rbeg;
   o.rend = rend;
 #pragma unroll
   for (int p = 0; p < geom::kLoads; ++p) {
     o.off[p] = uint32_t((col0 + geom::km_col(w, l, n0, N)) * 2);
     const int r = rbeg + geom::km_row(p, w, l);
-    o.nxt[p] = perm ? perm[r < rend ? r : rend - 1] / ktop : 0;
+    o.nxt[p] = tok && rend > rbeg ? tok[r < rend ? r : rend - 1] : 0;
   }
 }
 
 template <int KIND, int STAGE>
-__device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
+__device__ __forceinline__ void km_issue(const KmOp& o, int k0, v4u* lds) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (KIND == kKC) {
 #pragma unroll
@@ -401,17 +401,27 @@ __device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
 #pragma unroll
     for (int p = 0; p < geom::kLoads; ++p) {
       const int r = o.rbeg + k0 + geom::km_row(p, w, l);
-      const uint32_t src = o.perm ? uint32_t(o.nxt[p]) : uint32_t(r);
-      const uint32_t voff = r < o.rend ? src * o.ld2 + o.off[p] : kKmOutOfRange;
+      // source row below 2^24 and row bytes below 2^24 (checked on the host)
+      const uint32_t src = o.tok ? uint32_t(o.nxt[p]) : uint32_t(r);
+      const uint32_t voff = r < o.rend ? __umul24(src, o.ld2) + o.off[p] : kKmOutOfRange;
       dma16<false>(o.r0, voff, 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
     }
-    if (o.perm) {  // source rows of the next step, one step ahead of their use
+  }
+}
+
+// kKR with tok: the source rows of step k0 + kBK, loaded one step ahead of their use.
+// Called after every load of step k0 has been issued: nothing reads them before the
+// next step's wait, and a wait for them would also wait for loads issued before them.
+template <int KIND>
+__device__ __forceinline__ void km_prefetch(KmOp& o, int k0) {
+  if (KIND != kKR) return;
+  if (!o.tok) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
 #pragma unroll
-      for (int p = 0; p < geom::kLoads; ++p) {
-        const int r = o.rbeg + k0 + kBK + geom::km_row(p, w, l);
-        o.nxt[p] = o.perm[r < o.rend ? r : o.rend - 1] / o.ktop;
-      }
-    }
+  for (int p = 0; p < geom::kLoads; ++p) {
+    const int r = o.rbeg + k0 + kBK + geom::km_row(p, w, l);
+    o.nxt[p] = o.tok[r < o.rend ? r : o.rend - 1];
   }
 }
 
@@ -479,6 +489,8 @@ template <int AK, int BK, int S>
 __device__ __forceinline__ void km_issue_step(KmOp& a, KmOp& b, int k0) {
   km_issue<AK, S>(a, k0, g_lds_a);
   km_issue<BK, S>(b, k0, g_lds_b);
+  km_prefetch<AK>(a, k0);
+  km_prefetch<BK>(b, k0);
 }
 
 // One K step kb in stage S, as tile_step.

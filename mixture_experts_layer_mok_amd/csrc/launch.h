@@ -33,12 +33,8 @@ struct Ptrs {
   uint16_t* bdab;     // [T*k, 2I] their gradients
   uint16_t* dxbuf;    // [T*k, D] per-pair dX contributions (pair-indexed)
   float* dgpart;      // [T*k, nNdh] router-weight gradient partials per dH n-tile
-  uint16_t* xt;       // [D, TKP] panels of X columns per expert
-  uint16_t* gdyt;     // [D, TKP] panels of gate * dY
-  uint16_t* ht;       // [I, TKP] panels of h
-  uint16_t* dat;      // [I, TKP] panels of dL/da
-  uint16_t* dbt;      // [I, TKP] panels of dL/db
-  int32_t* roff;      // [E_loc + 1] first panel column of each expert
+  uint16_t* gh;       // [T*k, I] gate weight times h per routed row (dW_down operand)
+  int32_t* tok;       // [T*k] token of each routed row
 };
 
 inline Ptrs make_ptrs(const Layout& L, void* ws) {
@@ -69,12 +65,8 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.bdab = u16(L.off_bdab);
   P.dxbuf = u16(L.off_dxbuf);
   P.dgpart = L.save ? reinterpret_cast<float*>(b + L.off_dgpart) : nullptr;
-  P.xt = u16(L.off_xt);
-  P.gdyt = u16(L.off_gdyt);
-  P.ht = u16(L.off_ht);
-  P.dat = u16(L.off_dat);
-  P.dbt = u16(L.off_dbt);
-  P.roff = L.save ? reinterpret_cast<int32_t*>(b + L.off_roff) : nullptr;
+  P.gh = u16(L.off_gh);
+  P.tok = L.save ? reinterpret_cast<int32_t*>(b + L.off_tok) : nullptr;
   return P;
 }
 

@@ -62,10 +62,8 @@ struct Layout {
   size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
   size_t off_wsg, off_wsu, off_wsd;  // repacked weight scales (MXFP8, when needed)
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
-  int64_t TKP;      // width of the transposed per-expert panels: T*k + 64*E_loc
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
-  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_xt, off_gdyt, off_ht, off_dat, off_dbt,
-      off_roff;
+  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_tok;
   size_t total;
 };
 
@@ -158,31 +156,24 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   if (L->repack_wd) {
     L->off_wsd = o; o = align_up(o + size_t(nl) * D * L->wds_ld, A);
   }
-  // backward regions (present when the forward saves for backward).  Row buffers are
-  // indexed by routed row (at most T*k rows); the transposed panels hold, per local
-  // expert, its rows as columns, padded with zeros to a multiple of 64.
-  L->TKP = align_up(size_t(L->TK), 64) + 64 * nl;
+  // backward regions (present when the forward saves for backward): row buffers indexed
+  // by routed row (at most T*k rows).
   L->nNdh = (I + kBN2 - 1) / kBN2;
-  L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = 0;
-  L->off_xt = L->off_gdyt = L->off_ht = L->off_dat = L->off_dbt = 0;
-  L->off_roff = 0;
+  L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = L->off_gh = L->off_tok = 0;
   if (L->save) {
-    // panel and weight offsets of the backward GEMM tiles stay below 2^32 bytes
-    // ... and the backward GEMMs read X and dY rows in place (offsets from their bases)
-    if ((D > I ? D : I) * L->TKP >= (int64_t(1) << 31) || 2 * I * D >= (int64_t(1) << 31) ||
-        T * D >= (int64_t(1) << 31))
+    // the backward GEMMs read weights with 32-bit offsets, and X, dY, [da | db] and g h
+    // rows as K-major routed rows, whose offsets stay below 2^31 bytes (bit 31 marks a
+    // row past the expert's end)
+    if (2 * I * D >= (int64_t(1) << 31) || 2 * T * D >= (int64_t(1) << 31) ||
+        L->TK * 4 * I >= (int64_t(1) << 31))
       return MOK_E_SHAPE;
-    const size_t TK = size_t(L->TK), TKP = size_t(L->TKP);
+    const size_t TK = size_t(L->TK);
     L->off_bab = o; o = align_up(o + TK * 2 * I * 2, A);
     L->off_bdab = o; o = align_up(o + TK * 2 * I * 2, A);
     L->off_dxbuf = o; o = align_up(o + TK * D * 2, A);
     L->off_dgpart = o; o = align_up(o + TK * L->nNdh * 4, A);
-    L->off_xt = o; o = align_up(o + size_t(D) * TKP * 2, A);
-    L->off_gdyt = o; o = align_up(o + size_t(D) * TKP * 2, A);
-    L->off_ht = o; o = align_up(o + size_t(I) * TKP * 2, A);
-    L->off_dat = o; o = align_up(o + size_t(I) * TKP * 2, A);
-    L->off_dbt = o; o = align_up(o + size_t(I) * TKP * 2, A);
-    L->off_roff = o; o = align_up(o + (nl + 1) * 4, A);
+    L->off_gh = o; o = align_up(o + TK * I * 2, A);
+    L->off_tok = o; o = align_up(o + TK * 4, A);
   }
   L->total = o;
   return MOK_OK;

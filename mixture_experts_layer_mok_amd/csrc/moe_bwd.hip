@@ -4,16 +4,16 @@
 // transfers, pulling dY by the schedule's table and pushing dX contributions back to
 // their tokens; news brief, design decisions: the router-weight gradient is formed
 // inside the SwiGLU backward), per routed row r of expert e (token t, slot j, gate g):
-//   u = dY[t] W_down[e]                      dH GEMM, against W_down transposed
+//   u = dY[t] W_down[e]                      dH GEMM (K over the rows of W_down)
 //   dG[t,j] = <u, h>                          in the dH epilogue (no second pass over o)
 //   da, db  = SwiGLU backward of g u          in the dH epilogue
-//   dx_r = da W_gate[e] + db W_up[e]          dX GEMM, against [W_gate | W_up] transposed
+//   dx_r = da W_gate[e] + db W_up[e]          dX GEMM (K over the rows of W_gate, W_up)
 //   dX[t] = sum over local slots j (ascending) of dx_r          fixed order
-//   dW_down[e] = sum_r (g dY[t])^T h,  dW_gate[e] = sum_r da^T x,  dW_up[e] = sum_r db^T x
-// The dW contractions run over the expert's rows; both operands are read from per-expert
-// transposed panels (rows of the expert as columns, zero padded to a multiple of 64) so
-// that every MFMA operand is K-contiguous, and each dW tile has one owner and one K
-// order: no atomics, bitwise reproducible.
+//   dW_down[e] = sum_r dY[t]^T (g h),  dW_gate[e] = sum_r da^T x,  dW_up[e] = sum_r db^T x
+// The GEMMs whose contraction runs over rows of a stored matrix (the weights for dH and
+// dX, the expert's routed rows for dW) read that operand K-major as stored, through
+// gfx950's transposing LDS reads: nothing is transposed in memory.  Each dW tile has one
+// owner and one K order (the expert's rows ascending): no atomics, bitwise reproducible.
 //
 // This file holds the path as separate kernels.  The gate/up pre-activations a, b come
 // from the forward where it still holds them and are recomputed otherwise (replay of
@@ -31,7 +31,6 @@ struct BwdParams {
   Ptrs P;
   BwdArgs a;
   int T, D, I, k, nl, mt_max, nDt, nIt, nNdh, n_mb_max, S;
-  int64_t TKP;
   int64_t slot_bytes, slot_ab;
   int ab_saved;  // 1: the forward wrote a, b of every row (unfused); 0: ring only (fused)
   int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
@@ -47,74 +46,12 @@ __device__ __forceinline__ const uint16_t* ab_rows(const BwdParams& p, const int
   return p.P.bab + int64_t(e.x) * 2 * p.I;
 }
 
-// ------------------------------------------------------------------------------------
-// preparation
-// ------------------------------------------------------------------------------------
-// Panel column offsets: roff[e+1] = roff[e] + round_up(count[e], 64).
-__global__ __launch_bounds__(64) void k_bwd_prep(BwdParams p) {
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    p.P.roff[0] = 0;
-    for (int e = 0; e < p.nl; ++e) {
-      acc += (p.P.counts[e] + 63) & ~63;
-      p.P.roff[e + 1] = acc;
-    }
-  }
-}
-
-
-// Expert panels of X and of gate * dY: column roff[e] + q holds routed row offsets[e] + q
-// of expert e (zero for q >= count[e]).  grid: (TKP / 64, D / 64).
-__global__ __launch_bounds__(256) void k_bwd_panels(BwdParams p) {
-  __shared__ uint16_t tx[64][72];
-  __shared__ uint16_t tg[64][72];
-  const int pc0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
-  if (pc0 >= p.P.roff[p.nl]) return;
-  int e = 0;
-  while (p.P.roff[e + 1] <= pc0) ++e;
-  const int q0 = pc0 - p.P.roff[e];
-  const int cnt = p.P.counts[e];
-  const int rbase = p.P.offsets[e] + q0;
-  const int t = threadIdx.x;
-  // rows of the 64 x 64 block: panel column c <-> routed row rbase + c
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + t;
-    const int c = idx >> 3, d8 = (idx & 7) * 8;
-    v4u vx = v4u{0u, 0u, 0u, 0u}, vg = v4u{0u, 0u, 0u, 0u};
-    if (q0 + c < cnt && d0 + d8 < p.D) {
-      const int q = p.P.perm[rbase + c];
-      const int64_t tok = q / p.k;
-      vx = *reinterpret_cast<const v4u*>(p.a.x + tok * p.D + d0 + d8);
-      const v4u vy = *reinterpret_cast<const v4u*>(p.a.dy + tok * p.D + d0 + d8);
-      const float g = p.a.gates[q];
-      const uint32_t w[4] = {vy.x, vy.y, vy.z, vy.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        o[e2] = pack_bf16x2(g * bf16_to_f32(uint16_t(w[e2] & 0xFFFF)),
-                            g * bf16_to_f32(uint16_t(w[e2] >> 16)));
-      vg = v4u{o[0], o[1], o[2], o[3]};
-    }
-    *reinterpret_cast<v4u*>(&tx[c][d8]) = vx;
-    *reinterpret_cast<v4u*>(&tg[c][d8]) = vg;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + t;
-    const int d = idx >> 3, c8 = (idx & 7) * 8;
-    if (d0 + d >= p.D) continue;
-    uint32_t wx[4], wg[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      wx[e2] = uint32_t(tx[c8 + 2 * e2][d]) | (uint32_t(tx[c8 + 2 * e2 + 1][d]) << 16);
-      wg[e2] = uint32_t(tg[c8 + 2 * e2][d]) | (uint32_t(tg[c8 + 2 * e2 + 1][d]) << 16);
-    }
-    const int64_t off = int64_t(d0 + d) * p.TKP + pc0 + c8;
-    *reinterpret_cast<v4u*>(p.P.xt + off) = v4u{wx[0], wx[1], wx[2], wx[3]};
-    *reinterpret_cast<v4u*>(p.P.gdyt + off) = v4u{wg[0], wg[1], wg[2], wg[3]};
-  }
+// Token of every routed row, tok[r] = perm[r] / k: the dW tiles gather X and dY rows by
+// it without a division in their load loop.
+__global__ __launch_bounds__(256) void k_bwd_tok(BwdParams p) {
+  const int R = int(p.P.hdr[kHdrR]);
+  for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256)
+    p.P.tok[r] = p.P.perm[r] / p.k;
 }
 
 // ------------------------------------------------------------------------------------
@@ -181,9 +118,8 @@ __global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
     km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
     TileAcc acc;
     tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
-    const int pc0 = p.P.roff[e.z] + (e.x - p.P.offsets[e.z]);
-    epi_dh(acc, e.y, e.x, pc0, p.P.roff[e.z + 1], n0, p.I, p.TKP, ab_rows(p, e, mb), p.a.gates,
-           p.P.perm, p.P.bdab, p.P.ht, p.P.dat, p.P.dbt, p.P.dgpart, nt, p.nNdh);
+    epi_dh(acc, e.y, e.x, n0, p.I, ab_rows(p, e, mb), p.a.gates, p.P.perm, p.P.bdab, p.P.gh,
+           p.P.dgpart, nt, p.nNdh);
   }
 }
 
@@ -207,34 +143,36 @@ __global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
   }
 }
 
-// dW GEMMs over the expert panels.  Per expert: dW_down tiles (D x I), then dW_gate and
-// dW_up tiles (I x D); K = the expert's padded row count (zero rows give zero tiles).
+// dW GEMMs, K over the expert's routed rows in ascending order, both operands read
+// K-major as stored: per expert, dW_down tiles (D x I: A = dY rows gathered by perm,
+// B = g h rows), then dW_gate and dW_up tiles (I x D: A = da / db rows, B = X rows
+// gathered by token).  Rows past the expert's last read zero; an expert without rows
+// gets zero tiles.  One workgroup owns each tile: no atomics.
 __global__ __launch_bounds__(512) void k_bwd_dw(BwdParams p) {
   const int per = p.nDt * p.nIt;
   const int e = blockIdx.x / (3 * per);
   const int q = blockIdx.x % (3 * per);
   const int which = q / per, r = q % per;
-  const int c0 = p.P.roff[e];
-  const int K = p.P.roff[e + 1] - c0;
+  const int rbeg = p.P.offsets[e], rend = rbeg + p.P.counts[e];
   const int64_t wsz = int64_t(p.I) * p.D;
-  const uint16_t *A, *B;
+  KmOp a, b;
   float* C;
-  int M, N, mt, nt;
-  if (which == 0) {  // dW_down[e] = gdY^T h : rows d, columns i
-    M = p.D; N = p.I; mt = r / p.nIt; nt = r % p.nIt;
-    A = p.P.gdyt; B = p.P.ht; C = p.a.dwd + e * wsz;
-  } else {           // dW_gate / dW_up[e] = da^T x / db^T x : rows i, columns d
-    M = p.I; N = p.D; mt = r / p.nDt; nt = r % p.nDt;
-    A = which == 1 ? p.P.dat : p.P.dbt; B = p.P.xt; C = (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz;
+  int M, N, m0, n0;
+  if (which == 0) {  // dW_down[e][d][i] = sum_r dY[t_r][d] (g h)[r][i]
+    M = p.D; N = p.I; m0 = (r / p.nIt) * kBM; n0 = (r % p.nIt) * kBN2;
+    km_init_rows(a, p.a.dy, p.D, 0, m0, p.D, p.P.tok, rbeg, rend);
+    km_init_rows(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
+    C = p.a.dwd + e * wsz;
+  } else {           // dW_gate / dW_up[e][i][d] = sum_r da / db[r][i] X[t_r][d]
+    M = p.I; N = p.D; m0 = (r / p.nDt) * kBM; n0 = (r % p.nDt) * kBN2;
+    km_init_rows(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr, rbeg,
+                 rend);
+    km_init_rows(b, p.a.x, p.D, 0, n0, p.D, p.P.tok, rbeg, rend);
+    C = (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz;
   }
-  const int m0 = mt * kBM, n0 = nt * kBN2;
-  const int rows = min(kBM, M - m0);
-  TileSrc src;
-  tile_src_init(src, geom::kSplit, A + int64_t(m0) * p.TKP + c0, p.TKP, rows, B + c0, B + c0,
-                p.TKP, n0, n0 + 128, N);
   TileAcc acc;
-  tile_gemm<false>(src, K, acc);
-  epi_store_f32(acc, rows, n0, N, C + int64_t(m0) * N, N);
+  tile_gemm_km<kKR, kKR>(a, b, (rend - rbeg + kBK - 1) / kBK, acc);
+  epi_store_f32(acc, min(kBM, M - m0), n0, N, C + int64_t(m0) * N, N);
 }
 
 // ------------------------------------------------------------------------------------
@@ -295,7 +233,6 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.nDt = int((L.D + kBN2 - 1) / kBN2);
   p.nIt = int((L.I + kBN2 - 1) / kBN2);
   p.nNdh = int(L.nNdh);
-  p.TKP = int64_t(L.TKP);
   p.S = int(L.S);
   p.slot_bytes = int64_t(L.slot_bytes);
   p.slot_ab = int64_t(L.slot_ab);
@@ -307,9 +244,8 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
       cus <= 0)
     return MOK_E_DEVICE;
   const dim3 tiles_grid = dim3(unsigned(cus));  // one 512-thread tile workgroup fits a CU
-  hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_panels, dim3(unsigned(L.TKP / 64), unsigned(L.D / 64)), dim3(256), 0, st,
-                     p);
+  hipLaunchKernelGGL(k_bwd_tok, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
+                     dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dh, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dx, tiles_grid, dim3(kThreads), 0, st, p);

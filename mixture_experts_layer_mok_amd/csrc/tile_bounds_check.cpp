@@ -53,6 +53,19 @@ static int check_km_weights(const char* what, int Kmat, int N, int n0) {
   return bad;
 }
 
+// K-major routed rows: a lane reads 16 bytes at column col0 + km_col(n0, N) of a source
+// row of ld elements; the columns must stay inside [col0, col0 + N) and the row.
+static int check_km_rows(const char* what, int64_t ld, int col0, int N, int n0) {
+  int bad = 0;
+  for (int w = 0; w < mok::geom::kWaves; ++w)
+    for (int l = 0; l < 64; ++l) {
+      const int c = col0 + mok::geom::km_col(w, l, n0, N);
+      if (c < col0 || c + 8 > col0 + N || c + 8 > ld) ++bad;
+    }
+  if (bad) std::printf("%s: %d bad columns (ld=%lld N=%d n0=%d)\n", what, bad, (long long)ld, N, n0);
+  return bad;
+}
+
 static int check_mx(const char* what, int layout, int K, int64_t lda, int64_t as_ld, int rows,
                     int64_t ldb, int64_t bs_ld, int N, int n0, int nb1) {
   const int nk = (K + 127) / 128;
@@ -98,8 +111,7 @@ int main(int argc, char** argv) {
     for (int n0 = 0; n0 < D; n0 += kBN2)
       bad += check("gemm2", mok::geom::kSplit, I, I, I, D, n0, n0 + 128, rows);
     // backward: dH's A = dY rows (K = D), dX's A = [da|db] rows (K = 2I); their B
-    // operands are K-major weights (below); dW (A, B = expert panels of width TKP, K <=
-    // panel width)
+    // operands are K-major weights, and dW reads K-major routed rows (below)
     for (int n0 = 0; n0 < I; n0 += kBN2)
       bad += check("dh", mok::geom::kSplit, D, D, D, I, n0, n0 + 128, rows);
     for (int n0 = 0; n0 < D; n0 += kBN2)
@@ -115,15 +127,18 @@ int main(int argc, char** argv) {
         bad += check_mx("gemm2-mx", mok::geom::kSplit, I, I, hs_ld, rows, I, wds_ld, D, n0,
                         n0 + 128);
     }
-    const int TKP = 4096;
-    for (int K : {64, 1024, 4096})
-      for (int n0 = 0; n0 < I; n0 += kBN2)
-        bad += check("dw", mok::geom::kSplit, K, TKP, TKP, I, n0, n0 + 128, rows);
   }
   // K-major weights: dH reads W_down [D rows, I columns], dX W_gate / W_up [I rows, D
   // columns] (K = 2I: the steps of each matrix stay inside it)
   for (int n0 = 0; n0 < I; n0 += kBN2) bad += check_km_weights("dh-wd", D, I, n0);
   for (int n0 = 0; n0 < D; n0 += kBN2) bad += check_km_weights("dx-wgu", I, D, n0);
+  // dW: dY / X rows (D columns), g h rows (I), da / db halves of [da | db] rows (2I)
+  for (int n0 = 0; n0 < D; n0 += kBN2) bad += check_km_rows("dw-x", D, 0, D, n0);
+  for (int n0 = 0; n0 < I; n0 += kBN2) {
+    bad += check_km_rows("dw-gh", I, 0, I, n0);
+    bad += check_km_rows("dw-da", 2 * I, 0, I, n0);
+    bad += check_km_rows("dw-db", 2 * I, I, I, n0);
+  }
   // K-major stage: each stage row gets its 32 chunks once, logical chunks a permutation
   for (int kk = 0; kk < 64; ++kk) {
     unsigned seen = 0;

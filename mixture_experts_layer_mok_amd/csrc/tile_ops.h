@@ -228,40 +228,31 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 
 // Epilogue of the dH GEMM of the backward (SwiGLU backward and router-weight gradient
 // fused).  The tile covered routed rows row0 + [0, rows) and intermediate columns
-// n0 + [0, 256) (split B layout: B tile row b is column n0 + b) of u = dY W_down.  Per
-// element, with a, b the saved gate/up pre-activations, g the row's gate weight,
-// s = sigmoid(a):  h = a s b;  dh = g u;  da = dh b s (1 + a (1 - s));  db = dh a s.
+// n0 + [0, 256) of u = dY W_down.  Per element, with a, b the saved gate/up
+// pre-activations, g the row's gate weight, s = sigmoid(a):
+//   h = a s b;  dh = g u;  da = dh b s (1 + a (1 - s));  db = dh a s.
 // a, b of tile row r are ab_tile[r * 2I + col] and ab_tile[r * 2I + I + col] (the tile's
-// rows in the ring slot or in the row buffer).
-// Writes da, db row-major into bdab [R, 2I] and, transposed, h / da / db into the
-// per-expert panels (row r of the tile is panel column pc0 + r; columns up to the
-// padded panel end pe are written, zeros past the valid rows), and the partial sum of
-// u h over this tile's columns for each row into dgpart[row][nt] (lanes first, then
-// the four column waves in order: a fixed summation order).
-//
-// The panel stores go through LDS: per 32 x 32 block a wave writes its values as
-// [column][row] (pitch 80 bytes: 16-byte aligned rows, few bank conflicts) into a
-// private 7.5 KB area of the free operand stages, then every lane stores 32
-// consecutive bytes of one panel row (16 rows of one column), instead of 8 bytes per
-// column scattered over 32 panel rows.
-__device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int pc0, int pe,
-                                       int n0, int I, int64_t TKP, const uint16_t* ab_tile,
-                                       const float* gates, const int32_t* perm, uint16_t* bdab,
-                                       uint16_t* ht, uint16_t* dat, uint16_t* dbt, float* dgpart,
-                                       int nt, int nNdh) {
-  constexpr int kPitch = 80, kPanelBytes = 32 * kPitch;
+// rows in the ring slot or in the row buffer).  Writes da, db row-major into bdab
+// [R, 2I], g h row-major into gh [R, I] (the dW_down operand: the gate weight is folded
+// into h there), and the partial sum of u h over this tile's columns for each row into
+// dgpart[row][nt] (lanes first, then the four column waves in order: a fixed summation
+// order).  Loads and stores go through buffer resources sized to the tile's rows, so
+// rows past the tile read zero and their stores are dropped.
+__device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int n0, int I,
+                                       const uint16_t* ab_tile, const float* gates,
+                                       const int32_t* perm, uint16_t* bdab, uint16_t* gh,
+                                       float* dgpart, int nt, int nNdh) {
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wm = w >> 2, wn = w & 3;
+  const int wn = w & 3;
   float* red = reinterpret_cast<float*>(g_lds_a);  // [4][256] row partials per column wave
   float* gate_of = red + 4 * 256;                  // [256] gate weight of each tile row
-  const uint32_t tbuf = lds_addr(g_lds_b) + uint32_t(w) * 3 * kPanelBytes;
-  uint16_t* const panels[3] = {ht, dat, dbt};
   const int64_t twoI = 2 * int64_t(I);
   if (tid < 256) gate_of[tid] = tid < rows ? gates[perm[row0 + tid]] : 0.f;
   const rsrc_t ab_res = row_rsrc(ab_tile, uint32_t(rows) * uint32_t(twoI) * 2u);
   const rsrc_t dab_res = row_rsrc(bdab + int64_t(row0) * twoI, uint32_t(rows) * uint32_t(twoI) * 2u);
+  const rsrc_t gh_res = row_rsrc(gh + int64_t(row0) * I, uint32_t(rows) * uint32_t(I) * 2u);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -276,21 +267,19 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
       if (cb >= I) continue;
       const int col = cb + (lane & 31);
       // a and b of the lane's 16 rows (acc_row(i, 4q + t) = acc_row(i, 0) + 8q + t), all
-      // loads issued before the first use; rows past the tile lie outside the resource
-      // and read zero
+      // loads issued before the first use
+      const uint32_t row_i = uint32_t(acc_row(tid, i, 0));
+      const uint32_t voff = (row_i * uint32_t(twoI) + col) * 2u;
+      const uint32_t goff = (row_i * uint32_t(I) + col) * 2u;
       uint16_t av[16], bv[16];
-      const uint32_t voff = (uint32_t(acc_row(tid, i, 0)) * uint32_t(twoI) + col) * 2u;
-      {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t so = uint32_t(8 * (v >> 2) + (v & 3)) * uint32_t(twoI) * 2u;
-          av[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so, 0);
-          bv[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so + uint32_t(I) * 2u, 0);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t so = uint32_t(8 * (v >> 2) + (v & 3)) * uint32_t(twoI) * 2u;
+        av[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so, 0);
+        bv[v] = __builtin_amdgcn_raw_buffer_load_b16(ab_res, voff, so + uint32_t(I) * 2u, 0);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t hv[2] = {0u, 0u}, dav[2] = {0u, 0u}, dbv[2] = {0u, 0u};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int rr = acc_row(tid, i, 4 * q + t);  // four consecutive rows
@@ -306,44 +295,15 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
           const float dh = g * u;
           const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
           const float db = dh * sl;
-          const uint16_t dab = ok ? f32_to_bf16(da) : uint16_t(0);
-          const uint16_t dbb = ok ? f32_to_bf16(db) : uint16_t(0);
-          const uint16_t hb = ok ? f32_to_bf16(h) : uint16_t(0);
-          {  // rows past the tile lie outside the resource: the stores are dropped
-            const uint32_t so = uint32_t(8 * q + t) * uint32_t(twoI) * 2u;
-            __builtin_amdgcn_raw_buffer_store_b16(dab, dab_res, voff, so, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(dbb, dab_res, voff, so + uint32_t(I) * 2u, 0);
-          }
-          hv[t >> 1] |= uint32_t(hb) << (16 * (t & 1));
-          dav[t >> 1] |= uint32_t(dab) << (16 * (t & 1));
-          dbv[t >> 1] |= uint32_t(dbb) << (16 * (t & 1));
-        }
-        // rows 8 q + 4 (lane / 32) .. +3 of column lane % 32 of this block
-        const uint32_t wa = tbuf + uint32_t(lane & 31) * kPitch + 16 * q + 8 * (lane >> 5);
-        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-        typedef __attribute__((address_space(3))) v2u lds_v2u;
-        *reinterpret_cast<lds_v2u*>(uintptr_t(wa)) = v2u{hv[0], hv[1]};
-        *reinterpret_cast<lds_v2u*>(uintptr_t(wa + kPanelBytes)) = v2u{dav[0], dav[1]};
-        *reinterpret_cast<lds_v2u*>(uintptr_t(wa + 2 * kPanelBytes)) = v2u{dbv[0], dbv[1]};
-      }
-      // the wave's LDS writes are visible to its own later reads once they completed
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      {
-        const int c = lane >> 1, hh = lane & 1;  // column, half (16 rows)
-        const int pcs = pc0 + wm * 128 + i * 32 + 16 * hh;
-        const uint32_t ra = tbuf + uint32_t(c) * kPitch + 32 * hh;
-        if (pcs < pe) {
-#pragma unroll
-          for (int pnl = 0; pnl < 3; ++pnl) {
-            const v4u lo = *reinterpret_cast<lds_cv4u*>(uintptr_t(ra + pnl * kPanelBytes));
-            const v4u hi = *reinterpret_cast<lds_cv4u*>(uintptr_t(ra + pnl * kPanelBytes + 16));
-            v4u* dst = reinterpret_cast<v4u*>(panels[pnl] + int64_t(cb + c) * TKP + pcs);
-            dst[0] = lo;
-            dst[1] = hi;
-          }
+          const uint32_t r8 = uint32_t(8 * q + t);
+          const uint32_t so = r8 * uint32_t(twoI) * 2u;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(da), dab_res, voff, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(db), dab_res, voff,
+                                                so + uint32_t(I) * 2u, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * h), gh_res, goff,
+                                                r8 * uint32_t(I) * 2u, 0);
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
