@@ -1,7 +1,7 @@
 """Benchmark of the MoE layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--M 2048] [--S 4]
-                    [--comm-cus 32] [--unfused] [--fwd-only] [--no-cpu-baseline]
+                    [--comm-cus C] [--unfused] [--fwd-only] [--no-cpu-baseline]
     python bench.py --sweep            # minibatch x comm-CU sweep of the forward, JSON lines
     python bench.py --copy-calibration # one plain device copy of known size (counter scale)
 
@@ -203,8 +203,8 @@ def sweep(args):
     from mixture_experts_layer_mok_amd.tuning import layer_two_wave_min_rows
     cus = L.mok_device_cus()
     mx = base.precision == L.MOK_PREC_MXFP8
-    comms = (32, 64, 96, 128) if mx else (16, 32, 48, 64)
-    Ms = (1024, 2048, 4096, 8192) if mx else (512, 1024, 1536, 2048, 2560, 3072, 3584, 4096,
+    comms = (24, 32, 40, 48, 64) if mx else (12, 16, 20, 24, 32, 48)
+    Ms = (1024, 2048, 4096) if mx else (512, 1024, 1536, 2048, 2560, 3072, 3584, 4096,
                                               6144, 8192)
     for comm in comms:
         for M in Ms:
@@ -311,10 +311,11 @@ def main():
         bwd_ms = float(np.mean(r["bwd_ms"]))
         out["bwd_ms"] = stats(r["bwd_ms"])
         out["bwd_tflops"] = round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2)
-    # the committed counters were taken on the default command (config 5, fused, M=2048,
-    # S=8, 32 comm CUs, forward saving a and b for the backward)
+    # the committed counters were taken on the default command (config 5 as defined, fused,
+    # forward saving a and b for the backward)
+    c5 = gen.CONFIGS[5]
     traffic = read_traffic() if (not args.unfused and with_bwd and args.config == 5
-                                 and cfg.M == 2048 and cfg.S == 8 and cfg.comm_cus == 32) else None
+                                 and (cfg.M, cfg.S, cfg.comm_cus) == (c5.M, c5.S, c5.comm_cus)) else None
     out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else
                        "forward (unfused launches)", "achieved": round(achieved, 2),
                        "peak": peak, "unit": "TFLOP/s",

@@ -190,35 +190,14 @@ __global__ __launch_bounds__(256) void k_bwd_dg(BwdParams p) {
   }
 }
 
-// dX[t] = sum over local slots j (ascending) of dxbuf[t*k + j], fp32, rounded once.
+// dX[t] = sum over local slots j (ascending) of dxbuf[t*k + j], fp32, rounded once
+// (zero for a token without local slots).
 __global__ __launch_bounds__(256) void k_bwd_dxsum(BwdParams p) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
-  const int lane = threadIdx.x & 63;
-  for (int t = gw; t < p.T; t += nw) {
-    const int64_t q0 = int64_t(t) * p.k;
-    const uint64_t has = __ballot(lane < p.k && p.P.pos[q0 + (lane < p.k ? lane : 0)] >= 0);
-    v4u* out = reinterpret_cast<v4u*>(p.a.dx + int64_t(t) * p.D);
-    for (int c = lane; c < (p.D >> 3); c += 64) {
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      uint64_t m = has;
-      while (m) {
-        const int j = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const v4u v = reinterpret_cast<const v4u*>(p.P.dxbuf + (q0 + j) * p.D)[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = __fadd_rn(acc[2 * e], bf16_to_f32(uint16_t(w[e] & 0xFFFF)));
-          acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], bf16_to_f32(uint16_t(w[e] >> 16)));
-        }
-      }
-      out[c] = v4u{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    }
-  }
+  for (int t = gw; t < p.T; t += nw)
+    wave_pair_sum<kCpolPlain>(p.a.dx + int64_t(t) * p.D, p.P.dxbuf, int64_t(t) * p.k, p.D,
+                              p.P.pos, nullptr, p.k);
 }
 
 // ------------------------------------------------------------------------------------

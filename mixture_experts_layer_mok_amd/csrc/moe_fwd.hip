@@ -80,89 +80,13 @@ __device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uin
 // ------------------------------------------------------------------------------------
 // combine
 // ------------------------------------------------------------------------------------
-// y[t] = sum_j gate_j * o[t*k+j] over the slots j with a local row, in ascending j per
-// element (acc = 0, then acc += gate_j * o_j, each step rounded to fp32).  One wave per
-// token; lane l owns the 16-byte chunks l, l + 64, ... of the row.  A token with a single
-// local slot (the usual case of an even expert share) is scaled in passes of kRowBatch
-// chunks per lane; otherwise the wave loads kCombChunks chunks of two slots at a time.
-// Either way 16 loads per lane are in flight.
-constexpr int kCombChunks = 8;
-
-__device__ __forceinline__ void acc_gated(float (&acc)[8], v4u v, float g) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc[2 * e] = __fadd_rn(acc[2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
-    acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
-  }
-}
-__device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
-  return v4u{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-}
-
+// y[t] = sum_j gate_j * o[t*k+j] over the slots j with a local row, in ascending j
+// (wave_pair_sum).
 template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
-  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
-  const uint32_t lane = threadIdx.x & 63;
-  const int D = p.D, k = p.k;
-  const uint32_t bytes = uint32_t(D) * 2;
-  const int64_t q0 = int64_t(t) * k;
-  const int32_t my_pos = int(lane) < k ? p.P.pos[q0 + lane] : -1;
-  const float my_g = int(lane) < k ? p.a.gates[q0 + lane] : 0.f;
-  const uint64_t has = __ballot(my_pos >= 0);
-  const rsrc_t ry = row_rsrc(p.a.y + int64_t(t) * D, bytes);
-  if (__popcll(has) == 1) {
-    const int j = __ffsll((unsigned long long)has) - 1;
-    const float g = __shfl(my_g, j);
-    const rsrc_t ro = row_rsrc(p.P.obuf + (q0 + j) * D, bytes);
-    for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kRowBatch) {
-      v4u v[kRowBatch];
-#pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) v[u] = buf_ld16<kPol>(ro, b0 + (lane + 64 * u) * 16);
-#pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        acc_gated(acc, v[u], g);
-        buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * u) * 16, pack_acc(acc));
-      }
-    }
-    return;
-  }
-  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kCombChunks) {
-    float acc[kCombChunks][8];
-#pragma unroll
-    for (int c = 0; c < kCombChunks; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-    uint64_t m = has;
-    while (m) {
-      const int j0 = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int j1 = m ? __ffsll((unsigned long long)m) - 1 : -1;
-      if (m) m &= m - 1;
-      const rsrc_t r0 = row_rsrc(p.P.obuf + (q0 + j0) * D, bytes);
-      // a missing second slot gets a zero-length range: its loads read nothing
-      const rsrc_t r1 = row_rsrc(p.P.obuf + (q0 + (j1 >= 0 ? j1 : j0)) * D, j1 >= 0 ? bytes : 0u);
-      v4u v0[kCombChunks], v1[kCombChunks];
-#pragma unroll
-      for (int c = 0; c < kCombChunks; ++c) {
-        v0[c] = buf_ld16<kPol>(r0, b0 + (lane + 64 * c) * 16);
-        v1[c] = buf_ld16<kPol>(r1, b0 + (lane + 64 * c) * 16);
-      }
-      const float g0 = __shfl(my_g, j0);
-#pragma unroll
-      for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v0[c], g0);
-      if (j1 >= 0) {
-        const float g1 = __shfl(my_g, j1);
-#pragma unroll
-        for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v1[c], g1);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kCombChunks; ++c)
-      buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
-  }
+  wave_pair_sum<kCoherent ? kCpolDev : kCpolPlain>(p.a.y + int64_t(t) * p.D, p.P.obuf,
+                                                   int64_t(t) * p.k, p.D, p.P.pos, p.a.gates,
+                                                   p.k);
 }
 
 // ------------------------------------------------------------------------------------

@@ -55,6 +55,93 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
     buf_st16<kCpolPlain>(rd, b, v4u{0u, 0u, 0u, 0u});
 }
 
+// dst = sum_j g_j * rows[q0 + j] over the slots j < k with pos[q0 + j] >= 0, per element
+// in ascending j (acc = 0, then acc += g_j * row_j, each step rounded to fp32), rounded
+// once to bf16; g_j = gates[q0 + j], or 1 without gates.  rows holds pair-indexed rows of
+// D bf16.  One wave per destination row; lane l owns the 16-byte chunks l, l + 64, ....
+// With a single slot (the usual case of an even expert share) the row is processed in
+// passes of kRowBatch chunks per lane; otherwise the wave loads kCombChunks chunks of
+// two slots at a time: either way 16 loads per lane are in flight.  Source loads use the
+// cache policy kPol (device scope for rows written by other workgroups of a running
+// kernel); every access goes through a row-length buffer resource.
+constexpr int kCombChunks = 8;
+
+__device__ __forceinline__ void acc_gated(float (&acc)[8], v4u v, float g) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] = __fadd_rn(acc[2 * e], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] & 0xFFFF))));
+    acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __fmul_rn(g, bf16_to_f32(uint16_t(w[e] >> 16))));
+  }
+}
+__device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
+  return v4u{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+}
+
+template <int kPol>
+__device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* rows, int64_t q0,
+                                              int D, const int32_t* pos, const float* gates,
+                                              int k) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t bytes = uint32_t(D) * 2;
+  const int32_t my_pos = int(lane) < k ? pos[q0 + lane] : -1;
+  const float my_g = int(lane) < k ? (gates ? gates[q0 + lane] : 1.0f) : 0.f;
+  const uint64_t has = __ballot(my_pos >= 0);
+  const rsrc_t ry = row_rsrc(dst, bytes);
+  if (__popcll(has) == 1) {
+    const int j = __ffsll((unsigned long long)has) - 1;
+    const float g = __shfl(my_g, j);
+    const rsrc_t ro = row_rsrc(rows + (q0 + j) * D, bytes);
+    for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kRowBatch) {
+      v4u v[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) v[u] = buf_ld16<kPol>(ro, b0 + (lane + 64 * u) * 16);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        acc_gated(acc, v[u], g);
+        buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * u) * 16, pack_acc(acc));
+      }
+    }
+    return;
+  }
+  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kCombChunks) {
+    float acc[kCombChunks][8];
+#pragma unroll
+    for (int c = 0; c < kCombChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+    uint64_t m = has;
+    while (m) {
+      const int j0 = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int j1 = m ? __ffsll((unsigned long long)m) - 1 : -1;
+      if (m) m &= m - 1;
+      const rsrc_t r0 = row_rsrc(rows + (q0 + j0) * D, bytes);
+      // a missing second slot gets a zero-length range: its loads read nothing
+      const rsrc_t r1 = row_rsrc(rows + (q0 + (j1 >= 0 ? j1 : j0)) * D, j1 >= 0 ? bytes : 0u);
+      v4u v0[kCombChunks], v1[kCombChunks];
+#pragma unroll
+      for (int c = 0; c < kCombChunks; ++c) {
+        v0[c] = buf_ld16<kPol>(r0, b0 + (lane + 64 * c) * 16);
+        v1[c] = buf_ld16<kPol>(r1, b0 + (lane + 64 * c) * 16);
+      }
+      const float g0 = __shfl(my_g, j0);
+#pragma unroll
+      for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v0[c], g0);
+      if (j1 >= 0) {
+        const float g1 = __shfl(my_g, j1);
+#pragma unroll
+        for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v1[c], g1);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kCombChunks; ++c)
+      buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // GEMM tiles
 // ------------------------------------------------------------------------------------

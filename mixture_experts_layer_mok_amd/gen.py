@@ -62,16 +62,17 @@ CONFIGS = {
     1: LayerConfig("c1-tiny-fwd", T=128, D=128, I=64, E=4, k=2, M=32, S=2, comm_cus=8),
     2: LayerConfig("c2-small-fwd-bf16", T=4096, D=2048, I=1024, E=16, k=4, M=1024, S=2,
                    comm_cus=32),
+    # comm_cus: the best of the minibatch x comm-CU sweeps of the fused forward
     3: LayerConfig("c3-share-fwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8, M=2048,
-                   S=4, comm_cus=32),
-    # the skewed load puts ~86k rows on this GPU: the data movers need twice the CUs
-    # (minibatch x comm-CU sweep of the MXFP8 forward)
+                   S=4, comm_cus=20),
+    # the skewed load puts ~86k rows on this GPU, which the data movers quantise and
+    # combine (about five slots per token): they need more CUs than the even share
     4: LayerConfig("c4-share-zipf-fwd-mxfp8", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
-                   M=2048, S=4, comm_cus=64, precision=PREC_MXFP8, zipf_s=1.2),
+                   M=2048, S=4, comm_cus=32, precision=PREC_MXFP8, zipf_s=1.2),
     # eight ring slots (about 61 MB each) hold every minibatch of this share, so the
     # backward finds a and b of all of them in the ring and replays nothing
     5: LayerConfig("c5-share-fwd-bwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
-                   M=2048, S=8, comm_cus=32),
+                   M=2048, S=8, comm_cus=20),
 }
 
 
