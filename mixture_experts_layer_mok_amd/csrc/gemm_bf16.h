@@ -301,11 +301,16 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //   kKC  K-contiguous rows (the tile above; rows may be gathered);
 //   kKW  K-major weight matrix [K rows][ld]: tile column n is column n of every row;
 //        K rows past ksplit come from a second matrix (dX stacks W_gate over W_up);
-//   kKR  K-major routed rows: K index q is routed row rbeg + q, whose data is row
-//        tok[r] of a token matrix (gathered; tok = the token of each routed row) or row
-//        r of a row matrix; rows at or past rend read zero (bit 31 of the offset,
-//        against a 2 GB resource).
-enum KmKind { kKC = 0, kKW = 1, kKR = 2 };
+//   kKR  K-major routed rows of a row matrix: K index q is routed row r = rbeg + q at
+//        byte r * row bytes;
+//   kKG  K-major routed rows gathered: row r starts at byte rowb[r] of the resource.
+//        The offsets are staged in LDS per window of kRowTabLds rows (loaded at the
+//        start and every kRowTabLds rows): reading them from memory in the load loop
+//        would share the in-order vector-memory counter with the operand loads, so that
+//        every wait for the one also waits for the other.
+// For kKR and kKG, rows at or past rend read zero (bit 31 of the offset, against a 2 GB
+// resource).
+enum KmKind { kKC = 0, kKW = 1, kKR = 2, kKG = 3 };
 constexpr uint32_t kKmOutOfRange = 0x80000000u;
 constexpr int kKmRowBytes = 512;  // one staged K row: 256 bf16
 
@@ -314,9 +319,9 @@ struct KmOp {
   uint32_t off[geom::kLoads];  // kKC / kKW: per-lane byte offsets; kKR: column bytes
   uint32_t ld2;                // kKW: bytes per K row; kKR: bytes per source row
   int ksplit;                  // kKW
-  const int32_t* tok;          // kKR: source row of each routed row (null: row r itself)
-  int rbeg, rend;              // kKR
-  int32_t nxt[geom::kLoads];   // kKR with tok: source rows of the next step to issue
+  const uint32_t* rowb;        // kKG: byte offset of each routed row
+  int rbeg, rend;              // kKR, kKG
+  uint32_t nxt[geom::kLoads];  // kKG: offsets of the rows of the next step to issue
 };
 
 __device__ __forceinline__ i32x4_t make_rsrc_2g_km(const void* base) {
@@ -363,27 +368,45 @@ __device__ __forceinline__ void km_init_weights(KmOp& o, const uint16_t* W0, con
     o.off[p] = uint32_t((int64_t(geom::km_row(p, w, l)) * ld + geom::km_col(w, l, n0, N)) * 2);
 }
 
-// K-major routed rows [rbeg, rend): source row tok[r] (tok != null) or r of M, ld
-// elements per row; tile columns n0 .. n0+255 of N (col0 added to every column).
-__device__ __forceinline__ void km_init_rows(KmOp& o, const uint16_t* M, int64_t ld, int col0,
-                                             int n0, int N, const int32_t* tok, int rbeg,
+constexpr int kRowTabLds = 4096;  // routed-row offsets per LDS window (64 K steps)
+static __shared__ uint32_t g_lds_rowtab[kRowTabLds];
+
+// Window of row offsets [rbeg + q0, rbeg + q0 + kRowTabLds) into LDS (zero past rend).
+// Every thread of the workgroup calls it; it ends with a barrier.
+__device__ __forceinline__ void km_load_rowtab(const KmOp& o, int q0) {
+  for (int i = threadIdx.x; i < kRowTabLds; i += kThreads) {
+    const int r = o.rbeg + q0 + i;
+    g_lds_rowtab[i] = r < o.rend ? o.rowb[r] : 0u;
+  }
+  __syncthreads();
+}
+
+// K-major routed rows [rbeg, rend) of base (kKR: row r at r * ld * 2; kKG: at rowb[r]);
+// tile columns n0 .. n0+255 of N (col0 added to every column).  For kKG every thread of
+// the workgroup must call this (it stages the first window of offsets).
+template <int KIND>
+__device__ __forceinline__ void km_init_rows(KmOp& o, const void* base, int64_t ld, int col0,
+                                             int n0, int N, const uint32_t* rowb, int rbeg,
                                              int rend) {
+  static_assert(KIND == kKR || KIND == kKG, "routed-row operand");
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  o.r0 = make_rsrc_2g_km(M);
+  o.r0 = make_rsrc_2g_km(base);
   o.ld2 = uint32_t(ld * 2);
-  o.tok = tok;
+  o.rowb = rowb;
   o.rbeg = rbeg;
   o.rend = rend;
 #pragma unroll
-  for (int p = 0; p < geom::kLoads; ++p) {
+  for (int p = 0; p < geom::kLoads; ++p)
     o.off[p] = uint32_t((col0 + geom::km_col(w, l, n0, N)) * 2);
-    const int r = rbeg + geom::km_row(p, w, l);
-    o.nxt[p] = tok && rend > rbeg ? tok[r < rend ? r : rend - 1] : 0;
+  if (KIND == kKG) {
+    km_load_rowtab(o, 0);
+#pragma unroll
+    for (int p = 0; p < geom::kLoads; ++p) o.nxt[p] = g_lds_rowtab[geom::km_row(p, w, l)];
   }
 }
 
 template <int KIND, int STAGE>
-__device__ __forceinline__ void km_issue(const KmOp& o, int k0, v4u* lds) {
+__device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (KIND == kKC) {
 #pragma unroll
@@ -398,30 +421,28 @@ __device__ __forceinline__ void km_issue(const KmOp& o, int k0, v4u* lds) {
                    lds + STAGE * kStageChunks + (p * 8 + w) * 64);
   } else {
     const int l = threadIdx.x & 63;
+    uint32_t voff[geom::kLoads];
 #pragma unroll
     for (int p = 0; p < geom::kLoads; ++p) {
       const int r = o.rbeg + k0 + geom::km_row(p, w, l);
-      // source row below 2^24 and row bytes below 2^24 (checked on the host)
-      const uint32_t src = o.tok ? uint32_t(o.nxt[p]) : uint32_t(r);
-      const uint32_t voff = r < o.rend ? __umul24(src, o.ld2) + o.off[p] : kKmOutOfRange;
-      dma16<false>(o.r0, voff, 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+      // row index and row bytes below 2^24 (checked on the host); kKG offsets were read
+      // from LDS at the previous issue, so no wait holds up these loads
+      const uint32_t rb = KIND == kKG ? o.nxt[p] : __umul24(uint32_t(r), o.ld2);
+      voff[p] = r < o.rend ? rb + o.off[p] : kKmOutOfRange;
     }
-  }
-}
-
-// kKR with tok: the source rows of step k0 + kBK, loaded one step ahead of their use.
-// Called after every load of step k0 has been issued: nothing reads them before the
-// next step's wait, and a wait for them would also wait for loads issued before them.
-template <int KIND>
-__device__ __forceinline__ void km_prefetch(KmOp& o, int k0) {
-  if (KIND != kKR) return;
-  if (!o.tok) return;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
 #pragma unroll
-  for (int p = 0; p < geom::kLoads; ++p) {
-    const int r = o.rbeg + k0 + kBK + geom::km_row(p, w, l);
-    o.nxt[p] = o.tok[r < o.rend ? r : o.rend - 1];
+    for (int p = 0; p < geom::kLoads; ++p)
+      dma16<false>(o.r0, voff[p], 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+    if (KIND == kKG) {
+      // offsets of the next step; a next step that starts a new window reloads it (every
+      // wave read its offsets from the old one at the previous issue, before the barrier
+      // that preceded this one)
+      const int kn = k0 + kBK;
+      if (kn % kRowTabLds == 0) km_load_rowtab(o, kn);
+#pragma unroll
+      for (int p = 0; p < geom::kLoads; ++p)
+        o.nxt[p] = g_lds_rowtab[(kn + geom::km_row(p, w, l)) % kRowTabLds];
+    }
   }
 }
 
@@ -489,8 +510,6 @@ template <int AK, int BK, int S>
 __device__ __forceinline__ void km_issue_step(KmOp& a, KmOp& b, int k0) {
   km_issue<AK, S>(a, k0, g_lds_a);
   km_issue<BK, S>(b, k0, g_lds_b);
-  km_prefetch<AK>(a, k0);
-  km_prefetch<BK>(b, k0);
 }
 
 // One K step kb in stage S, as tile_step.
@@ -522,7 +541,8 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K loop of nk steps over operands a (kind AK: kKC or kKR) and b (kind BK: kKW or kKR).
+// K loop of nk steps over operands a (kind AK: kKC, kKR or kKG) and b (kind BK: kKW, kKR
+// or kKG; at most one kKG operand: they share the LDS offset table).
 // C = A B^T as for tile_gemm, with A's tile row m / B's tile row n read as column m / n
 // of a K-major operand.  Ends with a barrier.
 template <int AK, int BK>

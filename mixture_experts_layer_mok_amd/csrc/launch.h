@@ -34,7 +34,8 @@ struct Ptrs {
   uint16_t* dxbuf;    // [T*k, D] per-pair dX contributions (pair-indexed)
   float* dgpart;      // [T*k, nNdh] router-weight gradient partials per dH n-tile
   uint16_t* gh;       // [T*k, I] gate weight times h per routed row (dW_down operand)
-  int32_t* tok;       // [T*k] token of each routed row
+  uint32_t* dyb;      // [T*k] byte offset of each routed row's dY row in dy
+  uint32_t* xb;       // [T*k] byte offset of each routed row's X row (ring or x)
 };
 
 inline Ptrs make_ptrs(const Layout& L, void* ws) {
@@ -66,7 +67,8 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.dxbuf = u16(L.off_dxbuf);
   P.dgpart = L.save ? reinterpret_cast<float*>(b + L.off_dgpart) : nullptr;
   P.gh = u16(L.off_gh);
-  P.tok = L.save ? reinterpret_cast<int32_t*>(b + L.off_tok) : nullptr;
+  P.dyb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_dyb) : nullptr;
+  P.xb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_xb) : nullptr;
   return P;
 }
 

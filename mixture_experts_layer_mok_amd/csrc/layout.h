@@ -63,7 +63,7 @@ struct Layout {
   size_t off_wsg, off_wsu, off_wsd;  // repacked weight scales (MXFP8, when needed)
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
-  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_tok;
+  size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
   size_t total;
 };
 
@@ -159,7 +159,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   // backward regions (present when the forward saves for backward): row buffers indexed
   // by routed row (at most T*k rows).
   L->nNdh = (I + kBN2 - 1) / kBN2;
-  L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = L->off_gh = L->off_tok = 0;
+  L->off_bab = L->off_bdab = L->off_dxbuf = L->off_dgpart = L->off_gh = L->off_dyb = L->off_xb = 0;
   if (L->save) {
     // the backward GEMMs read weights with 32-bit offsets, and X, dY, [da | db] and g h
     // rows as K-major routed rows, whose offsets stay below 2^31 bytes (bit 31 marks a
@@ -173,7 +173,8 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_dxbuf = o; o = align_up(o + TK * D * 2, A);
     L->off_dgpart = o; o = align_up(o + TK * L->nNdh * 4, A);
     L->off_gh = o; o = align_up(o + TK * I * 2, A);
-    L->off_tok = o; o = align_up(o + TK * 4, A);
+    L->off_dyb = o; o = align_up(o + TK * 4, A);
+    L->off_xb = o; o = align_up(o + TK * 4, A);
   }
   L->total = o;
   return MOK_OK;

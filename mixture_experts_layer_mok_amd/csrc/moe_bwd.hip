@@ -33,6 +33,8 @@ struct BwdParams {
   int T, D, I, k, nl, mt_max, nDt, nIt, nNdh, n_mb_max, S;
   int64_t slot_bytes, slot_ab;
   int ab_saved;  // 1: the forward wrote a, b of every row (unfused); 0: ring only (fused)
+  int ring_2g;   // 1: ring offsets stay below 2^31 bytes
+  int64_t slot_x;
   int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
 };
 
@@ -46,12 +48,36 @@ __device__ __forceinline__ const uint16_t* ab_rows(const BwdParams& p, const int
   return p.P.bab + int64_t(e.x) * 2 * p.I;
 }
 
-// Token of every routed row, tok[r] = perm[r] / k: the dW tiles gather X and dY rows by
-// it without a division in their load loop.
-__global__ __launch_bounds__(256) void k_bwd_tok(BwdParams p) {
+// After a fused forward with every minibatch still in its ring slot, the slots hold the
+// X rows of all routed rows, in routed order per minibatch.
+__device__ __forceinline__ bool x_in_ring(const BwdParams& p) {
+  return !p.ab_saved && p.ring_2g && int(p.P.hdr[kHdrNmb]) <= p.S;
+}
+
+// Byte offsets of each routed row's dY and X data, for the dW tiles' gathered loads (no
+// division or search in their load loop): dY row perm[r] / k of dy; X row from the ring
+// slot that still holds it when every minibatch is resident after a fused forward
+// (contiguous rows per minibatch), else row perm[r] / k of x.
+__global__ __launch_bounds__(256) void k_bwd_rows(BwdParams p) {
   const int R = int(p.P.hdr[kHdrR]);
-  for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256)
-    p.P.tok[r] = p.P.perm[r] / p.k;
+  const int n_mb = int(p.P.hdr[kHdrNmb]);
+  const bool x_ring = x_in_ring(p);
+  for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256) {
+    const uint32_t tb = uint32_t(p.P.perm[r] / p.k) * uint32_t(p.D) * 2u;
+    p.P.dyb[r] = tb;
+    if (x_ring) {
+      int lo = 0, hi = n_mb - 1;  // minibatch of row r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.P.mb_start[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      p.P.xb[r] = uint32_t((lo % p.S) * p.slot_bytes + p.slot_x) +
+                  uint32_t(r - p.P.mb_start[lo]) * uint32_t(p.D) * 2u;
+    } else {
+      p.P.xb[r] = tb;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -145,34 +171,40 @@ __global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
 
 // dW GEMMs, K over the expert's routed rows in ascending order, both operands read
 // K-major as stored: per expert, dW_down tiles (D x I: A = dY rows gathered by perm,
-// B = g h rows), then dW_gate and dW_up tiles (I x D: A = da / db rows, B = X rows
-// gathered by token).  Rows past the expert's last read zero; an expert without rows
+// B = g h rows), then dW_gate and dW_up tiles (I x D: A = da / db rows, B = X rows, from
+// the ring when it holds them all).  Rows past the expert's last read zero; an expert without rows
 // gets zero tiles.  One workgroup owns each tile: no atomics.
+template <int AK, int BK>
+__device__ __forceinline__ void dw_tile(KmOp& a, KmOp& b, int nk, int rows, int n0, int N,
+                                        float* C) {
+  TileAcc acc;
+  tile_gemm_km<AK, BK>(a, b, nk, acc);
+  epi_store_f32(acc, rows, n0, N, C, N);
+}
+
 __global__ __launch_bounds__(512) void k_bwd_dw(BwdParams p) {
   const int per = p.nDt * p.nIt;
   const int e = blockIdx.x / (3 * per);
   const int q = blockIdx.x % (3 * per);
   const int which = q / per, r = q % per;
   const int rbeg = p.P.offsets[e], rend = rbeg + p.P.counts[e];
+  const int nk = (rend - rbeg + kBK - 1) / kBK;
   const int64_t wsz = int64_t(p.I) * p.D;
   KmOp a, b;
-  float* C;
-  int M, N, m0, n0;
   if (which == 0) {  // dW_down[e][d][i] = sum_r dY[t_r][d] (g h)[r][i]
-    M = p.D; N = p.I; m0 = (r / p.nIt) * kBM; n0 = (r % p.nIt) * kBN2;
-    km_init_rows(a, p.a.dy, p.D, 0, m0, p.D, p.P.tok, rbeg, rend);
-    km_init_rows(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
-    C = p.a.dwd + e * wsz;
+    const int m0 = (r / p.nIt) * kBM, n0 = (r % p.nIt) * kBN2;
+    km_init_rows<kKG>(a, p.a.dy, p.D, 0, m0, p.D, p.P.dyb, rbeg, rend);
+    km_init_rows<kKR>(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
+    dw_tile<kKG, kKR>(a, b, nk, min(kBM, p.D - m0), n0, p.I, p.a.dwd + e * wsz + int64_t(m0) * p.I);
   } else {           // dW_gate / dW_up[e][i][d] = sum_r da / db[r][i] X[t_r][d]
-    M = p.I; N = p.D; m0 = (r / p.nDt) * kBM; n0 = (r % p.nDt) * kBN2;
-    km_init_rows(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr, rbeg,
-                 rend);
-    km_init_rows(b, p.a.x, p.D, 0, n0, p.D, p.P.tok, rbeg, rend);
-    C = (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz;
+    const int m0 = (r / p.nDt) * kBM, n0 = (r % p.nDt) * kBN2;
+    km_init_rows<kKR>(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr,
+                      rbeg, rend);
+    km_init_rows<kKG>(b, x_in_ring(p) ? static_cast<const void*>(p.P.ring) : p.a.x, p.D, 0, n0,
+                      p.D, p.P.xb, rbeg, rend);
+    dw_tile<kKR, kKG>(a, b, nk, min(kBM, p.I - m0), n0, p.D,
+                      (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz + int64_t(m0) * p.D);
   }
-  TileAcc acc;
-  tile_gemm_km<kKR, kKR>(a, b, (rend - rbeg + kBK - 1) / kBK, acc);
-  epi_store_f32(acc, min(kBM, M - m0), n0, N, C + int64_t(m0) * N, N);
 }
 
 // ------------------------------------------------------------------------------------
@@ -216,6 +248,8 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.slot_bytes = int64_t(L.slot_bytes);
   p.slot_ab = int64_t(L.slot_ab);
   p.ab_saved = L.unfused ? 1 : 0;
+  p.slot_x = int64_t(L.slot_x);
+  p.ring_2g = int64_t(L.S) * int64_t(L.slot_bytes) < (int64_t(1) << 31) ? 1 : 0;
   p.per_mt = int(L.nN1 + L.nN2);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -223,7 +257,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
       cus <= 0)
     return MOK_E_DEVICE;
   const dim3 tiles_grid = dim3(unsigned(cus));  // one 512-thread tile workgroup fits a CU
-  hipLaunchKernelGGL(k_bwd_tok, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
+  hipLaunchKernelGGL(k_bwd_rows, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
                      dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dh, tiles_grid, dim3(kThreads), 0, st, p);

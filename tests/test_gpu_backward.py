@@ -82,6 +82,23 @@ def test_backward_edge_cases():
         assert torch.count_nonzero(t).item() == 0, name
 
 
+@pytest.mark.parametrize("S", [2, 8], ids=["replay", "all-resident"])
+def test_backward_expert_longer_than_row_table(S):
+    """Expert 1 holds 9000 routed rows: the dW tiles run past two windows of the row
+    offset table (4096 rows each); with 8 ring slots every minibatch stays resident and
+    the X rows come from the ring, with 2 the early ones are replayed and X is gathered."""
+    cfg = gen.small_config("long", T=9000, D=128, I=128, E=4, k=2, M=4096, S=S, comm_cus=8)
+    d = gen.make_inputs(cfg, seed=21, with_dy=True)
+    ids = d["ids"].copy()
+    ids[:, 0] = 1
+    ids[:, 1] = np.where(ids[:, 1] == 1, 2, ids[:, 1])
+    dev = DevInputs(d, ids=ids)
+    _, g, layer = run_fwd_bwd(cfg, dev)
+    assert layer.status() == 0
+    assert int(layer.tables()["counts"][1]) == 9000
+    _compare(cfg, d, ids, g, f"long-expert S={S}")
+
+
 def test_backward_config5_full_and_deterministic():
     cfg = gen.CONFIGS[5]
     say("[c5] generating")
