@@ -22,6 +22,7 @@
 // minibatches whose slot was recycled, mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for
 // the backward writes a, b of every row, and nothing is replayed.
 #include <algorithm>
+#include <mutex>
 
 #include "tile_ops.h"
 
@@ -235,6 +236,36 @@ __global__ __launch_bounds__(256) void k_bwd_dxsum(BwdParams p) {
 // ------------------------------------------------------------------------------------
 // host
 // ------------------------------------------------------------------------------------
+// A side stream per device, with a fork and a join event: the dX row sum and the router-
+// weight gradient run on it beside the dW GEMMs.  They need no LDS and few registers, so
+// their workgroups fit next to a dW workgroup on a CU, and they move memory while dW
+// keeps the matrix cores busy.  Created on first use at the default priority and kept
+// until the process ends.  The enqueue sequence holds a lock, so that calls from several
+// host threads do not interleave their uses of the two events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+static SideStream g_side[kMaxDevices];
+static std::mutex g_side_mu;
+
+static SideStream* side_stream_locked(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.failed) return nullptr;
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      return nullptr;
+    }
+  }
+  return &ss;
+}
+
 mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, hipStream_t st) {
   BwdParams p;
   p.P = P;
@@ -262,11 +293,26 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dh, tiles_grid, dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(k_bwd_dx, tiles_grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dw, dim3(unsigned(L.nl * 3 * p.nDt * p.nIt)), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dg, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536))),
-                     dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dxsum, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
-                     dim3(256), 0, st, p);
+  const dim3 dg_grid(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536)));
+  const dim3 dxsum_grid(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20)));
+  const dim3 dw_grid(unsigned(L.nl * 3 * p.nDt * p.nIt));
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = side_stream_locked(dev);
+    if (ss && hipEventRecord(ss->fork, st) == hipSuccess &&
+        hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
+      hipLaunchKernelGGL(k_bwd_dg, dg_grid, dim3(256), 0, ss->s, p);
+      hipLaunchKernelGGL(k_bwd_dxsum, dxsum_grid, dim3(256), 0, ss->s, p);
+      hipLaunchKernelGGL(k_bwd_dw, dw_grid, dim3(kThreads), 0, st, p);
+      if (hipEventRecord(ss->join, ss->s) != hipSuccess ||
+          hipStreamWaitEvent(st, ss->join, 0) != hipSuccess)
+        return MOK_E_LAUNCH;
+    } else {
+      hipLaunchKernelGGL(k_bwd_dw, dw_grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL(k_bwd_dg, dg_grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_bwd_dxsum, dxsum_grid, dim3(256), 0, st, p);
+    }
+  }
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
 }
 

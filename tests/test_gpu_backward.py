@@ -99,6 +99,29 @@ def test_backward_expert_longer_than_row_table(S):
     _compare(cfg, d, ids, g, f"long-expert S={S}")
 
 
+def test_backward_outputs_ordered_on_caller_stream():
+    """Part of the backward runs on the library's side stream; a caller that waits on its
+    own stream only must still see every output complete."""
+    cfg = SMALL[1]
+    d = gen.make_inputs(cfg, seed=13, with_dy=True)
+    dev = DevInputs(d)
+    _, ref, _ = run_fwd_bwd(cfg, dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        layer = MoKLayer(L.desc_from_config(cfg, flags=L.MOK_FLAG_SAVE_FOR_BWD))
+        layer.schedule(dev.ids, stream=s.cuda_stream)
+        layer.forward(dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd, stream=s.cuda_stream)
+        for _ in range(3):
+            g = layer.backward(dev.dy, dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd,
+                               stream=s.cuda_stream)
+            # copies enqueued on the same stream see finished outputs
+            got = {k: v.clone() for k, v in g.items()}
+    s.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+
+
 def test_backward_config5_full_and_deterministic():
     cfg = gen.CONFIGS[5]
     say("[c5] generating")
