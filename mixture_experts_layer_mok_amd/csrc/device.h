@@ -21,13 +21,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
 }
 // Round to nearest, ties to even.  Values here are finite.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// float32 -> bf16, round to nearest even, with gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; every value rounded here is finite).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(v4u v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -7,7 +7,10 @@
 // one scale dword per row and step) is checked the same way: every code load stays
 // inside its own row's K bytes, every scale load inside its row of scales, and every
 // valid offset below 2^31 (the range of its buffer resource; setting bit 31 makes a load
-// out of range).  Built with the host compiler only; exits non-zero on a violation.
+// out of range).  The backward's K-major operands are checked too: weight offsets over
+// every K step, the column clamps of routed-row loads, and that each staged K row gets
+// all of its chunks once.  Built with the host compiler only; exits non-zero on a
+// violation.
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
