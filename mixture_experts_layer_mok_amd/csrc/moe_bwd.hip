@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void k_bwd_dxsum(BwdParams p) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   for (int t = gw; t < p.T; t += nw)
-    wave_pair_sum<kCpolPlain>(p.a.dx + int64_t(t) * p.D, p.P.dxbuf, int64_t(t) * p.k, p.D,
+    wave_pair_sum<kCpolPlain, 2>(p.a.dx + int64_t(t) * p.D, p.P.dxbuf, int64_t(t) * p.k, p.D,
                               p.P.pos, nullptr, p.k);
 }
 

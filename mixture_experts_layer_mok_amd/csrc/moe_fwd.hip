@@ -84,7 +84,7 @@ __device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uin
 // (wave_pair_sum).
 template <bool kCoherent>
 __device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
-  wave_pair_sum<kCoherent ? kCpolDev : kCpolPlain>(p.a.y + int64_t(t) * p.D, p.P.obuf,
+  wave_pair_sum<kCoherent ? kCpolDev : kCpolPlain, 4>(p.a.y + int64_t(t) * p.D, p.P.obuf,
                                                    int64_t(t) * p.k, p.D, p.P.pos, p.a.gates,
                                                    p.k);
 }

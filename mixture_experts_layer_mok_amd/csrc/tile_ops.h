@@ -61,9 +61,10 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // D bf16.  One wave per destination row; lane l owns the 16-byte chunks l, l + 64, ....
 // With a single slot (the usual case of an even expert share) the row is processed in
 // passes of kRowBatch chunks per lane; otherwise the wave loads kCombChunks chunks of
-// two slots at a time: either way 16 loads per lane are in flight.  Source loads use the
-// cache policy kPol (device scope for rows written by other workgroups of a running
-// kernel); every access goes through a row-length buffer resource.
+// kSlots slots at a time (8 kSlots loads per lane in flight; the forward's data movers
+// take 4, which their registers allow beside the tile code of the same kernel).  Source
+// loads use the cache policy kPol (device scope for rows written by other workgroups of
+// a running kernel); every access goes through a row-length buffer resource.
 constexpr int kCombChunks = 8;
 
 __device__ __forceinline__ void acc_gated(float (&acc)[8], v4u v, float g) {
@@ -79,7 +80,7 @@ __device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
 }
 
-template <int kPol>
+template <int kPol, int kSlots>
 __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* rows, int64_t q0,
                                               int D, const int32_t* pos, const float* gates,
                                               int k) {
@@ -114,26 +115,28 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
       for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
     uint64_t m = has;
     while (m) {
-      const int j0 = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int j1 = m ? __ffsll((unsigned long long)m) - 1 : -1;
-      if (m) m &= m - 1;
-      const rsrc_t r0 = row_rsrc(rows + (q0 + j0) * D, bytes);
-      // a missing second slot gets a zero-length range: its loads read nothing
-      const rsrc_t r1 = row_rsrc(rows + (q0 + (j1 >= 0 ? j1 : j0)) * D, j1 >= 0 ? bytes : 0u);
-      v4u v0[kCombChunks], v1[kCombChunks];
+      // the next kSlots local slots in ascending order; missing ones get a zero-length
+      // range, whose loads read nothing
+      int js[kSlots];
+      rsrc_t rs[kSlots];
 #pragma unroll
-      for (int c = 0; c < kCombChunks; ++c) {
-        v0[c] = buf_ld16<kPol>(r0, b0 + (lane + 64 * c) * 16);
-        v1[c] = buf_ld16<kPol>(r1, b0 + (lane + 64 * c) * 16);
+      for (int u = 0; u < kSlots; ++u) {
+        js[u] = m ? __ffsll((unsigned long long)m) - 1 : -1;
+        if (m) m &= m - 1;
+        rs[u] = row_rsrc(rows + (q0 + (js[u] >= 0 ? js[u] : 0)) * D, js[u] >= 0 ? bytes : 0u);
       }
-      const float g0 = __shfl(my_g, j0);
+      v4u v[kSlots][kCombChunks];
 #pragma unroll
-      for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v0[c], g0);
-      if (j1 >= 0) {
-        const float g1 = __shfl(my_g, j1);
+      for (int c = 0; c < kCombChunks; ++c)
 #pragma unroll
-        for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v1[c], g1);
+        for (int u = 0; u < kSlots; ++u) v[u][c] = buf_ld16<kPol>(rs[u], b0 + (lane + 64 * c) * 16);
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u) {
+        if (js[u] >= 0) {  // wave-uniform
+          const float g = __shfl(my_g, js[u]);
+#pragma unroll
+          for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v[u][c], g);
+        }
       }
     }
 #pragma unroll
