@@ -69,10 +69,11 @@ typedef enum {
                                        the resident minibatches for mok_moe_bwd          */
 #define MOK_FLAG_UNFUSED 0x2u       /* run the same steps as separate kernels over
                                        full-size buffers (comparison / phase timing)     */
-#define MOK_FLAG_SHORT_WAITS 0x4u   /* bounded waits of the fused forward expire after 1 us
-                                       instead of 2 s: the run sets MOK_DEV_TIMEOUT and
-                                       exits early with y undefined (tests the timeout
-                                       path; never for production use)                   */
+#define MOK_FLAG_SHORT_WAITS 0x4u   /* bounded waits of the fused forward and of the
+                                       backward's dH/dX launch expire after 1 us instead
+                                       of 2 s: the run sets MOK_DEV_TIMEOUT and exits
+                                       early with its outputs undefined (tests the
+                                       timeout path; never for production use)           */
 
 /* sticky device status bits (mok_read_device_status) */
 #define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */
@@ -164,7 +165,10 @@ mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* t
  * accumulated; experts with no rows get 0).  dW sums over rows run in a fixed order.
  * Asynchronous on stream: the dX row sum and d_topk_w run on an internal per-device
  * stream beside the dW GEMMs and are joined back to `stream` by an event, so all
- * outputs are complete when work enqueued later on `stream` starts. */
+ * outputs are complete when work enqueued later on `stream` starts.  dH and dX run as
+ * one persistent launch whose waits are bounded: should one expire, the device status
+ * gets MOK_DEV_TIMEOUT (mok_read_device_status) and the outputs are undefined; the
+ * next mok_schedule clears the status. */
 mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
                          const int32_t* topk_ids, const float* topk_w, const void* w_gate,
                          const void* w_up, const void* w_down, void* dx, float* d_topk_w,

@@ -81,6 +81,7 @@ template <bool COH>
 __device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t voff, uint32_t soff,
                                       const v4u* lds_wave_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  soff = __builtin_amdgcn_readfirstlane(soff);  // uniform; kept in an SGPR for the asm
   if (COH)
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen sc1 lds" ::"v"(voff),
                  "s"(rsrc), "s"(soff), "s"(m0)
@@ -299,6 +300,8 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //
 // Operand kinds:
 //   kKC  K-contiguous rows (the tile above; rows may be gathered);
+//   kKCD kKC read at device scope (sc1): rows written earlier in the same launch by
+//        workgroups on other XCDs;
 //   kKW  K-major weight matrix [K rows][ld]: tile column n is column n of every row;
 //        K rows past ksplit come from a second matrix (dX stacks W_gate over W_up);
 //   kKR  K-major routed rows of a row matrix: K index q is routed row r = rbeg + q at
@@ -310,7 +313,8 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //        every wait for the one also waits for the other.
 // For kKR and kKG, rows at or past rend read zero (bit 31 of the offset, against a 2 GB
 // resource).
-enum KmKind { kKC = 0, kKW = 1, kKR = 2, kKG = 3 };
+enum KmKind { kKC = 0, kKW = 1, kKR = 2, kKG = 3, kKCD = 4 };
+constexpr bool km_kcontig(int kind) { return kind == kKC || kind == kKCD; }
 constexpr uint32_t kKmOutOfRange = 0x80000000u;
 constexpr int kKmRowBytes = 512;  // one staged K row: 256 bf16
 
@@ -408,10 +412,11 @@ __device__ __forceinline__ void km_init_rows(KmOp& o, const void* base, int64_t 
 template <int KIND, int STAGE>
 __device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (KIND == kKC) {
+  if (km_kcontig(KIND)) {
 #pragma unroll
     for (int p = 0; p < geom::kLoads; ++p)
-      dma16<false>(o.r0, o.off[p], uint32_t(k0) * 2, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+      dma16<KIND == kKCD>(o.r0, o.off[p], uint32_t(k0) * 2,
+                          lds + STAGE * kStageChunks + (p * 8 + w) * 64);
   } else if (KIND == kKW) {
     const bool second = k0 >= o.ksplit;
     const uint32_t so = uint32_t(second ? k0 - o.ksplit : k0) * o.ld2;
@@ -479,7 +484,7 @@ __device__ __forceinline__ void km_frag_addr_init(KmFragAddr& fa) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wm = w >> 2, wn = w & 3;
-  if (AK == kKC) {
+  if (km_kcontig(AK)) {
     const int r32 = lane & 31;
     const uint32_t a0 = lds_addr(g_lds_a) + uint32_t(wm * 128 + r32) * 128;
 #pragma unroll
@@ -497,7 +502,7 @@ template <int AK, int S>
 __device__ __forceinline__ void km_frag_load(TileFrag& f, const KmFragAddr& fa, int ks) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (AK == kKC)
+    if (km_kcontig(AK))
       f.a[i] = *reinterpret_cast<lds_cv4u*>(uintptr_t(fa.a[ks] + S * kStageBytes + i * 32 * 128));
     else
       f.a[i] = km_frag(fa.a[i] + S * kStageBytes + ks * 16 * kKmRowBytes);
@@ -541,8 +546,8 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K loop of nk steps over operands a (kind AK: kKC, kKR or kKG) and b (kind BK: kKW, kKR
-// or kKG; at most one kKG operand: they share the LDS offset table).
+// K loop of nk steps over operands a (kind AK: kKC, kKCD, kKR or kKG) and b (kind BK: kKW,
+// kKR or kKG; at most one kKG operand: they share the LDS offset table).
 // C = A B^T as for tile_gemm, with A's tile row m / B's tile row n read as column m / n
 // of a K-major operand.  Ends with a barrier.
 template <int AK, int BK>

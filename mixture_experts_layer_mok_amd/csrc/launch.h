@@ -19,6 +19,7 @@ struct Ptrs {
   int32_t* tile_base; // [n_mb_max + 1]
   int32_t* mb_start;  // [n_mb_max + 1]: first row of each minibatch; [n_mb] = R
   uint32_t* sync;     // device counters
+  uint32_t* bsync;    // backward counters: dH tiles done per m-tile
   uint16_t* obuf;     // [T*k, D] bf16: expert output of pair t*k + j
   uint8_t* ring;      // S slots
   uint8_t* full_x;    // unfused: [T*k, D] dispatched rows (bf16 or MX codes)
@@ -52,6 +53,7 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.tile_base = reinterpret_cast<int32_t*>(b + L.off_tile_base);
   P.mb_start = reinterpret_cast<int32_t*>(b + L.off_mb_start);
   P.sync = reinterpret_cast<uint32_t*>(b + L.off_sync);
+  P.bsync = reinterpret_cast<uint32_t*>(b + L.off_sync + L.sync_bwd);
   P.obuf = reinterpret_cast<uint16_t*>(b + L.off_obuf);
   P.ring = b + L.off_ring;
   P.full_x = L.unfused ? b + L.off_full_x : nullptr;

@@ -35,6 +35,7 @@ enum HdrWord : int {
   kHdrAbort = 5,       // set when a bounded wait expires; every loop exits
   kHdrFwdTiles = 6,    // fused forward: total tiles
   kHdrDrainTicket = 7, // fused forward: next drain work chunk
+  kHdrBwdTicket = 8,   // backward dH/dX kernel: next tile ticket
   kHdrWords = 64
 };
 
@@ -56,7 +57,7 @@ struct Layout {
   bool repack_wg, repack_wd;
   // byte offsets into the workspace
   size_t off_hdr, off_counts, off_offsets, off_blk, off_perm, off_pos, off_mt_tab, off_mt_cnt,
-      off_tile_base, off_mb_start, off_sync, sync_bytes, off_obuf, off_ring, slot_bytes;
+      off_tile_base, off_mb_start, off_sync, sync_bytes, sync_bwd, off_obuf, off_ring, slot_bytes;
   int64_t slot_rows;  // rows one slot holds: a minibatch's tiles may run past its window
   size_t slot_x, slot_xs, slot_h, slot_hs, slot_ab;  // offsets inside one slot
   size_t off_full_x, off_full_xs, off_full_h, off_full_hs;
@@ -123,11 +124,9 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->off_tile_base = o; o = align_up(o + (L->n_mb_max + 1) * 4, A);
   L->off_mb_start = o; o = align_up(o + (L->n_mb_max + 1) * 4, A);
   // forward counters: ready[n_mb], done[n_mb], hdone[n_mb * mt_max];
-  // backward counters: bready[n_mb], bdone[n_mb], hd[n_mb*mt_max], dxd[n_mb*mt_max],
-  // wdone[n_mb * nl * 3]
-  L->sync_bytes = align_up((2 * L->n_mb_max + L->n_mb_max * L->mt_max) * 4, A) +
-                  align_up((2 * L->n_mb_max + 2 * L->n_mb_max * L->mt_max +
-                            3 * L->n_mb_max * nl) * 4, A);
+  // backward counters (from sync_bwd): dH tiles done per m-tile [n_mb * mt_max]
+  L->sync_bwd = align_up((2 * L->n_mb_max + L->n_mb_max * L->mt_max) * 4, A);
+  L->sync_bytes = L->sync_bwd + align_up(L->n_mb_max * L->mt_max * 4, A);
   L->off_sync = o; o = align_up(o + L->sync_bytes, A);
   L->off_obuf = o; o = align_up(o + size_t(L->TK) * D * 2, A);
   // one ring slot

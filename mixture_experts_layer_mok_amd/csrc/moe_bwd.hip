@@ -15,12 +15,13 @@
 // gfx950's transposing LDS reads: nothing is transposed in memory.  Each dW tile has one
 // owner and one K order (the expert's rows ascending): no atomics, bitwise reproducible.
 //
-// This file holds the path as separate kernels.  The gate/up pre-activations a, b come
-// from the forward where it still holds them and are recomputed otherwise (replay of
-// GEMM1), following the reverse ring traversal: after a fused forward the ring slots
-// hold the last S minibatches (the dH epilogue reads their a, b there), and only
-// minibatches whose slot was recycled, mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for
-// the backward writes a, b of every row, and nothing is replayed.
+// dH and dX share one persistent launch (tile tickets); the other steps are separate
+// kernels.  The gate/up pre-activations a, b come from the forward where it still holds
+// them and are recomputed otherwise (replay of GEMM1), following the reverse ring
+// traversal: after a fused forward the ring slots hold the last S minibatches (the dH
+// epilogue reads their a, b there), and only minibatches whose slot was recycled,
+// mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for the
+// backward writes a, b of every row, and nothing is replayed.
 #include <algorithm>
 #include <mutex>
 
@@ -37,6 +38,7 @@ struct BwdParams {
   int ring_2g;   // 1: ring offsets stay below 2^31 bytes
   int64_t slot_x;
   int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
+  uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
 };
 
 // a, b of the rows of m-tile e in minibatch mb: in the ring slot while the minibatch is
@@ -63,6 +65,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(BwdParams p) {
   const int R = int(p.P.hdr[kHdrR]);
   const int n_mb = int(p.P.hdr[kHdrNmb]);
   const bool x_ring = x_in_ring(p);
+  // counters of the dH/dX launch that follows on the same stream
+  const int nc = p.n_mb_max * p.mt_max;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < nc; i += gridDim.x * 256) p.P.bsync[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    p.P.hdr[kHdrBwdTicket] = 0;
+    p.P.hdr[kHdrAbort] = 0;
+  }
   for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256) {
     const uint32_t tb = uint32_t(p.P.perm[r] / p.k) * uint32_t(p.D) * 2u;
     p.P.dyb[r] = tb;
@@ -128,45 +137,72 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
   }
 }
 
-// dH GEMM: u = dY rows x W_down[e] (K = D over the rows of W_down, read K-major), fused
-// SwiGLU backward and dG partials.
-__global__ __launch_bounds__(512) void k_bwd_dh(BwdParams p) {
-  const int nq = int(p.P.hdr[kHdrMtiles]) * p.nNdh;
+// dH tile (m-tile g, column tile nt): u = dY rows x W_down[e] (K = D over the rows of
+// W_down, read K-major), fused SwiGLU backward and dG partials.  da, db are stored at
+// device scope: dX tiles on other XCDs read them in the same launch.
+__device__ __forceinline__ void dh_tile(const BwdParams& p, int g, int nt) {
   const int64_t wsz = int64_t(p.I) * p.D;
-  for (int q = blockIdx.x; q < nq; q += gridDim.x) {
-    int4 e;
-    int mb;
-    mtile_at(p, q / p.nNdh, e, mb);
-    const int nt = q % p.nNdh;
-    const int n0 = nt * kBN2;
-    const uint16_t* wd = p.a.wd + e.z * wsz;
-    KmOp a, b;
-    km_init_kc_gather(a, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y);
-    km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
-    TileAcc acc;
-    tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
-    epi_dh(acc, e.y, e.x, n0, p.I, ab_rows(p, e, mb), p.a.gates, p.P.perm, p.P.bdab, p.P.gh,
-           p.P.dgpart, nt, p.nNdh);
-  }
+  int4 e;
+  int mb;
+  mtile_at(p, g, e, mb);
+  const int n0 = nt * kBN2;
+  const uint16_t* wd = p.a.wd + e.z * wsz;
+  KmOp a, b;
+  km_init_kc_gather(a, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y);
+  km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
+  TileAcc acc;
+  tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
+  epi_dh<kCpolDev>(acc, e.y, e.x, n0, p.I, ab_rows(p, e, mb), p.a.gates, p.P.perm, p.P.bdab,
+                   p.P.gh, p.P.dgpart, nt, p.nNdh);
 }
 
-// dX GEMM: dx rows = [da | db] x [W_gate; W_up][e] (K = 2I over the rows of W_gate, then
-// W_up, read K-major), pushed to their pairs.
-__global__ __launch_bounds__(512) void k_bwd_dx(BwdParams p) {
-  const int nq = int(p.P.hdr[kHdrMtiles]) * p.nDt;
+// dX tile (m-tile g, column tile nt): dx rows = [da | db] x [W_gate; W_up][e] (K = 2I over
+// the rows of W_gate, then W_up, read K-major), pushed to their pairs.  The da, db rows
+// come from dH tiles of the same launch, so they are read at device scope.
+__device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
   const int64_t K = 2 * int64_t(p.I);
   const int64_t wsz = int64_t(p.I) * p.D;
-  for (int q = blockIdx.x; q < nq; q += gridDim.x) {
-    int4 e;
-    int mb;
-    mtile_at(p, q / p.nDt, e, mb);
-    const int n0 = (q % p.nDt) * kBN2;
-    KmOp a, b;
-    km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
-    km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
-    TileAcc acc;
-    tile_gemm_km<kKC, kKW>(a, b, int(K / kBK), acc);
-    epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+  int4 e;
+  int mb;
+  mtile_at(p, g, e, mb);
+  const int n0 = nt * kBN2;
+  KmOp a, b;
+  km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
+  km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
+  TileAcc acc;
+  tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
+  epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+}
+
+// dH and dX in one persistent launch.  Workgroups take tile tickets in order: first
+// every dH tile (m-tiles slowest), then every dX tile.  A dX tile of m-tile g waits until
+// the dH tiles of g have all signalled, so the last round of dH tiles shares the CUs with
+// the first dX tiles instead of leaving most of them idle.  Every dH ticket is taken
+// before any dX ticket and a dH tile waits for nothing, so each wait ends.  Waits are
+// bounded and every loop exits once the abort word is set.
+__global__ __launch_bounds__(512) void k_bwd_dhdx(BwdParams p) {
+  uint32_t* hdr = p.P.hdr;
+  uint32_t* hd = p.P.bsync;
+  const uint32_t mt = hdr[kHdrMtiles];
+  const uint32_t nh = mt * uint32_t(p.nNdh);
+  const uint32_t total = nh + mt * uint32_t(p.nDt);
+  __shared__ uint32_t s_tk;
+  while (true) {
+    if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrBwdTicket, 1u);
+    __syncthreads();
+    const uint32_t tk = __builtin_amdgcn_readfirstlane(s_tk);  // wave-uniform
+    __syncthreads();
+    if (tk >= total || aborted(hdr)) break;
+    if (tk < nh) {
+      const int g = int(tk) / p.nNdh;
+      dh_tile(p, g, int(tk) % p.nNdh);
+      wg_signal_add(hd + g, 1u);
+    } else {
+      const int q = int(tk - nh);
+      const int g = q / p.nDt;
+      if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
+      dx_tile(p, g, q % p.nDt);
+    }
   }
 }
 
@@ -282,6 +318,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.slot_x = int64_t(L.slot_x);
   p.ring_2g = int64_t(L.S) * int64_t(L.slot_bytes) < (int64_t(1) << 31) ? 1 : 0;
   p.per_mt = int(L.nN1 + L.nN2);
+  p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -291,8 +328,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   hipLaunchKernelGGL(k_bwd_rows, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
                      dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dh, tiles_grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dx, tiles_grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_bwd_dhdx, tiles_grid, dim3(kThreads), 0, st, p);
   const dim3 dg_grid(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536)));
   const dim3 dxsum_grid(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20)));
   const dim3 dw_grid(unsigned(L.nl * 3 * p.nDt * p.nIt));

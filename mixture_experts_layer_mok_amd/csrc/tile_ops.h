@@ -327,7 +327,9 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 // into h there), and the partial sum of u h over this tile's columns for each row into
 // dgpart[row][nt] (lanes first, then the four column waves in order: a fixed summation
 // order).  Loads and stores go through buffer resources sized to the tile's rows, so
-// rows past the tile read zero and their stores are dropped.
+// rows past the tile read zero and their stores are dropped.  kStPol is the cache policy
+// of the da, db stores (kCpolDev when the same launch reads them on other XCDs).
+template <int kStPol>
 __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int n0, int I,
                                        const uint16_t* ab_tile, const float* gates,
                                        const int32_t* perm, uint16_t* bdab, uint16_t* gh,
@@ -387,9 +389,9 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
           const float db = dh * sl;
           const uint32_t r8 = uint32_t(8 * q + t);
           const uint32_t so = r8 * uint32_t(twoI) * 2u;
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(da), dab_res, voff, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(da), dab_res, voff, so, kStPol);
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(db), dab_res, voff,
-                                                so + uint32_t(I) * 2u, 0);
+                                                so + uint32_t(I) * 2u, kStPol);
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * h), gh_res, goff,
                                                 r8 * uint32_t(I) * 2u, 0);
         }

@@ -151,3 +151,27 @@ def test_backward_after_fused_and_unfused_forward_agree(cfg):
     for name in g_f:
         assert torch.equal(g_f[name], g_u[name]), name
         assert torch.equal(g_f[name], g_1[name]), name
+
+
+def test_backward_wait_timeout_exits_and_recovers():
+    """dX tiles wait for the dH tiles of their m-tile inside one launch.  With
+    MOK_FLAG_SHORT_WAITS such a wait expires after 1 us, well before a dH tile with
+    K = 1024 ends, so the backward must time out after an (unfused, wait-free) forward:
+    the launch still exits, the status word carries MOK_DEV_TIMEOUT, and the next
+    schedule, forward and backward on the same workspace are correct again."""
+    cfg = gen.small_config("bwd-timeout", T=512, D=1024, I=512, E=4, k=2, M=256, S=2,
+                           comm_cus=8)
+    d = gen.make_inputs(cfg, seed=14, with_dy=True)
+    dev = DevInputs(d)
+    say("[bwd-timeout] short waits")
+    flags = L.MOK_FLAG_SAVE_FOR_BWD | L.MOK_FLAG_UNFUSED
+    _, _, layer = run_fwd_bwd(cfg, dev, flags=flags | L.MOK_FLAG_SHORT_WAITS)
+    assert layer.status() & L.MOK_DEV_TIMEOUT
+    say("[bwd-timeout] recovery run")
+    layer.desc = L.desc_from_config(cfg, flags=flags)
+    layer.schedule(dev.ids)
+    layer.forward(dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd)
+    g = layer.backward(dev.dy, dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    _compare(cfg, d, d["ids"], g, cfg.name)
