@@ -192,38 +192,63 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
     }
 }
 
-// Epilogue of GEMM2: rows [0, rows), hidden columns [n0, n0 + 256) (B tile row b is
-// hidden column n0 + b in the split layout); row r's result is
-// pushed to obuf row perm_rows[r] (its pair index t*k + j).
+// Epilogue of GEMM2 and of dX: rows [0, rows), columns [n0, n0 + 256) of D (B tile row b
+// is column n0 + b in the split layout); row r's result goes to obuf row perm_rows[r]
+// (its pair index t*k + j).  The tile is first staged in LDS as bf16 rows (tile rows
+// 0..127 in the A stages, 128..255 in the B stages; free once the K loop has ended), so
+// that each wave then writes whole 512-byte row segments, 8 bytes a lane, instead of
+// 2-byte pieces.  A row's staged columns are XOR-swizzled by 32 on bit 2 of the row: the
+// two half-waves of an MFMA block write rows 4 apart, which would otherwise share
+// banks.  With kCoherent the row stores are device scope.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
                                             const int32_t* perm_rows, uint16_t* obuf) {
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
+  const int w = tid >> 6;
+  const int wn = w & 3;
+  {
+    uint16_t* st = reinterpret_cast<uint16_t*>(w >> 2 ? g_lds_b : g_lds_a);
+    const int swz = (lane >> 5) << 5;  // bit 2 of every row this lane holds
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int dst[16];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = acc_row(tid, i, v);
-      dst[v] = row < rows ? perm_rows[row] : -1;
-    }
+      for (int j = 0; j < 2; ++j) {
+        const int b = (brow_of(j, wn) + (lane & 31)) ^ swz;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + brow_of(j, wn) + (lane & 31);
-      if (col >= D) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (dst[v] >= 0) {
-          uint16_t* o = obuf + int64_t(dst[v]) * D + col;
-          const uint16_t b = f32_to_bf16(acc.c[i][j][v]);
-          if (kCoherent) st_dev_u16(o, b);
-          else *o = b;
+        for (int v = 0; v < 16; ++v) {
+          const int rl = acc_row(tid, i, v) & 127;
+          st[rl * 256 + b] = f32_to_bf16(acc.c[i][j][v]);
         }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      }
   }
+  __syncthreads();
+  // wave w writes tile rows w, w + 8, ..: their destinations are loaded one per lane
+  // and all 32 staged rows are read before the first store, so that no load waits
+  // behind a store (vector memory operations complete in order)
+  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int kRowsPerWave = 256 / (kThreads / 64);
+  const int wr = __builtin_amdgcn_readfirstlane(w);
+  const int my_r = wr + (kThreads / 64) * (lane % kRowsPerWave);
+  const int my_dst = my_r < rows ? perm_rows[my_r] : 0;
+  uint64_t val[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = wr + (kThreads / 64) * k;
+    val[k] = *reinterpret_cast<const uint64_t*>(
+        reinterpret_cast<const uint16_t*>(r >> 7 ? g_lds_b : g_lds_a) + (r & 127) * 256 +
+        ((4 * lane) ^ (((r >> 2) & 1) << 5)));
+  }
+  const uint32_t row_bytes = uint32_t(D) * 2u;
+  const uint32_t off = uint32_t(n0 + 4 * lane) * 2u;  // columns past D are dropped
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = wr + (kThreads / 64) * k;
+    if (r >= rows) break;  // wave-uniform
+    const int dst = __builtin_amdgcn_readlane(my_dst, k);
+    buf_st8<kPol>(row_rsrc(obuf + int64_t(dst) * D, row_bytes), off, val[k]);
+  }
+  __syncthreads();
 }
 
 // Epilogue of the MXFP8 GEMM1: SwiGLU as in epi_swiglu, then H is MX-quantised along I.
