@@ -153,43 +153,99 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
 // block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
 // column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
 // Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
-// [rows, 2I]: gate in [0, I), up in [I, 2I).  With kCoherent both are written at device
-// scope: in the fused kernel a ring slot is rewritten by workgroups on other XCDs within
-// one launch, and a plain store would leave a dirty line in one XCD's L2 that could be
-// written back after a newer one from another XCD.
+// [rows, 2I]: gate in [0, I), up in [I, 2I).  h is formed from the fp32 accumulators.
+// Each output is staged in LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255
+// in the B stages) and then written as whole row segments, 8 bytes a lane.  Staged
+// columns are XOR-swizzled in 16-column groups by (up half, bit 2 of the row), so that
+// the four lane groups of an MFMA block that write at once hit different banks.  With
+// kCoherent both are written at device scope: in the fused kernel a ring slot is
+// rewritten by workgroups on other XCDs within one launch, and a plain store would leave
+// a dirty line in one XCD's L2 that could be written back after a newer one from another
+// XCD.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
                                            uint16_t* H, int64_t ldh, uint16_t* AB) {
+  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int W = kThreads / 64;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
+  const int w = tid >> 6;
+  const int wn = w & 3;
+  const int wr = __builtin_amdgcn_readfirstlane(w);
   const bool gate_lane = (lane & 16) == 0;
+  const int rbit = lane >> 5;  // bit 2 of every row this lane holds
+  const int l32 = lane & 31, half = lane >> 5;
+  const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
+  uint16_t* st = reinterpret_cast<uint16_t*>(w >> 2 ? g_lds_b : g_lds_a);
+  auto stage_row = [](int r) {
+    return reinterpret_cast<const uint16_t*>(r >> 7 ? g_lds_b : g_lds_a);
+  };
+  if (AB) {
+    // rows of 256 columns: gate 0..127, up 128..255
+    const int sw = ((gate_lane ? 0 : 2) | rbit) << 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + (brow_of(j, wn) >> 5) * 16 + (lane & 15);
+      for (int j = 0; j < 2; ++j) {
+        const int c = (16 * (2 * wn + j) + (lane & 15) + (gate_lane ? 0 : 128)) ^ sw;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = acc.c[i][j][v];
-        const float y = __shfl_xor(x, 16);
-        const int row = acc_row(tid, i, v);
-        if (row < rows && col < I) {
-          if (H && gate_lane) {
-            const uint16_t h = f32_to_bf16(silu_f(x) * y);
-            const int off = row * int(ldh) + col;  // < 2^31: row < 256, ldh <= 65536
-            if (kCoherent) st_dev_u16(H + off, h);
-            else H[off] = h;
-          }
-          if (AB) {
-            uint16_t* ab = AB + row * 2 * I + (gate_lane ? col : I + col);
-            if (kCoherent) st_dev_u16(ab, f32_to_bf16(x));
-            else *ab = f32_to_bf16(x);
-          }
+        for (int v = 0; v < 16; ++v)
+          st[(acc_row(tid, i, v) & 127) * 256 + c] = f32_to_bf16(acc.c[i][j][v]);
+      }
+    __syncthreads();
+    // wave w: rows w, w + 8, ..; lanes 0..31 write the gate segment, 32..63 the up one
+    constexpr int kRows = 256 / W;
+    uint64_t val[kRows];
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int r = wr + W * k;
+      const int c = (4 * l32 + 128 * half) ^ (((half << 1) | ((r >> 2) & 1)) << 4);
+      val[k] = *reinterpret_cast<const uint64_t*>(stage_row(r) + (r & 127) * 256 + c);
+    }
+    const rsrc_t rab = row_rsrc(AB, uint32_t(rows) * uint32_t(2 * I) * 2u);
+    const uint32_t coff = uint32_t((half ? I : 0) + n0 + 4 * l32) * 2u;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int r = wr + W * k;
+      if (r >= rows) break;  // wave-uniform
+      if (col_ok) buf_st8<kPol>(rab, uint32_t(r) * uint32_t(2 * I) * 2u + coff, val[k]);
+    }
+    __syncthreads();
+  }
+  if (H) {
+    // rows of 128 columns (gate lanes form h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = (16 * (2 * wn + j) + (lane & 15)) ^ (rbit << 4);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float x = acc.c[i][j][v];
+          const float y = __shfl_xor(x, 16);
+          if (gate_lane) st[(acc_row(tid, i, v) & 127) * 128 + c] = f32_to_bf16(silu_f(x) * y);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);  // one block at a time: few live registers
+    __syncthreads();
+    // wave w: row pairs w, w + 8, ..; a 256-byte segment is 32 lanes: two rows a store
+    constexpr int kPairs = 128 / W;
+    uint64_t val[kPairs];
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * (wr + W * k) + half;
+      const int c = (4 * l32) ^ (((r >> 2) & 1) << 4);
+      val[k] = *reinterpret_cast<const uint64_t*>(stage_row(r) + (r & 127) * 128 + c);
     }
+    const rsrc_t rh = row_rsrc(H, uint32_t(rows) * uint32_t(ldh) * 2u);
+    const uint32_t coff = uint32_t(n0 + 4 * l32) * 2u;
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * (wr + W * k) + half;
+      if (2 * (wr + W * k) >= rows) break;  // wave-uniform; the odd row is checked below
+      if (col_ok && r < rows) buf_st8<kPol>(rh, uint32_t(r) * uint32_t(ldh) * 2u + coff, val[k]);
+    }
+    __syncthreads();
+  }
 }
 
 // Epilogue of GEMM2 and of dX: rows [0, rows), columns [n0, n0 + 256) of D (B tile row b
