@@ -4,6 +4,7 @@
                     [--comm-cus C] [--unfused] [--fwd-only] [--no-cpu-baseline]
     python bench.py --sweep            # minibatch x comm-CU sweep of the forward, JSON lines
     python bench.py --copy-calibration # one plain device copy of known size (counter scale)
+    python bench.py --autotune [--autotune-cache F]  # tune M and comm CUs first, then time
 
 A step is one pass of the layer over one batch of synthetic input on one GPU's share of
 an expert-parallel layer (hidden 7168, expert intermediate 2048, 64 experts of which 8
@@ -59,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--autotune", action="store_true",
+                    help="choose M and comm CUs for this shape on the device before timing")
+    ap.add_argument("--autotune-cache", default=None, help="JSON cache of tuned choices")
     ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
@@ -271,6 +275,21 @@ def main():
     dev = torch.device("cuda:0")
     d, t, layer = setup(cfg, args.unfused, with_bwd, dev)
     R = routed_rows(cfg, d["ids"])
+    tuned = None
+    if args.autotune:
+        from mixture_experts_layer_mok_amd import autotune as A
+        from mixture_experts_layer_mok_amd.layer import MoKLayer
+        log("tuning the minibatch size and the comm-CU split for this shape")
+        ch = A.tune(L.desc_from_config(cfg), t["x"], t["ids"], t["gates"], t["wg"], t["wu"],
+                    t["wd"], scales=(t.get("sg"), t.get("su"), t.get("sd")),
+                    cache_path=args.autotune_cache)
+        tuned = {"minibatch_rows": ch.minibatch_rows, "comm_cus": ch.comm_cus,
+                 "fwd_ms": ch.fwd_ms, "trials": len(ch.trials)}
+        cfg = cfg.replace(M=ch.minibatch_rows, comm_cus=ch.comm_cus)
+        flags = (L.MOK_FLAG_UNFUSED if args.unfused else 0) | (L.MOK_FLAG_SAVE_FOR_BWD if with_bwd else 0)
+        del layer
+        torch.cuda.empty_cache()
+        layer = MoKLayer(L.desc_from_config(cfg, flags=flags), device=dev)
     flops_fwd = 6.0 * cfg.D * cfg.I * R
     flops_bwd = 12.0 * cfg.D * cfg.I * R if with_bwd else 0.0
     log(f"timing {args.steps} steps after {args.warmup} warmup")
@@ -300,7 +319,7 @@ def main():
                                f"top-{cfg.k}" + (", forward+backward" if with_bwd else
                                                  ", forward"),
                    "routed_rows": R, "minibatch_rows": cfg.M, "ring_slots": cfg.S,
-                   "comm_cus": cfg.comm_cus, "mode": mode},
+                   "comm_cus": cfg.comm_cus, "mode": mode, **({"autotuned": tuned} if tuned else {})},
         "schedule_ms": stats(r["sched_ms"]),
         "fwd_ms": stats(r["fwd_ms"]),
         "fwd_tflops": round(achieved, 2),
