@@ -554,7 +554,31 @@ __device__ __forceinline__ void km_issue_step(KmOp& a, KmOp& b, int k0) {
   km_issue<BK, S>(b, k0, g_lds_b);
 }
 
-// One K step kb in stage S, as tile_step.
+// Load p (0..3) of one K step of a non-gathered K-major or K-contiguous operand, into
+// stage STAGE of lds, or with `dummy` into g_lds_dummy (loads past the last step).
+template <int KIND, int STAGE>
+__device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* lds, bool dummy) {
+  static_assert(KIND != kKG, "gathered operands are issued per step (km_issue)");
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const v4u* dst = dummy ? g_lds_dummy + w * 64 : lds + STAGE * kStageChunks + (p * 8 + w) * 64;
+  if (km_kcontig(KIND)) {
+    dma16<KIND == kKCD>(o.r0, o.off[p], uint32_t(k0) * 2, dst);
+  } else if (KIND == kKW) {
+    const bool second = k0 >= o.ksplit;
+    const uint32_t so = uint32_t(second ? k0 - o.ksplit : k0) * o.ld2;
+    dma16<false>(second ? o.r1 : o.r0, o.off[p], so, dst);
+  } else {
+    const int l = threadIdx.x & 63;
+    const int r = o.rbeg + k0 + geom::km_row(p, w, l);
+    const uint32_t voff = r < o.rend ? __umul24(uint32_t(r), o.ld2) + o.off[p] : kKmOutOfRange;
+    dma16<false>(o.r0, voff, 0u, dst);
+  }
+}
+
+// One K step kb in stage S, as tile_step: after the barrier, the loads of step kb + 2 of
+// each non-gathered operand go out one per MFMA of the last slice (past the last step
+// into g_lds_dummy, so the MFMAs sit in no branch); a gathered operand's loads, which
+// read their offsets from the LDS row table, go out in one group before them.
 template <int AK, int BK, int S>
 __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, int kb, int nk,
                                         TileFrag& f0, TileFrag& f1, TileAcc& acc) {
@@ -575,12 +599,27 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kb + 2 < nk) km_issue_step<AK, BK, S>(a, b, (kb + 2) * kBK);
-    km_frag_load<AK, SN>(f0, fa, 0);
+    if (kb + 2 < nk) {
+      if (AK == kKG) km_issue<AK, S>(a, (kb + 2) * kBK, g_lds_a);
+      if (BK == kKG) km_issue<BK, S>(b, (kb + 2) * kBK, g_lds_b);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f1, acc);
+  const bool past = kb + 2 >= nk;
+  const int kn = __builtin_amdgcn_readfirstlane(past ? kb * kBK : (kb + 2) * kBK);
+  km_frag_load<AK, SN>(f0, fa, 0);  // past the last step: stale, unused
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = q >> 1, j = q & 1;
+    acc.c[i][j] = mfma32x32x16(f1.a[i], f1.b[j], acc.c[i][j]);
+    if (q < 4) {
+      if (AK != kKG) km_issue_one<AK == kKG ? kKC : AK, S>(a, kn, q, g_lds_a, past);
+    } else {
+      if (BK != kKG) km_issue_one<BK == kKG ? kKW : BK, S>(b, kn, q - 4, g_lds_b, past);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // K loop of nk steps over operands a (kind AK: kKC, kKCD, kKR or kKG) and b (kind BK: kKW,
@@ -614,6 +653,7 @@ __device__ __forceinline__ void tile_gemm_km(KmOp& a, KmOp& b, int nk, TileAcc& 
     km_step<AK, BK, 0>(a, b, fa, kb, nk, f0, f1, acc);
     if (kb + 1 < nk) km_step<AK, BK, 1>(a, b, fa, kb + 1, nk, f0, f1, acc);
   }
+  wait_vmcnt<0>();  // the loads issued past the last step
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
