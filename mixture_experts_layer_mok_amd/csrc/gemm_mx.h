@@ -98,26 +98,32 @@ __device__ __forceinline__ void mx_src_init(MxSrc& s, int layout, const uint8_t*
 //     chunk 64 bytes lower instead (same row, in bounds); their LDS slots belong to
 //     slice 1, which a half step multiplies with zero scales.
 template <bool COH, int STAGE>
-__device__ __forceinline__ void mx_issue(const MxSrc& s, int ks, int nk, bool valid, bool half) {
+__device__ __forceinline__ void mx_issue_part(const MxSrc& s, int ks, int nk, bool valid, bool half,
+                                              int q) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const uint32_t kb = uint32_t(ks) * 128;
   const TileSrc& d = s.data;
   const uint32_t adj = valid ? ((half && !geom::mx_chunk_in_half(w, l)) ? 0u - 64u : 0u)
                              : kOffOutOfRange;
-#pragma unroll
-  for (int p = 0; p < geom::kLoads; ++p)
-    dma16<COH>(d.ra, d.oa[p] + adj, kb, stage_a<STAGE>() + (p * 8 + w) * 64);
-  const bool paired_up = d.layout == geom::kPaired && ((w >> 1) & 1);
-#pragma unroll
-  for (int p = 0; p < geom::kLoads; ++p) {
+  if (q < geom::kLoads) {
+    dma16<COH>(d.ra, d.oa[q] + adj, kb, stage_a<STAGE>() + (q * 8 + w) * 64);
+  } else if (q < 2 * geom::kLoads) {
+    const int p = q - geom::kLoads;
+    const bool paired_up = d.layout == geom::kPaired && ((w >> 1) & 1);
     const bool use_b1 = d.layout == geom::kPaired ? paired_up : (p >= 2);
-    dma16<false>(use_b1 ? d.rb1 : d.rb0, d.ob[p] + adj, kb,
-                 stage_b<STAGE>() + (p * 8 + w) * 64);
+    dma16<false>(use_b1 ? d.rb1 : d.rb0, d.ob[p] + adj, kb, stage_b<STAGE>() + (p * 8 + w) * 64);
+  } else {
+    // one instruction for every wave: the LDS destination is a wave-uniform select
+    const uint32_t* sdst = (w < 4 ? g_lds_sa : g_lds_sb) + STAGE * 256 + (w & 3) * 64;
+    dma4<COH>(s.scale + (valid ? ks : nk - 1) * 4, sdst);
   }
-  // one instruction for every wave: the LDS destination is a wave-uniform select
-  const uint32_t* sdst = (w < 4 ? g_lds_sa : g_lds_sb) + STAGE * 256 + (w & 3) * 64;
-  dma4<COH>(s.scale + (valid ? ks : nk - 1) * 4, sdst);
+}
+
+template <bool COH, int STAGE>
+__device__ __forceinline__ void mx_issue(const MxSrc& s, int ks, int nk, bool valid, bool half) {
+#pragma unroll
+  for (int q = 0; q <= 2 * geom::kLoads; ++q) mx_issue_part<COH, STAGE>(s, ks, nk, valid, half, q);
 }
 
 struct MxScales {
@@ -226,7 +232,10 @@ __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, 
   wait_all_loads();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  mx_issue<COH, S>(src, ks + 2, nk, ks + 2 < nk, src.half_last && ks + 2 == nk - 1);
+  // the loads of step ks + 2: the scales now, the data two per MFMA row of slice 1 (a
+  // burst of them fills the vector-memory queue and holds up the MFMAs behind it)
+  const bool nvalid = ks + 2 < nk, nhalf = src.half_last && ks + 2 == nk - 1;
+  mx_issue_part<COH, S>(src, ks + 2, nk, nvalid, nhalf, 2 * geom::kLoads);
   bn[0] = mx_read_b<SN>(fa, 0, 0);
   bn[1] = mx_read_b<SN>(fa, 0, 1);
   // slice 1 (zero scales on a half step: its products fall below the smallest float),
@@ -241,6 +250,8 @@ __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, 
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
     mx_mma_row<1>(a[i], b, s1.a[i], s1, acc.c[i]);
+    mx_issue_part<COH, S>(src, ks + 2, nk, nvalid, nhalf, 2 * i);
+    mx_issue_part<COH, S>(src, ks + 2, nk, nvalid, nhalf, 2 * i + 1);
     __builtin_amdgcn_sched_barrier(0);
     a[i] = mx_read_a<SN>(fa, 0, i);
   }
