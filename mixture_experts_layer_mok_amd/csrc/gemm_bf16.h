@@ -343,6 +343,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //        K rows past ksplit come from a second matrix (dX stacks W_gate over W_up);
 //   kKR  K-major routed rows of a row matrix: K index q is routed row r = rbeg + q at
 //        byte r * row bytes;
+//   kKRD kKR read at device scope (rows written earlier in the same launch);
 //   kKG  K-major routed rows gathered: row r starts at byte rowb[r] of the resource.
 //        The offsets are staged in LDS per window of kRowTabLds rows (loaded at the
 //        start and every kRowTabLds rows): reading them from memory in the load loop
@@ -350,7 +351,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
 //        every wait for the one also waits for the other.
 // For kKR and kKG, rows at or past rend read zero (bit 31 of the offset, against a 2 GB
 // resource).
-enum KmKind { kKC = 0, kKW = 1, kKR = 2, kKG = 3, kKCD = 4 };
+enum KmKind { kKC = 0, kKW = 1, kKR = 2, kKG = 3, kKCD = 4, kKRD = 5 };
 constexpr bool km_kcontig(int kind) { return kind == kKC || kind == kKCD; }
 constexpr uint32_t kKmOutOfRange = 0x80000000u;
 constexpr int kKmRowBytes = 512;  // one staged K row: 256 bf16
@@ -429,7 +430,7 @@ template <int KIND>
 __device__ __forceinline__ void km_init_rows(KmOp& o, const void* base, int64_t ld, int col0,
                                              int n0, int N, const uint32_t* rowb, int rbeg,
                                              int rend) {
-  static_assert(KIND == kKR || KIND == kKG, "routed-row operand");
+  static_assert(KIND == kKR || KIND == kKRD || KIND == kKG, "routed-row operand");
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   o.r0 = make_rsrc_2g_km(base);
   o.ld2 = uint32_t(ld * 2);
@@ -474,7 +475,7 @@ __device__ __forceinline__ void km_issue(KmOp& o, int k0, v4u* lds) {
     }
 #pragma unroll
     for (int p = 0; p < geom::kLoads; ++p)
-      dma16<false>(o.r0, voff[p], 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
+      dma16<KIND == kKRD>(o.r0, voff[p], 0u, lds + STAGE * kStageChunks + (p * 8 + w) * 64);
     if (KIND == kKG) {
       // offsets of the next step; a next step that starts a new window reloads it (every
       // wave read its offsets from the old one at the previous issue, before the barrier
@@ -571,7 +572,7 @@ __device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* 
     const int l = threadIdx.x & 63;
     const int r = o.rbeg + k0 + geom::km_row(p, w, l);
     const uint32_t voff = r < o.rend ? __umul24(uint32_t(r), o.ld2) + o.off[p] : kKmOutOfRange;
-    dma16<false>(o.r0, voff, 0u, dst);
+    dma16<KIND == kKRD>(o.r0, voff, 0u, dst);
   }
 }
 

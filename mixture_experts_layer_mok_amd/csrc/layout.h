@@ -35,7 +35,9 @@ enum HdrWord : int {
   kHdrAbort = 5,       // set when a bounded wait expires; every loop exits
   kHdrFwdTiles = 6,    // fused forward: total tiles
   kHdrDrainTicket = 7, // fused forward: next drain work chunk
-  kHdrBwdTicket = 8,   // backward dH/dX kernel: next tile ticket
+  kHdrBwdTicket = 8,   // backward kernel: next ticket
+  kHdrBwdDhDone = 9,   // backward kernel: dH tiles done
+  kHdrBwdDxDone = 10,  // backward kernel: dX tiles done
   kHdrWords = 64
 };
 

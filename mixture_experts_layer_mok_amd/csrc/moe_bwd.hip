@@ -15,15 +15,15 @@
 // gfx950's transposing LDS reads: nothing is transposed in memory.  Each dW tile has one
 // owner and one K order (the expert's rows ascending): no atomics, bitwise reproducible.
 //
-// dH and dX share one persistent launch (tile tickets); the other steps are separate
-// kernels.  The gate/up pre-activations a, b come from the forward where it still holds
+// dH, dX, dW and the row sums back to token order run in one persistent launch (tickets);
+// the per-row offsets and the GEMM1 replay are launches before it.  The gate/up
+// pre-activations a, b come from the forward where it still holds
 // them and are recomputed otherwise (replay of GEMM1), following the reverse ring
 // traversal: after a fused forward the ring slots hold the last S minibatches (the dH
 // epilogue reads their a, b there), and only minibatches whose slot was recycled,
 // mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for the
 // backward writes a, b of every row, and nothing is replayed.
 #include <algorithm>
-#include <mutex>
 
 #include "tile_ops.h"
 
@@ -65,11 +65,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(BwdParams p) {
   const int R = int(p.P.hdr[kHdrR]);
   const int n_mb = int(p.P.hdr[kHdrNmb]);
   const bool x_ring = x_in_ring(p);
-  // counters of the dH/dX launch that follows on the same stream
+  // counters of the backward launch that follows on the same stream
   const int nc = p.n_mb_max * p.mt_max;
   for (int i = blockIdx.x * 256 + threadIdx.x; i < nc; i += gridDim.x * 256) p.P.bsync[i] = 0;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     p.P.hdr[kHdrBwdTicket] = 0;
+    p.P.hdr[kHdrBwdDhDone] = 0;
+    p.P.hdr[kHdrBwdDxDone] = 0;
     p.P.hdr[kHdrAbort] = 0;
   }
   for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256) {
@@ -158,7 +160,8 @@ __device__ __forceinline__ void dh_tile(const BwdParams& p, int g, int nt) {
 
 // dX tile (m-tile g, column tile nt): dx rows = [da | db] x [W_gate; W_up][e] (K = 2I over
 // the rows of W_gate, then W_up, read K-major), pushed to their pairs.  The da, db rows
-// come from dH tiles of the same launch, so they are read at device scope.
+// come from dH tiles of the same launch, so they are read at device scope, and the dx
+// rows are stored at device scope for the row sums of the same launch.
 __device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
   const int64_t K = 2 * int64_t(p.I);
   const int64_t wsz = int64_t(p.I) * p.D;
@@ -171,46 +174,15 @@ __device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
   km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
   TileAcc acc;
   tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
-  epi_scatter<false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
-}
-
-// dH and dX in one persistent launch.  Workgroups take tile tickets in order: first
-// every dH tile (m-tiles slowest), then every dX tile.  A dX tile of m-tile g waits until
-// the dH tiles of g have all signalled, so the last round of dH tiles shares the CUs with
-// the first dX tiles instead of leaving most of them idle.  Every dH ticket is taken
-// before any dX ticket and a dH tile waits for nothing, so each wait ends.  Waits are
-// bounded and every loop exits once the abort word is set.
-__global__ __launch_bounds__(512) void k_bwd_dhdx(BwdParams p) {
-  uint32_t* hdr = p.P.hdr;
-  uint32_t* hd = p.P.bsync;
-  const uint32_t mt = hdr[kHdrMtiles];
-  const uint32_t nh = mt * uint32_t(p.nNdh);
-  const uint32_t total = nh + mt * uint32_t(p.nDt);
-  __shared__ uint32_t s_tk;
-  while (true) {
-    if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrBwdTicket, 1u);
-    __syncthreads();
-    const uint32_t tk = __builtin_amdgcn_readfirstlane(s_tk);  // wave-uniform
-    __syncthreads();
-    if (tk >= total || aborted(hdr)) break;
-    if (tk < nh) {
-      const int g = int(tk) / p.nNdh;
-      dh_tile(p, g, int(tk) % p.nNdh);
-      wg_signal_add(hd + g, 1u);
-    } else {
-      const int q = int(tk - nh);
-      const int g = q / p.nDt;
-      if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
-      dx_tile(p, g, q % p.nDt);
-    }
-  }
+  epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
 }
 
 // dW GEMMs, K over the expert's routed rows in ascending order, both operands read
 // K-major as stored: per expert, dW_down tiles (D x I: A = dY rows gathered by perm,
 // B = g h rows), then dW_gate and dW_up tiles (I x D: A = da / db rows, B = X rows, from
-// the ring when it holds them all).  Rows past the expert's last read zero; an expert without rows
-// gets zero tiles.  One workgroup owns each tile: no atomics.
+// the ring when it holds them all).  g h, da and db come from dH tiles of the same
+// launch and are read at device scope.  Rows past the expert's last read zero; an expert
+// without rows gets zero tiles.  One workgroup owns each tile: no atomics.
 template <int AK, int BK>
 __device__ __forceinline__ void dw_tile(KmOp& a, KmOp& b, int nk, int rows, int n0, int N,
                                         float* C) {
@@ -219,11 +191,11 @@ __device__ __forceinline__ void dw_tile(KmOp& a, KmOp& b, int nk, int rows, int 
   epi_store_f32(acc, rows, n0, N, C, N);
 }
 
-__global__ __launch_bounds__(512) void k_bwd_dw(BwdParams p) {
+// dW tile q of nl * 3 * nDt * nIt: expert, then dW_down / dW_gate / dW_up, then tiles.
+__device__ __forceinline__ void dw_tile_at(const BwdParams& p, int q) {
   const int per = p.nDt * p.nIt;
-  const int e = blockIdx.x / (3 * per);
-  const int q = blockIdx.x % (3 * per);
-  const int which = q / per, r = q % per;
+  const int e = q / (3 * per);
+  const int which = (q % (3 * per)) / per, r = q % per;
   const int rbeg = p.P.offsets[e], rend = rbeg + p.P.counts[e];
   const int nk = (rend - rbeg + kBK - 1) / kBK;
   const int64_t wsz = int64_t(p.I) * p.D;
@@ -231,77 +203,107 @@ __global__ __launch_bounds__(512) void k_bwd_dw(BwdParams p) {
   if (which == 0) {  // dW_down[e][d][i] = sum_r dY[t_r][d] (g h)[r][i]
     const int m0 = (r / p.nIt) * kBM, n0 = (r % p.nIt) * kBN2;
     km_init_rows<kKG>(a, p.a.dy, p.D, 0, m0, p.D, p.P.dyb, rbeg, rend);
-    km_init_rows<kKR>(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
-    dw_tile<kKG, kKR>(a, b, nk, min(kBM, p.D - m0), n0, p.I, p.a.dwd + e * wsz + int64_t(m0) * p.I);
+    km_init_rows<kKRD>(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
+    dw_tile<kKG, kKRD>(a, b, nk, min(kBM, p.D - m0), n0, p.I, p.a.dwd + e * wsz + int64_t(m0) * p.I);
   } else {           // dW_gate / dW_up[e][i][d] = sum_r da / db[r][i] X[t_r][d]
     const int m0 = (r / p.nDt) * kBM, n0 = (r % p.nDt) * kBN2;
-    km_init_rows<kKR>(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr,
-                      rbeg, rend);
+    km_init_rows<kKRD>(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr,
+                       rbeg, rend);
     km_init_rows<kKG>(b, x_in_ring(p) ? static_cast<const void*>(p.P.ring) : p.a.x, p.D, 0, n0,
                       p.D, p.P.xb, rbeg, rend);
-    dw_tile<kKR, kKG>(a, b, nk, min(kBM, p.I - m0), n0, p.D,
-                      (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz + int64_t(m0) * p.D);
+    dw_tile<kKRD, kKG>(a, b, nk, min(kBM, p.I - m0), n0, p.D,
+                       (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz + int64_t(m0) * p.D);
   }
 }
 
-// ------------------------------------------------------------------------------------
-// reductions back to token order
-// ------------------------------------------------------------------------------------
-// dG[t, j] = sum over dH n-tiles (ascending) of the partials of row pos[t, j]; 0 if none.
-__global__ __launch_bounds__(256) void k_bwd_dg(BwdParams p) {
-  const int64_t TK = int64_t(p.T) * p.k;
-  for (int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x; q < TK; q += int64_t(gridDim.x) * 256) {
+// Tokens [c * kSumTokens, +kSumTokens): dX[t] = sum over local slots j (ascending) of the
+// dx row of pair t*k + j, fp32, rounded once (zero for a token without local slots), one
+// wave per token; dG[t, j] = sum over dH column tiles (ascending) of the partials of row
+// pos[t, j], 0 if none.  The dx rows and the partials come from tiles of the same launch:
+// device-scope reads.
+constexpr int kSumTokens = 32;
+__device__ __forceinline__ void sum_chunk(const BwdParams& p, int c) {
+  const int t0 = c * kSumTokens, t1 = min(t0 + kSumTokens, p.T);
+  for (int t = t0 + (threadIdx.x >> 6); t < t1; t += kThreads / 64)
+    wave_pair_sum<kCpolDev, 2>(p.a.dx + int64_t(t) * p.D, p.P.dxbuf, int64_t(t) * p.k, p.D,
+                               p.P.pos, nullptr, p.k);
+  for (int64_t q = int64_t(t0) * p.k + threadIdx.x; q < int64_t(t1) * p.k; q += kThreads) {
     const int r = p.P.pos[q];
     float s = 0.f;
     if (r >= 0)
-      for (int nt = 0; nt < p.nNdh; ++nt) s += p.P.dgpart[int64_t(r) * p.nNdh + nt];
+      for (int nt = 0; nt < p.nNdh; ++nt)
+        s += __uint_as_float(ld_relaxed(reinterpret_cast<const uint32_t*>(
+            p.P.dgpart + int64_t(r) * p.nNdh + nt)));
     p.a.dg[q] = s;
   }
 }
 
-// dX[t] = sum over local slots j (ascending) of dxbuf[t*k + j], fp32, rounded once
-// (zero for a token without local slots).
-__global__ __launch_bounds__(256) void k_bwd_dxsum(BwdParams p) {
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  for (int t = gw; t < p.T; t += nw)
-    wave_pair_sum<kCpolPlain, 2>(p.a.dx + int64_t(t) * p.D, p.P.dxbuf, int64_t(t) * p.k, p.D,
-                              p.P.pos, nullptr, p.k);
+// The backward GEMMs and row sums in one persistent launch (one workgroup per CU).
+// Workgroups take tickets in this order:
+//   1. every dH tile (m-tiles slowest);
+//   2. every dX tile; one of m-tile g waits until the dH tiles of g have signalled;
+//   3. the first two rounds of dW tiles; a workgroup's first dW tile waits until every
+//      dH tile has signalled;
+//   4. the row-sum chunks; a workgroup's first chunk waits until every dX tile has
+//      signalled (they were all taken before, and are done by now in the normal case);
+//   5. the remaining dW tiles.
+// Every wait is on work with smaller tickets, so each ends.  One ticket stream removes the
+// idle tails between the steps, and the dW epilogues (256 KB of fp32 stores a tile) no
+// longer start on every CU at once: the CUs reach their dW tiles at different times.
+// Waits are bounded and every loop exits once the abort word is set.
+__global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
+  uint32_t* hdr = p.P.hdr;
+  uint32_t* hd = p.P.bsync;
+  const uint32_t mt = hdr[kHdrMtiles];
+  const uint32_t nh = mt * uint32_t(p.nNdh);
+  const uint32_t nx = mt * uint32_t(p.nDt);
+  const uint32_t nw = uint32_t(p.nl) * 3u * uint32_t(p.nDt) * uint32_t(p.nIt);
+  const uint32_t ns = uint32_t((p.T + kSumTokens - 1) / kSumTokens);
+  const uint32_t w1 = min(nw, 2u * gridDim.x);
+  const uint32_t b_x = nh, b_w1 = b_x + nx, b_s = b_w1 + w1, b_w2 = b_s + ns;
+  const uint32_t total = b_w2 + (nw - w1);
+  bool dh_all = false, dx_all = false;
+  __shared__ uint32_t s_tk;
+  while (true) {
+    if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrBwdTicket, 1u);
+    __syncthreads();
+    const uint32_t tk = __builtin_amdgcn_readfirstlane(s_tk);  // wave-uniform
+    __syncthreads();
+    if (tk >= total || aborted(hdr)) break;
+    if (tk < b_x) {
+      const int g = int(tk) / p.nNdh;
+      dh_tile(p, g, int(tk) % p.nNdh);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        fetch_add_relaxed(hd + g, 1u);
+        fetch_add_relaxed(hdr + kHdrBwdDhDone, 1u);
+      }
+    } else if (tk < b_w1) {
+      const int q = int(tk - b_x);
+      const int g = q / p.nDt;
+      if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
+      dx_tile(p, g, q % p.nDt);
+      wg_signal_add(hdr + kHdrBwdDxDone, 1u);
+    } else if (tk >= b_s && tk < b_w2) {
+      if (!dx_all) {
+        if (!wg_wait_geq(hdr + kHdrBwdDxDone, nx, hdr, p.wait_ticks)) break;
+        dx_all = true;
+      }
+      sum_chunk(p, int(tk - b_s));
+    } else {
+      if (!dh_all) {
+        if (!wg_wait_geq(hdr + kHdrBwdDhDone, nh, hdr, p.wait_ticks)) break;
+        dh_all = true;
+      }
+      dw_tile_at(p, int(tk < b_s ? tk - b_w1 : w1 + (tk - b_w2)));
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
 // host
 // ------------------------------------------------------------------------------------
-// A side stream per device, with a fork and a join event: the dX row sum and the router-
-// weight gradient run on it beside the dW GEMMs.  They need no LDS and few registers, so
-// their workgroups fit next to a dW workgroup on a CU, and they move memory while dW
-// keeps the matrix cores busy.  Created on first use at the default priority and kept
-// until the process ends.  The enqueue sequence holds a lock, so that calls from several
-// host threads do not interleave their uses of the two events.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-constexpr int kMaxDevices = 64;
-static SideStream g_side[kMaxDevices];
-static std::mutex g_side_mu;
-
-static SideStream* side_stream_locked(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  if (ss.failed) return nullptr;
-  if (!ss.s) {
-    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
-      ss.failed = true;
-      return nullptr;
-    }
-  }
-  return &ss;
-}
-
 mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, hipStream_t st) {
   BwdParams p;
   p.P = P;
@@ -328,27 +330,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   hipLaunchKernelGGL(k_bwd_rows, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
                      dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_dhdx, tiles_grid, dim3(kThreads), 0, st, p);
-  const dim3 dg_grid(unsigned(std::min<int64_t>((L.TK + 255) / 256, 65536)));
-  const dim3 dxsum_grid(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20)));
-  const dim3 dw_grid(unsigned(L.nl * 3 * p.nDt * p.nIt));
-  {
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = side_stream_locked(dev);
-    if (ss && hipEventRecord(ss->fork, st) == hipSuccess &&
-        hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
-      hipLaunchKernelGGL(k_bwd_dg, dg_grid, dim3(256), 0, ss->s, p);
-      hipLaunchKernelGGL(k_bwd_dxsum, dxsum_grid, dim3(256), 0, ss->s, p);
-      hipLaunchKernelGGL(k_bwd_dw, dw_grid, dim3(kThreads), 0, st, p);
-      if (hipEventRecord(ss->join, ss->s) != hipSuccess ||
-          hipStreamWaitEvent(st, ss->join, 0) != hipSuccess)
-        return MOK_E_LAUNCH;
-    } else {
-      hipLaunchKernelGGL(k_bwd_dw, dw_grid, dim3(kThreads), 0, st, p);
-      hipLaunchKernelGGL(k_bwd_dg, dg_grid, dim3(256), 0, st, p);
-      hipLaunchKernelGGL(k_bwd_dxsum, dxsum_grid, dim3(256), 0, st, p);
-    }
-  }
+  hipLaunchKernelGGL(k_bwd_main, tiles_grid, dim3(kThreads), 0, st, p);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
 }
 

@@ -409,7 +409,8 @@ __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows
 // dgpart[row][nt] (lanes first, then the four column waves in order: a fixed summation
 // order).  Loads and stores go through buffer resources sized to the tile's rows, so
 // rows past the tile read zero and their stores are dropped.  kStPol is the cache policy
-// of the da, db stores (kCpolDev when the same launch reads them on other XCDs).
+// of the da, db, g h and dG-partial stores (kCpolDev when the same launch reads them on
+// other XCDs).
 template <int kStPol>
 __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, int n0, int I,
                                        const uint16_t* ab_tile, const float* gates,
@@ -474,7 +475,7 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(db), dab_res, voff,
                                                 so + uint32_t(I) * 2u, kStPol);
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * h), gh_res, goff,
-                                                r8 * uint32_t(I) * 2u, 0);
+                                                r8 * uint32_t(I) * 2u, kStPol);
         }
       }
     }
@@ -491,8 +492,15 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  for (int r = tid; r < rows; r += kThreads)
-    dgpart[int64_t(row0 + r) * nNdh + nt] = ((red[r] + red[256 + r]) + red[512 + r]) + red[768 + r];
+  for (int r = tid; r < rows; r += kThreads) {
+    const float v = ((red[r] + red[256 + r]) + red[512 + r]) + red[768 + r];
+    float* d = dgpart + int64_t(row0 + r) * nNdh + nt;
+    if (kStPol == kCpolDev)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(d), __float_as_uint(v), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *d = v;
+  }
   __syncthreads();
 }
 
