@@ -240,8 +240,10 @@ __device__ __forceinline__ void sum_chunk(const BwdParams& p, int c) {
 
 // The backward GEMMs and row sums in one persistent launch (one workgroup per CU).
 // Workgroups take tickets in this order:
-//   1. every dH tile (m-tiles slowest);
-//   2. every dX tile; one of m-tile g waits until the dH tiles of g have signalled;
+//   1. every dH tile, m-tiles slowest and in reverse row order: the last minibatch first,
+//      as the ring is walked backwards (its slots hold the most recent minibatches);
+//   2. every dX tile, m-tiles in the same order; one of m-tile g waits until the dH tiles
+//      of g have signalled;
 //   3. the first two rounds of dW tiles; a workgroup's first dW tile waits until every
 //      dH tile has signalled;
 //   4. the row-sum chunks; a workgroup's first chunk waits until every dX tile has
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
     __syncthreads();
     if (tk >= total || aborted(hdr)) break;
     if (tk < b_x) {
-      const int g = int(tk) / p.nNdh;
+      const int g = int(mt) - 1 - int(tk) / p.nNdh;
       dh_tile(p, g, int(tk) % p.nNdh);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
       }
     } else if (tk < b_w1) {
       const int q = int(tk - b_x);
-      const int g = q / p.nDt;
+      const int g = int(mt) - 1 - q / p.nDt;
       if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
       dx_tile(p, g, q % p.nDt);
       wg_signal_add(hdr + kHdrBwdDxDone, 1u);
