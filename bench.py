@@ -42,6 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_fused_c5_traffic.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "layer_c5_mfma_counters.txt")
 KERNEL_SOURCES = ("moe_fwd.hip", "tile_ops.h", "gemm_bf16.h", "gemm_mx.h", "mx.h", "tile_geom.h",
                   "device.h", "layout.h", "launch.h")
 
@@ -92,6 +93,22 @@ def read_traffic():
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def read_mfma_counters():
+    """Matrix-core busy fraction and shader clock of the fused forward from the committed
+    counter summary (None when absent or taken on other kernel sources)."""
+    try:
+        with open(MFMA_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_hash = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    m_busy = re.search(r"^k_fwd_fused_mfma_busy:\s*([0-9.]+)", text, re.M)
+    m_clk = re.search(r"^k_fwd_fused_clock_ghz:\s*([0-9.]+)", text, re.M)
+    if not (m_hash and m_busy and m_clk) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return {"mfma_busy": float(m_busy.group(1)), "clock_ghz": float(m_clk.group(1))}
 
 
 def copy_calibration():
@@ -178,6 +195,43 @@ def time_layer(cfg, t, layer, steps, warmup, with_bwd):
     if with_bwd:
         res["bwd_ms"] = [e[2].elapsed_time(e[3]) for e in evs]
     return res
+
+
+def time_cold(cfg, t, layer, steps, with_bwd):
+    """Per-phase times with the caches cold: before each step a 1 GiB buffer is written
+    (outside the timed phases), which evicts the weights and rows from the 256 MB
+    Infinity Cache and the L2s."""
+    import torch
+    stream = torch.cuda.current_stream()
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=t["x"].device)
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=t["x"].device)
+    fwd, bwd = [], []
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        layer.schedule(t["ids"])
+        ev[0].record(stream)
+        layer.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"],
+                      scales=(t.get("sg"), t.get("su"), t.get("sd")), y=y)
+        ev[1].record(stream)
+        if with_bwd:
+            scrub.fill_((i + 128) & 0xFF)
+            ev[2].record(stream)
+            layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
+            ev.append(torch.cuda.Event(enable_timing=True))
+            ev[3].record(stream)
+        torch.cuda.synchronize()
+        fwd.append(ev[0].elapsed_time(ev[1]))
+        if with_bwd:
+            bwd.append(ev[2].elapsed_time(ev[3]))
+    if layer.status() != 0:
+        raise SystemExit(f"device status {layer.status():#x} after the cold-cache steps")
+    del scrub
+    torch.cuda.empty_cache()
+    out = {"fwd_ms": stats(fwd)}
+    if with_bwd:
+        out["bwd_ms"] = stats(bwd)
+    return out
 
 
 def stats(v):
@@ -339,6 +393,14 @@ def main():
                        "forward (unfused launches)", "achieved": round(achieved, 2),
                        "peak": peak, "unit": "TFLOP/s",
                        "frac": round(achieved / peak, 4), "traffic": traffic}
+    mfma = read_mfma_counters() if traffic is not None else None
+    if mfma:
+        # the counters' view: matrix cores busy per shader cycle, and the clock the card ran
+        # at; peak_at_clock is the dense peak scaled to that clock
+        out["roofline"].update(mfma_busy=mfma["mfma_busy"], clock_ghz=mfma["clock_ghz"],
+                               peak_at_clock=round(peak * mfma["clock_ghz"] / 2.4, 1))
+    log("timing cold-cache steps (1 GiB scrub before each)")
+    out["cold_cache"] = time_cold(cfg, t, layer, min(args.steps, 5), with_bwd)
     if not mx and not args.no_mx and args.config == 5:
         out["mxfp8_fwd"] = mx_forward_figure(args)
     if not args.no_cpu_baseline:
