@@ -70,7 +70,7 @@ typedef enum {
 #define MOK_FLAG_UNFUSED 0x2u       /* run the same steps as separate kernels over
                                        full-size buffers (comparison / phase timing)     */
 #define MOK_FLAG_SHORT_WAITS 0x4u   /* bounded waits of the fused forward and of the
-                                       backward's dH/dX launch expire after 1 us instead
+                                       backward's persistent launch expire after 1 us instead
                                        of 2 s: the run sets MOK_DEV_TIMEOUT and exits
                                        early with its outputs undefined (tests the
                                        timeout path; never for production use)           */
