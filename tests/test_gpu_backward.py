@@ -123,17 +123,25 @@ def test_backward_outputs_ordered_on_caller_stream():
 
 
 def test_backward_config5_full_and_deterministic():
+    """Config 5 against the oracle, then ten forward + backward runs in all, each on a new
+    workspace, bitwise equal in Y and every gradient."""
     cfg = gen.CONFIGS[5]
     say("[c5] generating")
     d = gen.make_inputs(cfg, with_dy=True)
     dev = DevInputs(d)
-    _, g1, layer = run_fwd_bwd(cfg, dev)
+    y1, g1, layer = run_fwd_bwd(cfg, dev)
     assert layer.status() == 0
+    del layer
     say("[c5] oracle backward (float64)")
     _compare(cfg, d, d["ids"], g1, "c5")
-    _, g2, _ = run_fwd_bwd(cfg, dev)
-    for k in g1:
-        assert torch.equal(g1[k], g2[k]), k
+    for run in range(2, 11):
+        y, g, layer = run_fwd_bwd(cfg, dev)
+        assert layer.status() == 0
+        del layer
+        assert torch.equal(y1, y), f"y differs in run {run}"
+        for k in g1:
+            assert torch.equal(g1[k], g[k]), f"{k} differs in run {run}"
+    say("[c5] 10 runs bitwise identical")
 
 
 @pytest.mark.parametrize("cfg", SMALL[1:3], ids=lambda c: c.name)
