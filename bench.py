@@ -1,7 +1,8 @@
 """Benchmark of the MoE layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--M 2048] [--S 4]
-                    [--comm-cus C] [--unfused] [--fwd-only] [--no-cpu-baseline]
+                    [--comm-cus C] [--unfused] [--fwd-only] [--no-cpu-baseline] [--no-mx]
+                    [--no-cold]
     python bench.py --sweep            # minibatch x comm-CU sweep of the forward, JSON lines
     python bench.py --copy-calibration # one plain device copy of known size (counter scale)
     python bench.py --autotune [--autotune-cache F]  # tune M and comm CUs first, then time
@@ -60,6 +61,7 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--autotune", action="store_true",
                     help="choose M and comm CUs for this shape on the device before timing")
@@ -399,8 +401,9 @@ def main():
         # at; peak_at_clock is the dense peak scaled to that clock
         out["roofline"].update(mfma_busy=mfma["mfma_busy"], clock_ghz=mfma["clock_ghz"],
                                peak_at_clock=round(peak * mfma["clock_ghz"] / 2.4, 1))
-    log("timing cold-cache steps (1 GiB scrub before each)")
-    out["cold_cache"] = time_cold(cfg, t, layer, min(args.steps, 5), with_bwd)
+    if not args.no_cold:
+        log("timing cold-cache steps (1 GiB scrub before each)")
+        out["cold_cache"] = time_cold(cfg, t, layer, min(args.steps, 5), with_bwd)
     if not mx and not args.no_mx and args.config == 5:
         out["mxfp8_fwd"] = mx_forward_figure(args)
     if not args.no_cpu_baseline:

@@ -159,12 +159,29 @@ __global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
   epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
 }
 
+// One wave per token; the next token's slot rows and gates are loaded while this one is
+// summed, so that the per-token lookups do not add a memory round trip each.
 __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  auto load = [&](int t, int32_t& ps, float& g) {
+    const bool on = t < p.T && lane < p.k;
+    ps = on ? p.P.pos[int64_t(t) * p.k + lane] : -1;
+    g = on ? p.a.gates[int64_t(t) * p.k + lane] : 0.f;
+  };
+  int32_t ps_n;
+  float g_n;
+  load(gw, ps_n, g_n);
   for (int t = gw; t < p.T; t += nw) {
-    if (token_last_row(p.P.pos, t, p.k) >= 0) wave_combine_token<false>(p, t);
-    else wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
+    const int32_t ps = ps_n;
+    const float g = g_n;
+    load(t + nw, ps_n, g_n);
+    if (wave_max(ps) >= 0)
+      wave_pair_sum_loaded<kCpolPlain, 4>(p.a.y + int64_t(t) * p.D, p.P.obuf, int64_t(t) * p.k,
+                                          p.D, ps, g);
+    else
+      wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
   }
 }
 

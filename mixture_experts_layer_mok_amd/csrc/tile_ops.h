@@ -80,14 +80,15 @@ __device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
 }
 
+// The same with the slots' rows and gates already loaded: lane j < k holds my_pos =
+// pos[q0 + j] and my_g = gates[q0 + j] (1 without gates); other lanes -1 and 0.  A caller
+// that walks tokens loads the next token's values while this one is summed.
 template <int kPol, int kSlots>
-__device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* rows, int64_t q0,
-                                              int D, const int32_t* pos, const float* gates,
-                                              int k) {
+__device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16_t* rows,
+                                                     int64_t q0, int D, int32_t my_pos,
+                                                     float my_g) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t bytes = uint32_t(D) * 2;
-  const int32_t my_pos = int(lane) < k ? pos[q0 + lane] : -1;
-  const float my_g = int(lane) < k ? (gates ? gates[q0 + lane] : 1.0f) : 0.f;
   const uint64_t has = __ballot(my_pos >= 0);
   const rsrc_t ry = row_rsrc(dst, bytes);
   if (__popcll(has) == 1) {
@@ -143,6 +144,16 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
     for (int c = 0; c < kCombChunks; ++c)
       buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
   }
+}
+
+template <int kPol, int kSlots>
+__device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* rows, int64_t q0,
+                                              int D, const int32_t* pos, const float* gates,
+                                              int k) {
+  const int lane = threadIdx.x & 63;
+  const int32_t my_pos = lane < k ? pos[q0 + lane] : -1;
+  const float my_g = lane < k ? (gates ? gates[q0 + lane] : 1.0f) : 0.f;
+  wave_pair_sum_loaded<kPol, kSlots>(dst, rows, q0, D, my_pos, my_g);
 }
 
 // ------------------------------------------------------------------------------------
