@@ -81,12 +81,17 @@ __device__ __forceinline__ MxOperands mx_ops_gemm2(const FwdParams& p, const uin
 // combine
 // ------------------------------------------------------------------------------------
 // y[t] = sum_j gate_j * o[t*k+j] over the slots j with a local row, in ascending j
-// (wave_pair_sum).
-template <bool kCoherent>
-__device__ __forceinline__ void wave_combine_token(const FwdParams& p, int t) {
-  wave_pair_sum<kCoherent ? kCpolDev : kCpolPlain, 4>(p.a.y + int64_t(t) * p.D, p.P.obuf,
-                                                   int64_t(t) * p.k, p.D, p.P.pos, p.a.gates,
-                                                   p.k);
+// (wave_pair_sum_loaded).
+// Routed row r: combine its token if r is the token's last local row.  The token's slot
+// rows and gates are loaded together, once, for both the test and the sum.
+__device__ __forceinline__ void combine_if_last(const FwdParams& p, int r) {
+  const int lane = threadIdx.x & 63;
+  const int t = p.P.perm[r] / p.k;
+  const int64_t q0 = int64_t(t) * p.k;
+  const int32_t ps = lane < p.k ? p.P.pos[q0 + lane] : -1;
+  const float g = lane < p.k ? p.a.gates[q0 + lane] : 0.f;
+  if (wave_max(ps) == r)
+    wave_pair_sum_loaded<kCpolDev, 4>(p.a.y + q0 / p.k * p.D, p.P.obuf, q0, p.D, ps, g);
 }
 
 // ------------------------------------------------------------------------------------
@@ -290,10 +295,7 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
     if (mb >= p.S) {
       const int cm = mb - p.S;
       const int lo = p.P.mb_start[cm], hi = p.P.mb_start[cm + 1];
-      for (int r = lo + gw; r < hi; r += nw) {
-        const int t = p.P.perm[r] / p.k;
-        if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
-      }
+      for (int r = lo + gw; r < hi; r += nw) combine_if_last(p, r);
     }
   }
 }
@@ -365,10 +367,7 @@ __device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) 
     }
     const int lo = p.P.mb_start[cm] + int(tk - cbase) * kDrainRows;
     const int hi = min(p.P.mb_start[cm + 1], lo + kDrainRows);
-    for (int r = lo + w; r < hi; r += W) {
-      const int t = p.P.perm[r] / p.k;
-      if (token_last_row(p.P.pos, t, p.k) == r) wave_combine_token<true>(p, t);
-    }
+    for (int r = lo + w; r < hi; r += W) combine_if_last(p, r);
   }
 }
 
