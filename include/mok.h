@@ -74,6 +74,12 @@ typedef enum {
                                        of 2 s: the run sets MOK_DEV_TIMEOUT and exits
                                        early with its outputs undefined (tests the
                                        timeout path; never for production use)           */
+#define MOK_FLAG_PERTURB 0x8u       /* debug: before each cross-workgroup signal (a gathered
+                                       minibatch, a finished tile) and before each drain or
+                                       row-sum chunk, the workgroup sleeps for a pseudo-random
+                                       0-28 us.  Changes the interleaving of the persistent
+                                       kernels only: outputs must stay bitwise the same
+                                       (tests the handoffs for ordering races)           */
 
 /* sticky device status bits (mok_read_device_status) */
 #define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */

@@ -26,6 +26,7 @@ MOK_PREC_MXFP8 = 1
 MOK_FLAG_SAVE_FOR_BWD = 0x1
 MOK_FLAG_UNFUSED = 0x2
 MOK_FLAG_SHORT_WAITS = 0x4
+MOK_FLAG_PERTURB = 0x8
 MOK_DEV_BAD_ID = 0x1
 MOK_DEV_TIMEOUT = 0x2
 

@@ -164,4 +164,17 @@ __device__ __forceinline__ void wg_signal_add(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ bool aborted(const uint32_t* hdr) { return ld_relaxed(hdr + kHdrAbort) != 0; }
 
+// MOK_FLAG_PERTURB: a pseudo-random pause of 0-7 s_sleep(127) (about 4 us each) chosen
+// from `salt`, taken by every wave of the workgroup.  It shifts when a signal is
+// published or a chunk is taken, and so the interleaving of the workgroups, never what
+// is computed.
+__device__ __forceinline__ void perturb_pause(bool on, uint32_t salt) {
+  if (!on) return;
+  uint32_t h = salt * 0x9E3779B1u;
+  h ^= h >> 15;
+  h *= 0x85EBCA77u;
+  h ^= h >> 13;
+  for (uint32_t i = 0; i < (h & 7u); ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace mok

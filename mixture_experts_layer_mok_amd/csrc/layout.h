@@ -51,7 +51,7 @@ struct Layout {
   int64_t n_mb_max;  // ceil(T*k / M)
   int64_t mt_max;    // m-tiles per minibatch, upper bound
   int64_t nN1, nN2;  // n-tiles of GEMM1 (over I) and GEMM2 (over D)
-  bool mx, save, unfused, short_waits;
+  bool mx, save, unfused, short_waits, perturb;
   // MXFP8: bytes per scale row of the layer's own X and H buffers (one dword per 128-wide
   // K step), and of the weight scales the tiles read (the caller's K / 32 when K % 128
   // == 0, else a repacked copy in the workspace with the padded stride)
@@ -86,7 +86,8 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   if (D * I >= (int64_t(1) << 31)) return MOK_E_SHAPE;  // a weight matrix in 32-bit offsets
   if (d->comm_cus < 1) return MOK_E_SHAPE;
   if (d->precision != MOK_PREC_BF16 && d->precision != MOK_PREC_MXFP8) return MOK_E_UNSUPPORTED;
-  if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED | MOK_FLAG_SHORT_WAITS))
+  if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED | MOK_FLAG_SHORT_WAITS |
+                   MOK_FLAG_PERTURB))
     return MOK_E_UNSUPPORTED;
   L->T = T; L->D = D; L->I = I; L->E = E; L->k = k; L->e0 = e0; L->nl = nl; L->M = M; L->S = S;
   L->TK = T * k;
@@ -94,6 +95,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->save = (d->flags & MOK_FLAG_SAVE_FOR_BWD) != 0;
   L->unfused = (d->flags & MOK_FLAG_UNFUSED) != 0;
   L->short_waits = (d->flags & MOK_FLAG_SHORT_WAITS) != 0;
+  L->perturb = (d->flags & MOK_FLAG_PERTURB) != 0;
   if (L->mx && L->save) return MOK_E_UNSUPPORTED;  // MXFP8 backward is not built
   L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
   L->NS = L->NB * (kSchedChunk / kSchedSub);

@@ -39,6 +39,7 @@ struct BwdParams {
   int64_t slot_x;
   int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
+  int perturb;          // MOK_FLAG_PERTURB
 };
 
 // a, b of the rows of m-tile e in minibatch mb: in the ring slot while the minibatch is
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
     if (tk < b_x) {
       const int g = int(mt) - 1 - int(tk) / p.nNdh;
       dh_tile(p, g, int(tk) % p.nNdh);
+      perturb_pause(p.perturb, tk);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -286,12 +288,14 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
       const int g = int(mt) - 1 - q / p.nDt;
       if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
       dx_tile(p, g, q % p.nDt);
+      perturb_pause(p.perturb, tk);
       wg_signal_add(hdr + kHdrBwdDxDone, 1u);
     } else if (tk >= b_s && tk < b_w2) {
       if (!dx_all) {
         if (!wg_wait_geq(hdr + kHdrBwdDxDone, nx, hdr, p.wait_ticks)) break;
         dx_all = true;
       }
+      perturb_pause(p.perturb, tk);
       sum_chunk(p, int(tk - b_s));
     } else {
       if (!dh_all) {
@@ -323,6 +327,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.ring_2g = int64_t(L.S) * int64_t(L.slot_bytes) < (int64_t(1) << 31) ? 1 : 0;
   p.per_mt = int(L.nN1 + L.nN2);
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
+  p.perturb = L.perturb ? 1 : 0;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

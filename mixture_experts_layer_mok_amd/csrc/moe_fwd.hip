@@ -43,6 +43,7 @@ struct FwdParams {
   FwdArgs a;
   int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
+  int perturb;          // MOK_FLAG_PERTURB
   int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
   // MXFP8: scale row strides of X / H rows and of the weight scales the tiles read, and
   // those weight scales (the caller's, or repacked copies in the workspace)
@@ -291,6 +292,7 @@ __device__ __forceinline__ void comm_role(const FwdParams& p, int c, int C, uint
       if (!wg_wait_geq(done + (mb - p.S), mb_tiles2(mb - p.S), hdr, p.wait_ticks)) return;
     }
     gather_mb<MX>(p, mb, gw, nw);
+    perturb_pause(p.perturb, blockIdx.x * 7919u + uint32_t(mb));
     wg_signal_add(ready + mb, 1);
     if (mb >= p.S) {
       const int cm = mb - p.S;
@@ -353,6 +355,7 @@ __device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) 
     const uint32_t tk = s_tk;
     __syncthreads();
     if (aborted(hdr)) return;
+    perturb_pause(p.perturb, tk * 31u + blockIdx.x);
     if (tk < nz) {
       const int t1 = min(p.T, int(tk + 1) * kDrainTokens);
       for (int t = int(tk) * kDrainTokens + w; t < t1; t += W)
@@ -428,12 +431,14 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
         run_tile_mx<true>(true, o, e.y, n0, p.D, p.I, acc);
         epi_swiglu_mx<true>(acc, e.y, n0, p.I, slot + p.slot_h + int64_t(r0) * p.I, p.I,
                             slot + p.slot_hs + int64_t(r0) * p.hs_ld, p.hs_ld);
+        perturb_pause(p.perturb, tk);
         wg_signal_add(hd, 1);
       } else {
         const MxOperands o = mx_ops_gemm2(p, slot + p.slot_h + int64_t(r0) * p.I,
                                           slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
         run_tile_mx<true>(false, o, e.y, n0, p.D, p.I, acc);
         epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+        perturb_pause(p.perturb, tk);
         wg_signal_add(done + mb, 1);
       }
       continue;
@@ -448,9 +453,11 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
       uint16_t* ab = p.save ? reinterpret_cast<uint16_t*>(slot + p.slot_ab) + int64_t(r0) * 2 * p.I
                             : nullptr;
       epi_swiglu<true>(acc, e.y, n0, p.I, slot_h + int64_t(r0) * p.I, p.I, ab);
+      perturb_pause(p.perturb, tk);
       wg_signal_add(hd, 1);
     } else {
       epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+      perturb_pause(p.perturb, tk);
       wg_signal_add(done + mb, 1);
     }
   }
@@ -466,6 +473,7 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   if (p.P.hdr[kHdrNmb] > 0) {
     gather_mb<MX>(p, 0, blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6),
                   gridDim.x * (kThreads / 64));
+    perturb_pause(p.perturb, blockIdx.x);
     wg_signal_add(ready, 1);
   }
   if (int(blockIdx.x) < C) comm_role<MX>(p, blockIdx.x, C, ready, done);
@@ -498,6 +506,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.S = int(L.S); p.mt_max = int(L.mt_max); p.nN1 = int(L.nN1); p.nN2 = int(L.nN2);
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
+  p.perturb = L.perturb ? 1 : 0;
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
   p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
   p.slot_ab = int64_t(L.slot_ab);
