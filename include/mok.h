@@ -169,12 +169,10 @@ mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* t
  * same inputs.  Outputs: dx [T, D] bf16, d_topk_w [T, k] fp32 (0 for non-local slots),
  * dw_gate, dw_up [E_loc, I, D] fp32 and dw_down [E_loc, D, I] fp32 (overwritten, not
  * accumulated; experts with no rows get 0).  dW sums over rows run in a fixed order.
- * Asynchronous on stream: the dX row sum and d_topk_w run on an internal per-device
- * stream beside the dW GEMMs and are joined back to `stream` by an event, so all
- * outputs are complete when work enqueued later on `stream` starts.  dH and dX run as
- * one persistent launch whose waits are bounded: should one expire, the device status
- * gets MOK_DEV_TIMEOUT (mok_read_device_status) and the outputs are undefined; the
- * next mok_schedule clears the status. */
+ * Asynchronous on stream; every launch goes to `stream`.  dH, dX, dW and the sums back
+ * to token order run as one persistent launch whose waits are bounded: should one
+ * expire, the device status gets MOK_DEV_TIMEOUT (mok_read_device_status) and the
+ * outputs are undefined; the next mok_schedule clears the status. */
 mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
                          const int32_t* topk_ids, const float* topk_w, const void* w_gate,
                          const void* w_up, const void* w_down, void* dx, float* d_topk_w,
