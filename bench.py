@@ -6,6 +6,7 @@
     python bench.py --sweep            # minibatch x comm-CU sweep of the forward, JSON lines
     python bench.py --copy-calibration # one plain device copy of known size (counter scale)
     python bench.py --autotune [--autotune-cache F]  # tune M and comm CUs first, then time
+    python bench.py --trace [--config 4]  # in-kernel trace of the fused forward, decoded
 
 A step is one pass of the layer over one batch of synthetic input on one GPU's share of
 an expert-parallel layer (hidden 7168, expert intermediate 2048, 64 experts of which 8
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
+    ap.add_argument("--trace", action="store_true",
+                    help="one traced fused forward: print where its time went (JSON)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--autotune", action="store_true",
                     help="choose M and comm CUs for this shape on the device before timing")
@@ -305,6 +308,43 @@ def mx_forward_figure(args):
     return res
 
 
+def trace_forward(args):
+    """Warm-up forwards, then one forward with MOK_FLAG_TRACE on the same workload, decoded
+    into where the compute and data-mover workgroups spent the kernel's span."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+    from mixture_experts_layer_mok_amd import trace as TR
+    from mixture_experts_layer_mok_amd.layer import MoKLayer
+    cfg = gen.CONFIGS[args.config]
+    over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}
+    cfg = cfg.replace(**over)
+    dev = torch.device("cuda:0")
+    save = cfg.precision == L.MOK_PREC_BF16 and args.config == 5
+    d, t, layer = setup(cfg, False, save, dev)
+    flags = L.MOK_FLAG_TRACE | (L.MOK_FLAG_SAVE_FOR_BWD if save else 0)
+    tl = MoKLayer(L.desc_from_config(cfg, flags=flags), device=dev)
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev)
+    sc = (t.get("sg"), t.get("su"), t.get("sd"))
+    for _ in range(args.warmup + 1):
+        tl.schedule(t["ids"])
+        tl.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"], scales=sc, y=y)
+    torch.cuda.synchronize()
+    if tl.status() != 0:
+        raise SystemExit(f"device status {tl.status():#x}")
+    tab = tl.tables()
+    d_ = tl.desc
+    nN1 = (d_.intermediate + 127) // 128
+    nN2 = (d_.hidden + 255) // 256
+    tiles = tab["n_mtiles"] * (nN1 + nN2)
+    recs, wgs = TR.read(tl, tiles, L.mok_device_cus())
+    out = {"trace": TR.summarize(recs, wgs, cfg.comm_cus),
+           "config": {"workload": cfg.name, "routed_rows": tab["R"], "minibatch_rows": cfg.M,
+                      "ring_slots": cfg.S, "comm_cus": cfg.comm_cus, "tiles": int(tiles)}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -322,6 +362,9 @@ def main():
     L.load()
     if args.sweep:
         sweep(args)
+        return
+    if args.trace:
+        trace_forward(args)
         return
     cfg = gen.CONFIGS[args.config]
     over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}

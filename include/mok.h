@@ -80,6 +80,9 @@ typedef enum {
                                        0-28 us.  Changes the interleaving of the persistent
                                        kernels only: outputs must stay bitwise the same
                                        (tests the handoffs for ordering races)           */
+#define MOK_FLAG_TRACE 0x10u        /* the fused forward writes timestamps of every tile and
+                                       workgroup into a trace region of the workspace
+                                       (mok_trace_layout); fused forward only            */
 
 /* sticky device status bits (mok_read_device_status) */
 #define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */
@@ -178,6 +181,21 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
                          const void* w_up, const void* w_down, void* dx, float* d_topk_w,
                          float* dw_gate, float* dw_up, float* dw_down, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Where the trace of a forward run with MOK_FLAG_TRACE lies in the workspace (host
+ * only): *offset_bytes from the workspace start, *words uint32 words.  Timestamps are
+ * the low 32 bits of the GPU's 100 MHz constant clock (10 ns units).  The region holds
+ *   tile records, 8 words per tile ticket t (t < the number of forward tiles):
+ *     [workgroup, (minibatch << 1) | (1 for GEMM2, 0 for GEMM1), ticket taken,
+ *      inputs ready (its wait ended), K loop done, signal done (the tile's stores
+ *      complete and published), epilogue stores issued, 0];
+ *   then workgroup records, 8 words per workgroup w (w < MOK_TRACE_MAX_WORKGROUPS):
+ *     [start, minibatch 0 gathered (fill done), role done, drain done,
+ *      role (1 comm, 0 compute), drain chunks taken, 0, 0].
+ * The caller reads the region after the forward has completed.  Errors: MOK_E_NULL,
+ * the descriptor's errors, MOK_E_UNSUPPORTED when the flag is not set. */
+#define MOK_TRACE_MAX_WORKGROUPS 1024
+mok_status_t mok_trace_layout(const mok_desc_t* desc, size_t* offset_bytes, size_t* words);
 
 /* Synchronise `stream`, then read the sticky device status word (MOK_DEV_* bits). */
 mok_status_t mok_read_device_status(const void* ws, void* stream, uint32_t* out);

@@ -27,6 +27,8 @@ MOK_FLAG_SAVE_FOR_BWD = 0x1
 MOK_FLAG_UNFUSED = 0x2
 MOK_FLAG_SHORT_WAITS = 0x4
 MOK_FLAG_PERTURB = 0x8
+MOK_FLAG_TRACE = 0x10
+MOK_TRACE_MAX_WORKGROUPS = 1024
 MOK_DEV_BAD_ID = 0x1
 MOK_DEV_TIMEOUT = 0x2
 
@@ -34,7 +36,7 @@ MOK_DEV_TIMEOUT = 0x2
 EXPORTS = (
     "mok_workspace_size", "mok_schedule", "mok_schedule_tables", "mok_quantize_mx",
     "mok_moe_fwd", "mok_moe_bwd", "mok_read_device_status", "mok_status_string",
-    "mok_device_cus",
+    "mok_device_cus", "mok_trace_layout",
 )
 
 
@@ -88,6 +90,8 @@ def load() -> ctypes.CDLL:
         "mok_read_device_status": (ctypes.c_int, [vp, vp, ctypes.POINTER(ctypes.c_uint32)]),
         "mok_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mok_device_cus": (ctypes.c_int32, []),
+        "mok_trace_layout": (ctypes.c_int, [D, ctypes.POINTER(ctypes.c_size_t),
+                                            ctypes.POINTER(ctypes.c_size_t)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -199,3 +203,11 @@ def mok_read_device_status(ws, stream=None) -> int:
 
 def mok_device_cus() -> int:
     return int(load().mok_device_cus())
+
+
+def mok_trace_layout(desc: mok_desc_t) -> tuple[int, int]:
+    """(byte offset, uint32 words) of the trace region of a MOK_FLAG_TRACE workspace."""
+    off, words = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mok_trace_layout", load().mok_trace_layout(ctypes.byref(desc), ctypes.byref(off),
+                                                       ctypes.byref(words)))
+    return off.value, words.value

@@ -31,6 +31,17 @@ mok_status_t mok_workspace_size(const mok_desc_t* desc, size_t* bytes) {
   return MOK_OK;
 }
 
+mok_status_t mok_trace_layout(const mok_desc_t* desc, size_t* offset_bytes, size_t* words) {
+  if (!desc || !offset_bytes || !words) return MOK_E_NULL;
+  Layout L;
+  const mok_status_t s = make_layout(desc, &L);
+  if (s != MOK_OK) return s;
+  if (!L.trace) return MOK_E_UNSUPPORTED;
+  *offset_bytes = L.off_trace;
+  *words = L.trace_words;
+  return MOK_OK;
+}
+
 mok_status_t mok_schedule(const mok_desc_t* desc, const int32_t* topk_ids, void* ws,
                           size_t ws_bytes, void* stream) {
   if (!desc || !topk_ids) return MOK_E_NULL;

@@ -78,9 +78,9 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
 // at LDS address lds_wave_base + 16 * l (the wave-uniform base travels in M0).  COH adds
 // sc1 (device scope).
 template <bool COH>
-__device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t voff, uint32_t soff,
-                                      const v4u* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+__device__ __forceinline__ void dma16_at(const i32x4_t& rsrc, uint32_t voff, uint32_t soff,
+                                         uint32_t lds_wave_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_addr);
   soff = __builtin_amdgcn_readfirstlane(soff);  // uniform; kept in an SGPR for the asm
   if (COH)
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen sc1 lds" ::"v"(voff),
@@ -90,6 +90,11 @@ __device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t voff, uint32
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
                  "s"(rsrc), "s"(soff), "s"(m0)
                  : "memory", "m0");
+}
+template <bool COH>
+__device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t voff, uint32_t soff,
+                                      const v4u* lds_wave_base) {
+  dma16_at<COH>(rsrc, voff, soff, lds_addr(lds_wave_base));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -228,17 +233,18 @@ template <bool COH, int STAGE>
 __device__ __forceinline__ void tile_issue_sel(const TileSrc& s, int k0, int q, bool dummy) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t kb = uint32_t(k0) * 2;
-  const v4u* dst;
-  if (q < 4) dst = stage_a<STAGE>() + (q * 8 + w) * 64;
-  else dst = stage_b<STAGE>() + ((q - 4) * 8 + w) * 64;
-  dst = dummy ? g_lds_dummy + w * 64 : dst;
+  // the destination is selected as an LDS address (selecting generic pointers to LDS
+  // makes the compiler emit an invalid null check of the shared aperture)
+  uint32_t dst = q < 4 ? lds_addr(stage_a<STAGE>() + (q * 8 + w) * 64)
+                       : lds_addr(stage_b<STAGE>() + ((q - 4) * 8 + w) * 64);
+  dst = dummy ? lds_addr(g_lds_dummy) + uint32_t(w) * 1024u : dst;
   if (q < 4) {
-    dma16<COH>(s.ra, s.oa[q], kb, dst);
+    dma16_at<COH>(s.ra, s.oa[q], kb, dst);
   } else {
     const int p = q - 4;
     const bool paired_up = s.layout == geom::kPaired && ((w >> 1) & 1);
     const bool use_b1 = s.layout == geom::kPaired ? paired_up : (p >= 2);
-    dma16<false>(use_b1 ? s.rb1 : s.rb0, s.ob[p], kb, dst);
+    dma16_at<false>(use_b1 ? s.rb1 : s.rb0, s.ob[p], kb, dst);
   }
 }
 
@@ -561,18 +567,19 @@ template <int KIND, int STAGE>
 __device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* lds, bool dummy) {
   static_assert(KIND != kKG, "gathered operands are issued per step (km_issue)");
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const v4u* dst = dummy ? g_lds_dummy + w * 64 : lds + STAGE * kStageChunks + (p * 8 + w) * 64;
+  const uint32_t dst = dummy ? lds_addr(g_lds_dummy) + uint32_t(w) * 1024u
+                             : lds_addr(lds + STAGE * kStageChunks + (p * 8 + w) * 64);
   if (km_kcontig(KIND)) {
-    dma16<KIND == kKCD>(o.r0, o.off[p], uint32_t(k0) * 2, dst);
+    dma16_at<KIND == kKCD>(o.r0, o.off[p], uint32_t(k0) * 2, dst);
   } else if (KIND == kKW) {
     const bool second = k0 >= o.ksplit;
     const uint32_t so = uint32_t(second ? k0 - o.ksplit : k0) * o.ld2;
-    dma16<false>(second ? o.r1 : o.r0, o.off[p], so, dst);
+    dma16_at<false>(second ? o.r1 : o.r0, o.off[p], so, dst);
   } else {
     const int l = threadIdx.x & 63;
     const int r = o.rbeg + k0 + geom::km_row(p, w, l);
     const uint32_t voff = r < o.rend ? __umul24(uint32_t(r), o.ld2) + o.off[p] : kKmOutOfRange;
-    dma16<KIND == kKRD>(o.r0, voff, 0u, dst);
+    dma16_at<KIND == kKRD>(o.r0, voff, 0u, dst);
   }
 }
 

@@ -37,6 +37,7 @@ struct Ptrs {
   uint16_t* gh;       // [T*k, I] gate weight times h per routed row (dW_down operand)
   uint32_t* dyb;      // [T*k] byte offset of each routed row's dY row in dy
   uint32_t* xb;       // [T*k] byte offset of each routed row's X row (ring or x)
+  uint32_t* trace;    // MOK_FLAG_TRACE: tile records, then workgroup records; else null
 };
 
 inline Ptrs make_ptrs(const Layout& L, void* ws) {
@@ -71,6 +72,7 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.gh = u16(L.off_gh);
   P.dyb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_dyb) : nullptr;
   P.xb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_xb) : nullptr;
+  P.trace = L.trace ? reinterpret_cast<uint32_t*>(b + L.off_trace) : nullptr;
   return P;
 }
 

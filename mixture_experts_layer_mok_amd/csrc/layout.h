@@ -51,7 +51,7 @@ struct Layout {
   int64_t n_mb_max;  // ceil(T*k / M)
   int64_t mt_max;    // m-tiles per minibatch, upper bound
   int64_t nN1, nN2;  // n-tiles of GEMM1 (over I) and GEMM2 (over D)
-  bool mx, save, unfused, short_waits, perturb;
+  bool mx, save, unfused, short_waits, perturb, trace;
   // MXFP8: bytes per scale row of the layer's own X and H buffers (one dword per 128-wide
   // K step), and of the weight scales the tiles read (the caller's K / 32 when K % 128
   // == 0, else a repacked copy in the workspace with the padded stride)
@@ -67,6 +67,7 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
   size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
+  size_t off_trace, trace_words;  // MOK_FLAG_TRACE: tile records, then workgroup records
   size_t total;
 };
 
@@ -87,7 +88,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   if (d->comm_cus < 1) return MOK_E_SHAPE;
   if (d->precision != MOK_PREC_BF16 && d->precision != MOK_PREC_MXFP8) return MOK_E_UNSUPPORTED;
   if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED | MOK_FLAG_SHORT_WAITS |
-                   MOK_FLAG_PERTURB))
+                   MOK_FLAG_PERTURB | MOK_FLAG_TRACE))
     return MOK_E_UNSUPPORTED;
   L->T = T; L->D = D; L->I = I; L->E = E; L->k = k; L->e0 = e0; L->nl = nl; L->M = M; L->S = S;
   L->TK = T * k;
@@ -96,6 +97,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->unfused = (d->flags & MOK_FLAG_UNFUSED) != 0;
   L->short_waits = (d->flags & MOK_FLAG_SHORT_WAITS) != 0;
   L->perturb = (d->flags & MOK_FLAG_PERTURB) != 0;
+  L->trace = (d->flags & MOK_FLAG_TRACE) != 0;
   if (L->mx && L->save) return MOK_E_UNSUPPORTED;  // MXFP8 backward is not built
   L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
   L->NS = L->NB * (kSchedChunk / kSchedSub);
@@ -178,6 +180,12 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_gh = o; o = align_up(o + TK * I * 2, A);
     L->off_dyb = o; o = align_up(o + TK * 4, A);
     L->off_xb = o; o = align_up(o + TK * 4, A);
+  }
+  L->off_trace = L->trace_words = 0;
+  if (L->trace) {
+    L->trace_words = size_t(L->n_mb_max) * L->mt_max * (L->nN1 + L->nN2) * 8 +
+                     size_t(MOK_TRACE_MAX_WORKGROUPS) * 8;
+    L->off_trace = o; o = align_up(o + L->trace_words * 4, A);
   }
   L->total = o;
   return MOK_OK;

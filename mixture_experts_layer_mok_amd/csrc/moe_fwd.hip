@@ -44,6 +44,7 @@ struct FwdParams {
   int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int perturb;          // MOK_FLAG_PERTURB
+  int64_t trace_tiles;  // MOK_FLAG_TRACE: tile records before the workgroup records
   int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
   // MXFP8: scale row strides of X / H rows and of the weight scales the tiles read, and
   // those weight scales (the caller's, or repacked copies in the workspace)
@@ -327,6 +328,15 @@ __device__ __forceinline__ bool wait_done_range(const FwdParams& p, const uint32
   return true;
 }
 
+// MOK_FLAG_TRACE: low 32 bits of the 100 MHz constant clock, and one record of 8 words
+// written by thread 0 (the layout is documented with mok_trace_layout).
+__device__ __forceinline__ uint32_t trace_now() { return uint32_t(wall_clock64()); }
+__device__ __forceinline__ void trace_put(uint32_t* rec, uint32_t a, uint32_t b, uint32_t c,
+                                          uint32_t d, uint32_t e, uint32_t f, uint32_t g = 0) {
+  if (threadIdx.x != 0) return;
+  rec[0] = a; rec[1] = b; rec[2] = c; rec[3] = d; rec[4] = e; rec[5] = f; rec[6] = g; rec[7] = 0;
+}
+
 // Drain, run by every workgroup once its role is done, so that the compute CUs help with
 // the data movement left at the end.  Work comes in chunks from a ticket: first the
 // token chunks (y = 0 for tokens without a local row), then, minibatch by minibatch, the
@@ -336,7 +346,7 @@ __device__ __forceinline__ bool wait_done_range(const FwdParams& p, const uint32
 constexpr int kDrainTokens = 64;
 constexpr int kDrainRows = 8;  // one row per wave: the final combine spreads over every CU
 
-__device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) {
+__device__ __forceinline__ uint32_t drain(const FwdParams& p, const uint32_t* done) {
   uint32_t* hdr = p.P.hdr;
   const int n_mb = int(hdr[kHdrNmb]);
   const int w = threadIdx.x >> 6;
@@ -349,13 +359,15 @@ __device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) 
   int cm = max(0, n_mb - p.S);
   uint32_t cbase = nz;  // first ticket of minibatch cm's row chunks (tickets only grow)
   int waited = 0;       // minibatches [0, waited) are known to be done
+  uint32_t taken = 0;   // chunks this workgroup took (trace)
   while (true) {
     if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrDrainTicket, 1u);
     __syncthreads();
     const uint32_t tk = s_tk;
     __syncthreads();
-    if (aborted(hdr)) return;
+    if (aborted(hdr)) return taken;
     perturb_pause(p.perturb, tk * 31u + blockIdx.x);
+    ++taken;
     if (tk < nz) {
       const int t1 = min(p.T, int(tk + 1) * kDrainTokens);
       for (int t = int(tk) * kDrainTokens + w; t < t1; t += W)
@@ -363,9 +375,9 @@ __device__ __forceinline__ void drain(const FwdParams& p, const uint32_t* done) 
       continue;
     }
     while (cm < n_mb && tk >= cbase + chunks(cm)) cbase += chunks(cm++);
-    if (cm >= n_mb) return;
+    if (cm >= n_mb) return taken - 1;  // this ticket was past the last chunk
     if (waited <= cm) {
-      if (!wait_done_range(p, done, waited, cm)) return;
+      if (!wait_done_range(p, done, waited, cm)) return taken;
       waited = cm + 1;
     }
     const int lo = p.P.mb_start[cm] + int(tk - cbase) * kDrainRows;
@@ -384,6 +396,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
   __shared__ uint32_t s_ticket;
   const int L = p.S >= 2 ? 1 : 0;
   const uint32_t per_mt = uint32_t(p.nN1 + p.nN2);
+  const bool trace = p.P.trace != nullptr;
   // m-tiles in minibatches [0, i), and the first ticket of block j
   auto mt_before = [&](int i) {
     i = i < 0 ? 0 : (i > n_mb ? n_mb : i);
@@ -399,6 +412,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     const uint32_t tk = s_ticket;
     __syncthreads();
     if (tk >= total || aborted(hdr)) break;
+    const uint32_t t_tk = trace ? trace_now() : 0u;
     while (j + 1 < n_mb + L && block_start(j + 1) <= tk) ++j;
     const uint32_t q0 = tk - block_start(j);
     const uint32_t g1n = j < n_mb ? uint32_t(p.P.mt_cnt[j] * p.nN1) : 0u;
@@ -420,6 +434,9 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     } else {
       if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr, p.wait_ticks)) break;
     }
+    const uint32_t t_ready = trace ? trace_now() : 0u;
+    uint32_t* rec = trace ? p.P.trace + int64_t(tk) * 8 : nullptr;
+    const uint32_t kind = (uint32_t(mb) << 1) | (g1 ? 0u : 1u);
     const int4 e = p.P.mt_tab[int64_t(mb) * p.mt_max + i];
     const int r0 = e.x - lo;
     if (MX) {
@@ -429,17 +446,23 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
         const MxOperands o = mx_ops_gemm1(p, slot + p.slot_x + int64_t(r0) * p.D,
                                           slot + p.slot_xs + int64_t(r0) * p.xs_ld, e.z);
         run_tile_mx<true>(true, o, e.y, n0, p.D, p.I, acc);
+        const uint32_t t_k = trace ? trace_now() : 0u;
         epi_swiglu_mx<true>(acc, e.y, n0, p.I, slot + p.slot_h + int64_t(r0) * p.I, p.I,
                             slot + p.slot_hs + int64_t(r0) * p.hs_ld, p.hs_ld);
+        const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(hd, 1);
+        if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
       } else {
         const MxOperands o = mx_ops_gemm2(p, slot + p.slot_h + int64_t(r0) * p.I,
                                           slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
         run_tile_mx<true>(false, o, e.y, n0, p.D, p.I, acc);
+        const uint32_t t_k = trace ? trace_now() : 0u;
         epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+        const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(done + mb, 1);
+        if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
       }
       continue;
     }
@@ -449,17 +472,22 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     const int n0 = nt * (g1 ? kBN1 : kBN2);
     TileAcc acc;
     run_tile<true>(g1, A, e.y, w0, w1, n0, p.D, p.I, acc);
+    const uint32_t t_k = trace ? trace_now() : 0u;
+    uint32_t t_e = 0u;
     if (g1) {
       uint16_t* ab = p.save ? reinterpret_cast<uint16_t*>(slot + p.slot_ab) + int64_t(r0) * 2 * p.I
                             : nullptr;
       epi_swiglu<true>(acc, e.y, n0, p.I, slot_h + int64_t(r0) * p.I, p.I, ab);
+      t_e = trace ? trace_now() : 0u;
       perturb_pause(p.perturb, tk);
       wg_signal_add(hd, 1);
     } else {
       epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+      t_e = trace ? trace_now() : 0u;
       perturb_pause(p.perturb, tk);
       wg_signal_add(done + mb, 1);
     }
+    if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
   }
 }
 
@@ -469,6 +497,8 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
   const int C = p.a.comm_cus;
+  const bool trace = p.P.trace != nullptr && blockIdx.x < MOK_TRACE_MAX_WORKGROUPS;
+  const uint32_t t0 = trace ? trace_now() : 0u;
   // fill: every workgroup gathers part of minibatch 0
   if (p.P.hdr[kHdrNmb] > 0) {
     gather_mb<MX>(p, 0, blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6),
@@ -476,9 +506,14 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
     perturb_pause(p.perturb, blockIdx.x);
     wg_signal_add(ready, 1);
   }
+  const uint32_t t1 = trace ? trace_now() : 0u;
   if (int(blockIdx.x) < C) comm_role<MX>(p, blockIdx.x, C, ready, done);
   else compute_role<MX>(p, C, ready, done, hdone);
-  drain(p, done);
+  const uint32_t t2 = trace ? trace_now() : 0u;
+  const uint32_t nd = drain(p, done);
+  if (trace)
+    trace_put(p.P.trace + p.trace_tiles * 8 + int64_t(blockIdx.x) * 8, t0, t1, t2, trace_now(),
+              int(blockIdx.x) < C ? 1u : 0u, nd);
 }
 
 // Weight scales with a row stride of K / 32 bytes, repacked to the tile's stride of one
@@ -507,6 +542,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
+  p.trace_tiles = int64_t(L.n_mb_max) * L.mt_max * (L.nN1 + L.nN2);
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
   p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
   p.slot_ab = int64_t(L.slot_ab);

@@ -1,0 +1,86 @@
+"""Decoding of the fused forward's in-kernel trace (MOK_FLAG_TRACE).
+
+The kernel writes, per tile ticket, the workgroup, the GEMM and minibatch, and four
+timestamps (ticket taken, inputs ready, K loop done, signal done) plus the time its
+epilogue's stores were all issued, and per
+workgroup the start, the end of the minibatch-0 fill, the end of its role and of its
+drain (record layout in include/mok.h, mok_trace_layout).  Timestamps are the low 32 bits
+of the 100 MHz constant clock.  `summarize` turns one run's records into where the time of
+the compute and data-mover workgroups went, as shares of the kernel's span.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TICK_US = 0.01  # 100 MHz
+
+
+def read(layer, tiles: int, cus: int) -> tuple[np.ndarray, np.ndarray]:
+    """Tile records [tiles, 8] and workgroup records [cus, 8] (uint32) of the last traced
+    forward on `layer` (a MoKLayer built with MOK_FLAG_TRACE); synchronises."""
+    import torch
+
+    from . import _lib as L
+    off, words = L.mok_trace_layout(layer.desc)
+    torch.cuda.synchronize(layer.device)
+    raw = layer.ws[off:off + words * 4].cpu().numpy().view(np.uint32)
+    d = layer.desc
+    nb = (d.num_tokens * d.top_k + d.minibatch_rows - 1) // d.minibatch_rows
+    tile_cap = (words - L.MOK_TRACE_MAX_WORKGROUPS * 8) // 8
+    assert tile_cap >= tiles and nb >= 1
+    return raw[:tiles * 8].reshape(tiles, 8).copy(), \
+        raw[tile_cap * 8:tile_cap * 8 + cus * 8].reshape(cus, 8).copy()
+
+
+def summarize(tiles: np.ndarray, wgs: np.ndarray, comm_cus: int) -> dict:
+    t0 = int(wgs[:, 0].min())
+
+    def rel(x):
+        return (x.astype(np.int64) - t0) & 0xFFFFFFFF  # ticks since the kernel start
+
+    start, fill, role, drain = (rel(wgs[:, i]) for i in range(4))
+    span = float(drain.max())
+    comp = np.arange(len(wgs)) >= comm_cus
+    wg = tiles[:, 0].astype(np.int64)
+    g2 = (tiles[:, 1] & 1).astype(bool)
+    t_tk, t_rd, t_k, t_end = (rel(tiles[:, i]) for i in range(2, 6))
+    t_e = rel(tiles[:, 6])
+    wait, kloop, epi = t_rd - t_tk, t_k - t_rd, t_end - t_k
+    epi_issue, signal = t_e - t_k, t_end - t_e
+    n_comp = int(comp.sum())
+    tot = span * n_comp
+    # per compute workgroup: time between its fill and its role end not inside a tile
+    inside = np.zeros(len(wgs))
+    np.add.at(inside, wg, (t_end - t_tk).astype(float))
+    fill_c = float((fill[comp] - start[comp]).sum())
+    role_c = float((role[comp] - fill[comp]).sum())
+    between = role_c - float(inside[comp].sum())
+    after = float((span - role[comp]).sum())  # drain and the idle end
+    us = lambda v: round(float(v) * TICK_US, 2)  # noqa: E731
+    out = {
+        "span_us": us(span),
+        "compute_cus": n_comp,
+        "compute_share": {
+            "k_loop": round(float(kloop.sum()) / tot, 4),
+            "epilogue_and_signal": round(float(epi.sum()) / tot, 4),
+            "wait_for_inputs": round(float(wait.sum()) / tot, 4),
+            "between_tiles": round(between / tot, 4),
+            "fill": round(fill_c / tot, 4),
+            "after_role": round(after / tot, 4),
+        },
+        "tile_us": {
+            name: {"n": int(m.sum()), "k_loop": us(kloop[m].mean()), "epilogue": us(epi[m].mean()),
+                   "epilogue_issue": us(epi_issue[m].mean()),
+                   "store_drain_and_signal": us(signal[m].mean()), "wait": us(wait[m].mean())}
+            for name, m in (("gemm1", ~g2), ("gemm2", g2)) if m.any()},
+        "first_tile_us": us(t_tk.min()),
+        "last_tile_end_us": us(t_end.max()),
+    }
+    if comm_cus > 0:
+        cm = ~comp
+        out["comm"] = {"fill_us": us((fill[cm] - start[cm]).mean()),
+                       "role_us": us((role[cm] - fill[cm]).mean()),
+                       "drain_us": us((drain[cm] - role[cm]).mean()),
+                       "drain_chunks": int(wgs[cm, 5].sum())}
+    out["drain_chunks_compute"] = int(wgs[comp, 5].sum())
+    return out

@@ -110,3 +110,17 @@ def test_entry_points_fail_before_touching_memory():
     assert lib.mok_moe_bwd(dp, *bw, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOK_E_NULL
     assert lib.mok_moe_bwd(dp, *bw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small, None) == \
         L.MOK_E_WORKSPACE
+
+
+def test_trace_layout():
+    """The trace region exists only with MOK_FLAG_TRACE, lies inside the workspace, and
+    holds 8 words per possible forward tile plus 8 per workgroup."""
+    with pytest.raises(L.MokError) as e:
+        L.mok_trace_layout(_desc())
+    assert e.value.code == L.MOK_E_UNSUPPORTED
+    d = _desc(flags=L.MOK_FLAG_TRACE)
+    off, words = L.mok_trace_layout(d)
+    total = L.mok_workspace_size(d)
+    assert off % 256 == 0 and off + words * 4 <= total
+    assert total > L.mok_workspace_size(_desc())
+    assert words > L.MOK_TRACE_MAX_WORKGROUPS * 8 and (words - L.MOK_TRACE_MAX_WORKGROUPS * 8) % 8 == 0
