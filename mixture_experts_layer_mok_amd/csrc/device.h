@@ -117,6 +117,10 @@ __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint64_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(v2u_t{uint32_t(v), uint32_t(v >> 32)}, r, off, 0, CPOL);
 }
 template <int CPOL>
+__device__ __forceinline__ void buf_st4(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CPOL);
+}
+template <int CPOL>
 __device__ __forceinline__ void buf_st1(rsrc_t r, uint32_t off, uint8_t v) {
   __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, CPOL);
 }

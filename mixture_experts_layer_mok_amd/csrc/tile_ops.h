@@ -8,6 +8,15 @@
 
 namespace mok {
 
+// One of the two tile stages as an LDS (address space 3) pointer: selecting between the
+// stage arrays as integers avoids generic-pointer selects, for which the compiler can
+// emit an invalid null check of the shared aperture.
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) const uint64_t lds_cu64_t;
+__device__ __forceinline__ lds_u16_t* stage16(bool second) {
+  return reinterpret_cast<lds_u16_t*>(uintptr_t(second ? lds_addr(g_lds_b) : lds_addr(g_lds_a)));
+}
+
 // ------------------------------------------------------------------------------------
 // wave-level data movement
 // ------------------------------------------------------------------------------------
@@ -187,10 +196,8 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
   const int rbit = lane >> 5;  // bit 2 of every row this lane holds
   const int l32 = lane & 31, half = lane >> 5;
   const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
-  uint16_t* st = reinterpret_cast<uint16_t*>(w >> 2 ? g_lds_b : g_lds_a);
-  auto stage_row = [](int r) {
-    return reinterpret_cast<const uint16_t*>(r >> 7 ? g_lds_b : g_lds_a);
-  };
+  lds_u16_t* st = stage16(w >> 2);
+  auto stage_row = [](int r) { return stage16(r >> 7); };
   if (AB) {
     // rows of 256 columns: gate 0..127, up 128..255
     const int sw = ((gate_lane ? 0 : 2) | rbit) << 4;
@@ -211,7 +218,7 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
     for (int k = 0; k < kRows; ++k) {
       const int r = wr + W * k;
       const int c = (4 * l32 + 128 * half) ^ (((half << 1) | ((r >> 2) & 1)) << 4);
-      val[k] = *reinterpret_cast<const uint64_t*>(stage_row(r) + (r & 127) * 256 + c);
+      val[k] = *reinterpret_cast<lds_cu64_t*>(stage_row(r) + (r & 127) * 256 + c);
     }
     const rsrc_t rab = row_rsrc(AB, uint32_t(rows) * uint32_t(2 * I) * 2u);
     const uint32_t coff = uint32_t((half ? I : 0) + n0 + 4 * l32) * 2u;
@@ -224,17 +231,27 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
     __syncthreads();
   }
   if (H) {
-    // rows of 128 columns (gate lanes form h)
+    // rows of 128 columns.  A gate lane and its up lane (l ^ 16) split the 16 rows of
+    // their column: one gfx950 v_permlane16_swap per row pair hands the up lane's value
+    // of row v to the gate lane and the gate lane's value of row v + 8 to the up lane,
+    // so that every lane forms 8 of the h values (rows v and v + 8 lie 16 tile rows
+    // apart).  Staged columns are XOR-swizzled by 16 on bit 2 of the row and by 8 on
+    // bit 4, so the two lanes of a pair and the two half-waves hit different banks.
+    const int cl = 16 * (2 * wn) + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int c = (16 * (2 * wn + j) + (lane & 15)) ^ (rbit << 4);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float x = acc.c[i][j][v];
-          const float y = __shfl_xor(x, 16);
-          if (gate_lane) st[(acc_row(tid, i, v) & 127) * 128 + c] = f32_to_bf16(silu_f(x) * y);
+        for (int v = 0; v < 8; ++v) {
+          const float xa = acc.c[i][j][v], xb = acc.c[i][j][v + 8];
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xa),
+                                                           __float_as_uint(xb), false, false);
+          const float g = gate_lane ? xa : __uint_as_float(sw[0]);
+          const float u = gate_lane ? __uint_as_float(sw[1]) : xb;
+          const int r = acc_row(tid, i, v) + (gate_lane ? 0 : 16);
+          const int c = (cl + 16 * j) ^ (rbit << 4) ^ (((r >> 4) & 1) << 3);
+          st[(r & 127) * 128 + c] = f32_to_bf16(silu_f(g) * u);
         }
       }
     __syncthreads();
@@ -244,8 +261,8 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
 #pragma unroll
     for (int k = 0; k < kPairs; ++k) {
       const int r = 2 * (wr + W * k) + half;
-      const int c = (4 * l32) ^ (((r >> 2) & 1) << 4);
-      val[k] = *reinterpret_cast<const uint64_t*>(stage_row(r) + (r & 127) * 128 + c);
+      const int c = (4 * l32) ^ (((r >> 2) & 1) << 4) ^ (((r >> 4) & 1) << 3);
+      val[k] = *reinterpret_cast<lds_cu64_t*>(stage_row(r) + (r & 127) * 128 + c);
     }
     const rsrc_t rh = row_rsrc(H, uint32_t(rows) * uint32_t(ldh) * 2u);
     const uint32_t coff = uint32_t(n0 + 4 * l32) * 2u;
@@ -275,7 +292,7 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
   const int w = tid >> 6;
   const int wn = w & 3;
   {
-    uint16_t* st = reinterpret_cast<uint16_t*>(w >> 2 ? g_lds_b : g_lds_a);
+    lds_u16_t* st = stage16(w >> 2);
     const int swz = (lane >> 5) << 5;  // bit 2 of every row this lane holds
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -302,8 +319,8 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
     const int r = wr + (kThreads / 64) * k;
-    val[k] = *reinterpret_cast<const uint64_t*>(
-        reinterpret_cast<const uint16_t*>(r >> 7 ? g_lds_b : g_lds_a) + (r & 127) * 256 +
+    val[k] = *reinterpret_cast<lds_cu64_t*>(
+        stage16(r >> 7) + (r & 127) * 256 +
         ((4 * lane) ^ (((r >> 2) & 1) << 5)));
   }
   const uint32_t row_bytes = uint32_t(D) * 2u;
@@ -320,50 +337,84 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
 
 // Epilogue of the MXFP8 GEMM1: SwiGLU as in epi_swiglu, then H is MX-quantised along I.
 // A 32-column MX block [n0 + 32 wn, +32) is exactly MFMA blocks j = 0, 1 of wave column
-// wn: for one row, the 16 gate lanes of a DPP row hold its 32 h values (two per lane),
-// so the block maximum is a 16-lane DPP reduction.  Writes codes Hc[row * ldh + col] and
-// scales Hs[row * hs_ld + col / 32].  I is a multiple of 32, so a block is wholly inside
-// or outside [0, I).
+// wn.  As in epi_swiglu, a gate lane and its up lane (l ^ 16) split the rows of their
+// column with one v_permlane16_swap per row pair and value block, so each 16-lane DPP
+// row then holds the 32 h values of one tile row's MX block (two per lane): the block
+// maximum is a 16-lane DPP reduction.  The codes and scales are staged in LDS (codes of
+// row r at byte r * 128, XOR-swizzled by 32 on bit 2 and by 64 on bit 4 of the row so
+// the four lane groups of a write hit different banks; scales after them), then written
+// as 128-byte row segments, 4 bytes a lane, and one byte per row and block.  Writes codes
+// Hc[row * ldh + col] and scales Hs[row * hs_ld + col / 32]; I is a multiple of 32, so a
+// block is wholly inside or outside [0, I).  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int n0, int I,
                                               uint8_t* Hc, int64_t ldh, uint8_t* Hs,
                                               int64_t hs_ld) {
+  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int W = kThreads / 64;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+  typedef __attribute__((address_space(3))) const uint32_t lds_cu32_t;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
+  const int w = tid >> 6;
+  const int wn = w & 3;
   const bool gate_lane = (lane & 16) == 0;
-  const int cb = n0 + 32 * wn;
-  if (cb >= I) return;  // wave-uniform
+  lds_u8_t* sc = reinterpret_cast<lds_u8_t*>(uintptr_t(lds_addr(g_lds_a)));  // [256][128]
+  lds_u8_t* ss = sc + 256 * 128;                                              // [256][4]
+  auto swz = [](int r) { return (((r >> 2) & 1) << 5) | (((r >> 4) & 1) << 6); };
+  if (n0 + 32 * wn < I) {  // wave-uniform
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float x0 = acc.c[i][0][v], x1 = acc.c[i][1][v];
-      const float y0 = __shfl_xor(x0, 16), y1 = __shfl_xor(x1, 16);
-      const float h0 = silu_f(x0) * y0, h1 = silu_f(x1) * y1;
-      const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
-      const int n = mx_shared_exp(amax);
-      const int row = acc_row(tid, i, v);
-      if (row < rows && gate_lane) {
+      for (int v = 0; v < 8; ++v) {
+        const auto s0 = __builtin_amdgcn_permlane16_swap(
+            __float_as_uint(acc.c[i][0][v]), __float_as_uint(acc.c[i][0][v + 8]), false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(
+            __float_as_uint(acc.c[i][1][v]), __float_as_uint(acc.c[i][1][v + 8]), false, false);
+        const float g0 = gate_lane ? acc.c[i][0][v] : __uint_as_float(s0[0]);
+        const float u0 = gate_lane ? __uint_as_float(s0[1]) : acc.c[i][0][v + 8];
+        const float g1 = gate_lane ? acc.c[i][1][v] : __uint_as_float(s1[0]);
+        const float u1 = gate_lane ? __uint_as_float(s1[1]) : acc.c[i][1][v + 8];
+        const float h0 = silu_f(g0) * u0, h1 = silu_f(g1) * u1;
+        const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+        const int n = mx_shared_exp(amax);
         const uint32_t cc = e4m3x2(ldexpf(h0, -n), ldexpf(h1, -n));
-        const uint8_t c0 = uint8_t(cc), c1 = uint8_t(cc >> 8);
-        uint8_t* hr = Hc + int64_t(row) * ldh + cb + (lane & 15);
-        if (kCoherent) {
-          st_dev_u8(hr, c0);
-          st_dev_u8(hr + 16, c1);
-        } else {
-          hr[0] = c0;
-          hr[16] = c1;
-        }
-        if ((lane & 15) == 0) {
-          uint8_t* sp = Hs + int64_t(row) * hs_ld + (cb >> 5);
-          if (kCoherent) st_dev_u8(sp, uint8_t(n + 127));
-          else *sp = uint8_t(n + 127);
-        }
+        const int r = (acc_row(tid, i, v) + (gate_lane ? 0 : 16)) & 255;
+        const int c = (32 * wn + (lane & 15)) ^ swz(r);
+        sc[r * 128 + c] = uint8_t(cc);
+        sc[r * 128 + (c ^ 16)] = uint8_t(cc >> 8);
+        if ((lane & 15) == 0) ss[r * 4 + wn] = uint8_t(n + 127);
       }
+      __builtin_amdgcn_sched_barrier(0);  // one block row at a time: few live registers
     }
-    __builtin_amdgcn_sched_barrier(0);  // one block row at a time: few live registers
   }
+  __syncthreads();
+  // wave w: row pairs w, w + 8, ..; lanes 0..31 write row 2p, lanes 32..63 row 2p + 1
+  // (one resource for the tile's rows: a buffer resource's base is wave-uniform, and the
+  // two half-waves write different rows)
+  const int half = lane >> 5, l32 = lane & 31;
+  const bool col_ok = n0 + 4 * l32 < I;  // I % 32 == 0: a 4-column group is all in or out
+  const rsrc_t rh = row_rsrc(Hc, uint32_t(rows) * uint32_t(ldh));
+  const int wr = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll 4
+  for (int k = 0; k < 128 / W; ++k) {
+    const int r = 2 * (wr + W * k) + half;
+    if (2 * (wr + W * k) >= rows) break;  // wave-uniform; the odd row is checked below
+    if (r < rows && col_ok) {
+      const uint32_t val = *reinterpret_cast<lds_cu32_t*>(sc + r * 128 + ((4 * l32) ^ swz(r)));
+      buf_st4<kPol>(rh, uint32_t(r) * uint32_t(ldh) + uint32_t(n0 + 4 * l32), val);
+    }
+  }
+  if (tid < rows) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (n0 + 32 * b >= I) break;
+      uint8_t* sp = Hs + int64_t(tid) * hs_ld + ((n0 + 32 * b) >> 5);
+      if (kCoherent) st_dev_u8(sp, ss[tid * 4 + b]);
+      else *sp = ss[tid * 4 + b];
+    }
+  }
+  __syncthreads();
 }
 
 // MXFP8 operands of one tile of either GEMM:
