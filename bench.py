@@ -342,6 +342,16 @@ def trace_forward(args):
     out = {"trace": TR.summarize(recs, wgs, cfg.comm_cus),
            "config": {"workload": cfg.name, "routed_rows": tab["R"], "minibatch_rows": cfg.M,
                       "ring_slots": cfg.S, "comm_cus": cfg.comm_cus, "tiles": int(tiles)}}
+    if save:
+        # the backward's persistent launch, traced on the same workspace (its records
+        # replace the forward's)
+        tl.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
+        torch.cuda.synchronize()
+        if tl.status() != 0:
+            raise SystemExit(f"device status {tl.status():#x} after the backward")
+        n = TR.bwd_tickets(d_, tab["n_mtiles"])
+        brecs, bwgs = TR.read(tl, n, L.mok_device_cus())
+        out["trace_backward"] = TR.summarize_bwd(brecs, bwgs)
     print(json.dumps(out), flush=True)
 
 

@@ -80,9 +80,10 @@ typedef enum {
                                        0-28 us.  Changes the interleaving of the persistent
                                        kernels only: outputs must stay bitwise the same
                                        (tests the handoffs for ordering races)           */
-#define MOK_FLAG_TRACE 0x10u        /* the fused forward writes timestamps of every tile and
+#define MOK_FLAG_TRACE 0x10u        /* the fused forward and the backward's persistent
+                                       launch write timestamps of every ticket and
                                        workgroup into a trace region of the workspace
-                                       (mok_trace_layout); fused forward only            */
+                                       (mok_trace_layout)                                */
 
 /* sticky device status bits (mok_read_device_status) */
 #define MOK_DEV_BAD_ID 0x1u   /* an id was < -1 or >= E; that pair was skipped          */
@@ -192,6 +193,11 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
  *   then workgroup records, 8 words per workgroup w (w < MOK_TRACE_MAX_WORKGROUPS):
  *     [start, minibatch 0 gathered (fill done), role done, drain done,
  *      role (1 comm, 0 compute), drain chunks taken, 0, 0].
+ * The backward's records (which replace the forward's) use the same layout: per ticket
+ *   [workgroup, kind (0 dH, 1 dX, 2 dW tile, 3 row-sum chunk), ticket taken, inputs
+ *    ready, K loop (or sum) done, end, 0, 0], per workgroup [start, start, end, end, 0,
+ *   tickets taken, 0, 0].  The region holds as many ticket records as the larger of the
+ *   two launches has tickets.
  * The caller reads the region after the forward has completed.  Errors: MOK_E_NULL,
  * the descriptor's errors, MOK_E_UNSUPPORTED when the flag is not set. */
 #define MOK_TRACE_MAX_WORKGROUPS 1024

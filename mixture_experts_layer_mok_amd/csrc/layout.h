@@ -67,7 +67,8 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
   size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
-  size_t off_trace, trace_words;  // MOK_FLAG_TRACE: tile records, then workgroup records
+  size_t off_trace, trace_words, trace_tickets;  // MOK_FLAG_TRACE: ticket records, then
+                                                // workgroup records
   size_t total;
 };
 
@@ -181,10 +182,16 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_dyb = o; o = align_up(o + TK * 4, A);
     L->off_xb = o; o = align_up(o + TK * 4, A);
   }
-  L->off_trace = L->trace_words = 0;
+  L->off_trace = L->trace_words = L->trace_tickets = 0;
   if (L->trace) {
-    L->trace_words = size_t(L->n_mb_max) * L->mt_max * (L->nN1 + L->nN2) * 8 +
-                     size_t(MOK_TRACE_MAX_WORKGROUPS) * 8;
+    // records for every forward tile ticket, or every backward ticket (dH, dX, dW tiles
+    // and row-sum chunks of 32 tokens), whichever is more
+    const size_t nDt = size_t((D + kBN2 - 1) / kBN2), nIt = size_t((I + kBN2 - 1) / kBN2);
+    const size_t fwd = size_t(L->n_mb_max) * L->mt_max * (L->nN1 + L->nN2);
+    const size_t bwd = size_t(L->n_mb_max) * L->mt_max * (nIt + nDt) + size_t(nl) * 3 * nDt * nIt +
+                       size_t((T + 31) / 32);
+    L->trace_tickets = fwd > bwd ? fwd : bwd;
+    L->trace_words = L->trace_tickets * 8 + size_t(MOK_TRACE_MAX_WORKGROUPS) * 8;
     L->off_trace = o; o = align_up(o + L->trace_words * 4, A);
   }
   L->total = o;

@@ -40,6 +40,7 @@ struct BwdParams {
   int per_mt;    // forward tiles per m-tile (GEMM1 + GEMM2 column tiles): tile_base unit
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int perturb;          // MOK_FLAG_PERTURB
+  int64_t trace_tickets; // MOK_FLAG_TRACE: ticket records before the workgroup records
 };
 
 // a, b of the rows of m-tile e in minibatch mb: in the ring slot while the minibatch is
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
 // dH tile (m-tile g, column tile nt): u = dY rows x W_down[e] (K = D over the rows of
 // W_down, read K-major), fused SwiGLU backward and dG partials.  da, db are stored at
 // device scope: dX tiles on other XCDs read them in the same launch.
-__device__ __forceinline__ void dh_tile(const BwdParams& p, int g, int nt) {
+__device__ __forceinline__ uint32_t dh_tile(const BwdParams& p, int g, int nt) {
   const int64_t wsz = int64_t(p.I) * p.D;
   int4 e;
   int mb;
@@ -155,15 +156,17 @@ __device__ __forceinline__ void dh_tile(const BwdParams& p, int g, int nt) {
   km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
   TileAcc acc;
   tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
+  const uint32_t t_k = uint32_t(wall_clock64());
   epi_dh<kCpolDev>(acc, e.y, e.x, n0, p.I, ab_rows(p, e, mb), p.a.gates, p.P.perm, p.P.bdab,
                    p.P.gh, p.P.dgpart, nt, p.nNdh);
+  return t_k;
 }
 
 // dX tile (m-tile g, column tile nt): dx rows = [da | db] x [W_gate; W_up][e] (K = 2I over
 // the rows of W_gate, then W_up, read K-major), pushed to their pairs.  The da, db rows
 // come from dH tiles of the same launch, so they are read at device scope, and the dx
 // rows are stored at device scope for the row sums of the same launch.
-__device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
+__device__ __forceinline__ uint32_t dx_tile(const BwdParams& p, int g, int nt) {
   const int64_t K = 2 * int64_t(p.I);
   const int64_t wsz = int64_t(p.I) * p.D;
   int4 e;
@@ -175,7 +178,9 @@ __device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
   km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
   TileAcc acc;
   tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
+  const uint32_t t_k = uint32_t(wall_clock64());
   epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
+  return t_k;
 }
 
 // dW GEMMs, K over the expert's routed rows in ascending order, both operands read
@@ -185,15 +190,17 @@ __device__ __forceinline__ void dx_tile(const BwdParams& p, int g, int nt) {
 // launch and are read at device scope.  Rows past the expert's last read zero; an expert
 // without rows gets zero tiles.  One workgroup owns each tile: no atomics.
 template <int AK, int BK>
-__device__ __forceinline__ void dw_tile(KmOp& a, KmOp& b, int nk, int rows, int n0, int N,
-                                        float* C) {
+__device__ __forceinline__ uint32_t dw_tile(KmOp& a, KmOp& b, int nk, int rows, int n0, int N,
+                                            float* C) {
   TileAcc acc;
   tile_gemm_km<AK, BK>(a, b, nk, acc);
+  const uint32_t t_k = uint32_t(wall_clock64());
   epi_store_f32(acc, rows, n0, N, C, N);
+  return t_k;
 }
 
 // dW tile q of nl * 3 * nDt * nIt: expert, then dW_down / dW_gate / dW_up, then tiles.
-__device__ __forceinline__ void dw_tile_at(const BwdParams& p, int q) {
+__device__ __forceinline__ uint32_t dw_tile_at(const BwdParams& p, int q) {
   const int per = p.nDt * p.nIt;
   const int e = q / (3 * per);
   const int which = (q % (3 * per)) / per, r = q % per;
@@ -205,15 +212,16 @@ __device__ __forceinline__ void dw_tile_at(const BwdParams& p, int q) {
     const int m0 = (r / p.nIt) * kBM, n0 = (r % p.nIt) * kBN2;
     km_init_rows<kKG>(a, p.a.dy, p.D, 0, m0, p.D, p.P.dyb, rbeg, rend);
     km_init_rows<kKRD>(b, p.P.gh, p.I, 0, n0, p.I, nullptr, rbeg, rend);
-    dw_tile<kKG, kKRD>(a, b, nk, min(kBM, p.D - m0), n0, p.I, p.a.dwd + e * wsz + int64_t(m0) * p.I);
+    return dw_tile<kKG, kKRD>(a, b, nk, min(kBM, p.D - m0), n0, p.I,
+                              p.a.dwd + e * wsz + int64_t(m0) * p.I);
   } else {           // dW_gate / dW_up[e][i][d] = sum_r da / db[r][i] X[t_r][d]
     const int m0 = (r / p.nDt) * kBM, n0 = (r % p.nDt) * kBN2;
     km_init_rows<kKRD>(a, p.P.bdab, 2 * int64_t(p.I), which == 1 ? 0 : p.I, m0, p.I, nullptr,
                        rbeg, rend);
     km_init_rows<kKG>(b, x_in_ring(p) ? static_cast<const void*>(p.P.ring) : p.a.x, p.D, 0, n0,
                       p.D, p.P.xb, rbeg, rend);
-    dw_tile<kKRD, kKG>(a, b, nk, min(kBM, p.I - m0), n0, p.D,
-                       (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz + int64_t(m0) * p.D);
+    return dw_tile<kKRD, kKG>(a, b, nk, min(kBM, p.I - m0), n0, p.D,
+                              (which == 1 ? p.a.dwg : p.a.dwu) + e * wsz + int64_t(m0) * p.D);
   }
 }
 
@@ -266,6 +274,9 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
   const uint32_t b_x = nh, b_w1 = b_x + nx, b_s = b_w1 + w1, b_w2 = b_s + ns;
   const uint32_t total = b_w2 + (nw - w1);
   bool dh_all = false, dx_all = false;
+  const bool trace = p.P.trace != nullptr;
+  const uint32_t t_start = trace ? uint32_t(wall_clock64()) : 0u;
+  uint32_t n_taken = 0;
   __shared__ uint32_t s_tk;
   while (true) {
     if (threadIdx.x == 0) s_tk = fetch_add_relaxed(hdr + kHdrBwdTicket, 1u);
@@ -273,9 +284,13 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
     const uint32_t tk = __builtin_amdgcn_readfirstlane(s_tk);  // wave-uniform
     __syncthreads();
     if (tk >= total || aborted(hdr)) break;
+    ++n_taken;
+    const uint32_t t_tk = trace ? uint32_t(wall_clock64()) : 0u;
+    uint32_t t_ready = t_tk, t_k = 0u, kind;
     if (tk < b_x) {
+      kind = 0;
       const int g = int(mt) - 1 - int(tk) / p.nNdh;
-      dh_tile(p, g, int(tk) % p.nNdh);
+      t_k = dh_tile(p, g, int(tk) % p.nNdh);
       perturb_pause(p.perturb, tk);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -284,26 +299,43 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
         fetch_add_relaxed(hdr + kHdrBwdDhDone, 1u);
       }
     } else if (tk < b_w1) {
+      kind = 1;
       const int q = int(tk - b_x);
       const int g = int(mt) - 1 - q / p.nDt;
       if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
-      dx_tile(p, g, q % p.nDt);
+      t_ready = trace ? uint32_t(wall_clock64()) : 0u;
+      t_k = dx_tile(p, g, q % p.nDt);
       perturb_pause(p.perturb, tk);
       wg_signal_add(hdr + kHdrBwdDxDone, 1u);
     } else if (tk >= b_s && tk < b_w2) {
+      kind = 3;
       if (!dx_all) {
         if (!wg_wait_geq(hdr + kHdrBwdDxDone, nx, hdr, p.wait_ticks)) break;
         dx_all = true;
       }
+      t_ready = trace ? uint32_t(wall_clock64()) : 0u;
       perturb_pause(p.perturb, tk);
       sum_chunk(p, int(tk - b_s));
+      t_k = trace ? uint32_t(wall_clock64()) : 0u;
     } else {
+      kind = 2;
       if (!dh_all) {
         if (!wg_wait_geq(hdr + kHdrBwdDhDone, nh, hdr, p.wait_ticks)) break;
         dh_all = true;
       }
-      dw_tile_at(p, int(tk < b_s ? tk - b_w1 : w1 + (tk - b_w2)));
+      t_ready = trace ? uint32_t(wall_clock64()) : 0u;
+      t_k = dw_tile_at(p, int(tk < b_s ? tk - b_w1 : w1 + (tk - b_w2)));
     }
+    if (trace && threadIdx.x == 0) {
+      uint32_t* rec = p.P.trace + int64_t(tk) * 8;
+      rec[0] = blockIdx.x; rec[1] = kind; rec[2] = t_tk; rec[3] = t_ready; rec[4] = t_k;
+      rec[5] = uint32_t(wall_clock64()); rec[6] = 0; rec[7] = 0;
+    }
+  }
+  if (trace && threadIdx.x == 0 && blockIdx.x < MOK_TRACE_MAX_WORKGROUPS) {
+    uint32_t* rec = p.P.trace + p.trace_tickets * 8 + int64_t(blockIdx.x) * 8;
+    rec[0] = t_start; rec[1] = t_start; rec[2] = uint32_t(wall_clock64()); rec[3] = rec[2];
+    rec[4] = 0; rec[5] = n_taken; rec[6] = 0; rec[7] = 0;
   }
 }
 
@@ -328,6 +360,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.per_mt = int(L.nN1 + L.nN2);
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
+  p.trace_tickets = int64_t(L.trace_tickets);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

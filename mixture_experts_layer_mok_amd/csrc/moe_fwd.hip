@@ -542,7 +542,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
-  p.trace_tiles = int64_t(L.n_mb_max) * L.mt_max * (L.nN1 + L.nN2);
+  p.trace_tiles = int64_t(L.trace_tickets);
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
   p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
   p.slot_ab = int64_t(L.slot_ab);

@@ -46,6 +46,20 @@ __device__ __forceinline__ float row16_max(float v) {
   return dpp_max_step<0x140>(v);  // row_mirror
 }
 
+// Sum over a 16-lane DPP row, the same butterfly as row16_max; every lane of the row
+// ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  const float t = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+  return v + t;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_sum_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_sum_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_sum_step<0x141>(v);  // row_half_mirror
+  return dpp_sum_step<0x140>(v);  // row_mirror
+}
+
 // Eight e4m3 codes of v[0..7] * 2^-n, packed little-endian.
 __device__ __forceinline__ uint64_t e4m3_pack8(const float (&v)[8], int n) {
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -n), ldexpf(v[1], -n), 0, false);

@@ -545,9 +545,13 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float v = s[q][t];
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
+        // sum over the 32 lanes of the half-wave: a DPP butterfly inside each 16-lane row
+        // (every lane ends with the same bits: each step adds a lane's value to its
+        // partner's, and addition commutes), then the two rows through one permlane swap
+        float v = row16_sum(s[q][t]);
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+        v += __uint_as_float((lane & 16) ? sw[0] : sw[1]);
         const int rr = acc_row(tid, i, 4 * q + t);
         if ((lane & 31) == 0 && rr < rows) red[wn * 256 + rr] = v;
       }

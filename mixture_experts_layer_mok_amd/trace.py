@@ -15,7 +15,7 @@ import numpy as np
 TICK_US = 0.01  # 100 MHz
 
 
-def read(layer, tiles: int, cus: int) -> tuple[np.ndarray, np.ndarray]:
+def read(layer, tiles: int, cus: int) -> tuple[np.ndarray, np.ndarray]:  # noqa: D401
     """Tile records [tiles, 8] and workgroup records [cus, 8] (uint32) of the last traced
     forward on `layer` (a MoKLayer built with MOK_FLAG_TRACE); synchronises."""
     import torch
@@ -83,4 +83,45 @@ def summarize(tiles: np.ndarray, wgs: np.ndarray, comm_cus: int) -> dict:
                        "drain_us": us((drain[cm] - role[cm]).mean()),
                        "drain_chunks": int(wgs[cm, 5].sum())}
     out["drain_chunks_compute"] = int(wgs[comp, 5].sum())
+    return out
+
+
+BWD_KINDS = ("dh", "dx", "dw", "row_sums")
+
+
+def bwd_tickets(desc, m_tiles: int) -> int:
+    """Tickets of the backward's persistent launch: dH, dX, dW tiles and row-sum chunks."""
+    nDt = (desc.hidden + 255) // 256
+    nIt = (desc.intermediate + 255) // 256
+    return m_tiles * (nIt + nDt) + desc.num_local_experts * 3 * nDt * nIt + \
+        (desc.num_tokens + 31) // 32
+
+
+def summarize_bwd(recs: np.ndarray, wgs: np.ndarray) -> dict:
+    """Backward launch: per ticket kind, the mean wait for inputs, K loop and epilogue
+    (for the row sums: the sum itself) in microseconds, and each kind's share of the
+    workgroups' time over the launch's span."""
+    t0 = int(wgs[:, 0].min())
+
+    def rel(x):
+        return (x.astype(np.int64) - t0) & 0xFFFFFFFF
+
+    span = float(rel(wgs[:, 2]).max())
+    tot = span * len(wgs)
+    kind = recs[:, 1]
+    t_tk, t_rd, t_k, t_end = (rel(recs[:, i]) for i in range(2, 6))
+    out = {"span_us": round(span * TICK_US, 2), "workgroups": int(len(wgs)), "kinds": {}}
+    busy = 0.0
+    for k, name in enumerate(BWD_KINDS):
+        m = kind == k
+        if not m.any():
+            continue
+        wait, body, epi = (t_rd - t_tk)[m], (t_k - t_rd)[m], (t_end - t_k)[m]
+        busy += float((t_end - t_tk)[m].sum())
+        out["kinds"][name] = {
+            "n": int(m.sum()), "wait_us": round(float(wait.mean()) * TICK_US, 2),
+            "k_loop_us" if k < 3 else "sum_us": round(float(body.mean()) * TICK_US, 2),
+            "epilogue_us": round(float(epi.mean()) * TICK_US, 2),
+            "share": round(float((t_end - t_tk)[m].sum()) / tot, 4)}
+    out["outside_tickets_share"] = round(1.0 - busy / tot, 4)
     return out
