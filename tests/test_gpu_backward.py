@@ -100,8 +100,8 @@ def test_backward_expert_longer_than_row_table(S):
 
 
 def test_backward_outputs_ordered_on_caller_stream():
-    """Part of the backward runs on the library's side stream; a caller that waits on its
-    own stream only must still see every output complete."""
+    """The backward runs on the caller's stream: work enqueued after it on a non-default
+    stream (copies of its outputs) sees every output complete, call after call."""
     cfg = SMALL[1]
     d = gen.make_inputs(cfg, seed=13, with_dy=True)
     dev = DevInputs(d)
