@@ -54,7 +54,7 @@ typedef enum {
   MOK_OK = 0,
   MOK_E_NULL = 1,        /* a required pointer is NULL                               */
   MOK_E_SHAPE = 2,       /* a size is out of range or inconsistent                   */
-  MOK_E_UNSUPPORTED = 3, /* valid request this build does not implement              */
+  MOK_E_UNSUPPORTED = 3, /* valid request the library does not implement            */
   MOK_E_WORKSPACE = 4,   /* workspace smaller than mok_workspace_size                */
   MOK_E_LAUNCH = 5,      /* the HIP runtime refused a launch                         */
   MOK_E_DEVICE = 6       /* no usable gfx950 device / runtime error                  */
