@@ -70,9 +70,11 @@ CONFIGS = {
     4: LayerConfig("c4-share-zipf-fwd-mxfp8", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
                    M=2048, S=4, comm_cus=32, precision=PREC_MXFP8, zipf_s=1.2),
     # eight ring slots (about 61 MB each) hold every minibatch of this share, so the
-    # backward finds a and b of all of them in the ring and replays nothing
+    # backward finds a and b of all of them in the ring and replays nothing; with no slot
+    # to recycle, the data movers only gather and combine, and 16 of them suffice (the
+    # per-shape tuner and a comm-CU sweep of the whole step agree)
     5: LayerConfig("c5-share-fwd-bwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
-                   M=2048, S=8, comm_cus=20),
+                   M=2048, S=8, comm_cus=16),
 }
 
 
