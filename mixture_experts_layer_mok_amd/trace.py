@@ -15,19 +15,18 @@ import numpy as np
 TICK_US = 0.01  # 100 MHz
 
 
-def read(layer, tiles: int, cus: int) -> tuple[np.ndarray, np.ndarray]:  # noqa: D401
-    """Tile records [tiles, 8] and workgroup records [cus, 8] (uint32) of the last traced
-    forward on `layer` (a MoKLayer built with MOK_FLAG_TRACE); synchronises."""
+def read(layer, tiles: int, cus: int) -> tuple[np.ndarray, np.ndarray]:
+    """Ticket records [tiles, 8] and workgroup records [cus, 8] (uint32) of the last traced
+    launch on `layer` (a MoKLayer built with MOK_FLAG_TRACE); synchronises."""
     import torch
 
     from . import _lib as L
     off, words = L.mok_trace_layout(layer.desc)
     torch.cuda.synchronize(layer.device)
     raw = layer.ws[off:off + words * 4].cpu().numpy().view(np.uint32)
-    d = layer.desc
-    nb = (d.num_tokens * d.top_k + d.minibatch_rows - 1) // d.minibatch_rows
     tile_cap = (words - L.MOK_TRACE_MAX_WORKGROUPS * 8) // 8
-    assert tile_cap >= tiles and nb >= 1
+    if tiles > tile_cap or cus > L.MOK_TRACE_MAX_WORKGROUPS:
+        raise ValueError(f"{tiles} tickets / {cus} workgroups exceed the trace region")
     return raw[:tiles * 8].reshape(tiles, 8).copy(), \
         raw[tile_cap * 8:tile_cap * 8 + cus * 8].reshape(cus, 8).copy()
 
