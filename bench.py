@@ -16,12 +16,16 @@ region.  Prints one JSON line.
 
 `value` is the algorithmic TFLOP/s of the step: 6*D*I flops per routed row forward,
 12*D*I backward (the GEMM1 replay of rows whose ring slot was recycled is not counted).
-`roofline` reports the dominant kernel, the persistent forward k_fwd_fused, against the
-bf16 dense MFMA peak; its duration comes from HIP events recorded on the stream the
-kernel is launched on, around the forward call (which also holds a tiny counter-reset
-kernel).  `traffic` is the HBM byte count of that kernel read from the committed
-FETCH_SIZE / WRITE_SIZE counter summary, scaled by the copy calibration, and null when
-the kernel sources changed since the counters were taken.
+`kernels` gives each persistent kernel's rate against the bf16 dense MFMA peak (the
+forward k_fwd_fused and the backward's k_bwd_main); their durations come from HIP events
+recorded on the stream the kernels are launched on, around the forward and the backward
+calls (each also holds a few-us helper launch).  `roofline` repeats the dominant one
+(the one with the longer time, k_bwd_main on the default workload); its `traffic` is the
+HBM byte count read from the committed FETCH_SIZE / WRITE_SIZE counter summary, scaled by
+the copy calibration, and null when the kernel sources changed since the counters were
+taken.  `phases_unfused` times the forward's four steps as separate launches with the
+in-kernel phase clock: dispatch and combine against HBM bandwidth, GEMM1 and GEMM2
+against the MFMA peak.  `mxfp8_fwd` does the same for the MXFP8 forward (config 4).
 `cpu_baseline` times the float64 NumPy oracle (forward + backward) on this host's cores.
 """
 from __future__ import annotations
@@ -43,10 +47,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_fused_c5_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bwd_main_c5_traffic.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "layer_c5_mfma_counters.txt")
-KERNEL_SOURCES = ("moe_fwd.hip", "tile_ops.h", "gemm_bf16.h", "gemm_mx.h", "mx.h", "tile_geom.h",
-                  "device.h", "layout.h", "launch.h")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_mok_amd", "csrc")
 
 
 def parse():
@@ -63,6 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
+    ap.add_argument("--no-phases", action="store_true",
+                    help="skip the per-phase rates of the forward as separate launches")
     ap.add_argument("--trace", action="store_true",
                     help="one traced fused forward: print where its time went (JSON)")
     ap.add_argument("--sweep", action="store_true")
@@ -78,16 +83,31 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source: counter summaries taken on other sources are stale."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "mixture_experts_layer_mok_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def read_traffic():
-    """HBM bytes per launch of the fused forward from the committed counter summary, or
-    None when it is absent or was taken on other kernel sources."""
+    """HBM bytes per launch of the backward's persistent kernel k_bwd_main from the
+    committed counter summary, or None when it is absent or was taken on other kernel
+    sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             text = f.read()
@@ -101,16 +121,16 @@ def read_traffic():
 
 
 def read_mfma_counters():
-    """Matrix-core busy fraction and shader clock of the fused forward from the committed
-    counter summary (None when absent or taken on other kernel sources)."""
+    """Matrix-core busy fraction and shader clock of k_bwd_main from the committed counter
+    summary (None when absent or taken on other kernel sources)."""
     try:
         with open(MFMA_FILE) as f:
             text = f.read()
     except OSError:
         return None
     m_hash = re.search(r"^source_hash:\s*(\w+)", text, re.M)
-    m_busy = re.search(r"^k_fwd_fused_mfma_busy:\s*([0-9.]+)", text, re.M)
-    m_clk = re.search(r"^k_fwd_fused_clock_ghz:\s*([0-9.]+)", text, re.M)
+    m_busy = re.search(r"^k_bwd_main_mfma_busy:\s*([0-9.]+)", text, re.M)
+    m_clk = re.search(r"^k_bwd_main_clock_ghz:\s*([0-9.]+)", text, re.M)
     if not (m_hash and m_busy and m_clk) or m_hash.group(1) != kernel_source_hash():
         return None
     return {"mfma_busy": float(m_busy.group(1)), "clock_ghz": float(m_clk.group(1))}
@@ -285,6 +305,58 @@ def sweep(args):
             torch.cuda.empty_cache()
 
 
+def phase_rates(cfg, t, R, runs):
+    """The same forward as separate launches (MOK_FLAG_UNFUSED) with the in-kernel phase
+    clock (MOK_FLAG_TRACE): per launch, the median span from its first workgroup start to
+    its last workgroup end over `runs` calls, and the rate that gives against the
+    algorithmic work: dispatch D (2 + s_out) + 8 bytes per routed row (s_out = 2 for bf16,
+    1 + 1/32 for MX codes and scales), combine 2 D per routed row + 2 D + 8 k per token,
+    GEMM1 4 D I and GEMM2 2 D I flops per routed row."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import trace as TR
+    from mixture_experts_layer_mok_amd.layer import MoKLayer
+    mx = cfg.precision == L.MOK_PREC_MXFP8
+    layer = MoKLayer(L.desc_from_config(cfg, flags=L.MOK_FLAG_UNFUSED | L.MOK_FLAG_TRACE),
+                     device=t["x"].device)
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=t["x"].device)
+    sc = (t.get("sg"), t.get("su"), t.get("sd"))
+    per = {n: [] for n in TR.PHASES}
+    for i in range(runs + 2):
+        layer.schedule(t["ids"])
+        layer.forward(t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"], scales=sc, y=y)
+        ph = TR.read_phases(layer)
+        if i >= 2:
+            for n in TR.PHASES:
+                per[n].append(ph[n])
+    if layer.status() != 0:
+        raise SystemExit(f"device status {layer.status():#x} after the unfused forwards")
+    s_out = (1 + 1 / 32) if mx else 2
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    work = {"gather": ("hbm", R * (cfg.D * (2 + s_out) + 8)),
+            "gemm1": ("mfma", 4.0 * cfg.D * cfg.I * R),
+            "gemm2": ("mfma", 2.0 * cfg.D * cfg.I * R),
+            "combine": ("hbm", R * 2 * cfg.D + cfg.T * (2 * cfg.D + 8 * cfg.k))}
+    out = {}
+    for n in TR.PHASES:
+        us = float(np.median(per[n]))
+        bound, w = work[n]
+        if bound == "hbm":
+            gbs = w / (us * 1e-6) / 1e9
+            out[n] = {"us": round(us, 1), "bound": "hbm", "bytes": int(w),
+                      "achieved_GBps": round(gbs, 1), "peak_GBps": PEAK_HBM_GBS,
+                      "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        else:
+            tf = w / (us * 1e-6) / 1e12
+            out[n] = {"us": round(us, 1), "bound": "mfma", "flops": w,
+                      "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": peak,
+                      "frac": round(tf / peak, 4)}
+    del layer
+    torch.cuda.empty_cache()
+    return out
+
+
 def mx_forward_figure(args):
     """The MXFP8 forward on the Zipf-skewed config-4 workload (the pages' MXFP8 mode),
     timed like the main line; reported beside the bf16 step."""
@@ -300,10 +372,15 @@ def mx_forward_figure(args):
     fwd = float(np.mean(r["fwd_ms"]))
     tf = 6.0 * cfg.D * cfg.I * R / (fwd * 1e-3) / 1e12
     res = {"workload": f"{cfg.name}: Zipf(1.2) routing, {R} routed rows",
+           "kernel": "k_fwd_fused<MX>",
            "schedule_ms": stats(r["sched_ms"]), "fwd_ms": stats(r["fwd_ms"]),
            "fwd_tflops": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "frac": round(tf / PEAK_FP8_TFLOPS, 4),
            "routed_rows_per_s": round(R / (r["ms_per_step"] * 1e-3), 1)}
-    del layer, t
+    del layer
+    torch.cuda.empty_cache()
+    log("timing the MXFP8 forward's phases as separate launches")
+    res["phases_unfused"] = phase_rates(cfg, t, R, 3)
+    del t
     torch.cuda.empty_cache()
     return res
 
@@ -439,21 +516,41 @@ def main():
         bwd_ms = float(np.mean(r["bwd_ms"]))
         out["bwd_ms"] = stats(r["bwd_ms"])
         out["bwd_tflops"] = round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2)
+    # per-kernel view: the persistent forward and the backward's persistent kernel, each
+    # against the bf16 dense MFMA peak.  Both durations come from HIP events on the stream
+    # the kernels run on, around the forward call (a counter-reset kernel of a few us, then
+    # k_fwd_fused) and around the backward call (the row-offset kernel and the empty replay
+    # launch, a few us, then k_bwd_main).
+    kernels = {"k_fwd_fused" if not args.unfused else "forward (unfused launches)": {
+        "ms": round(fwd_ms, 4), "flops": flops_fwd, "achieved_TFLOPs": round(achieved, 2),
+        "peak_TFLOPs": peak, "frac": round(achieved / peak, 4)}}
+    dominant = next(iter(kernels))
+    dom = kernels[dominant]
+    if with_bwd:
+        bwd_tf = flops_bwd / (bwd_ms * 1e-3) / 1e12
+        kernels["k_bwd_main"] = {"ms": round(bwd_ms, 4), "flops": flops_bwd,
+                                 "achieved_TFLOPs": round(bwd_tf, 2), "peak_TFLOPs": peak,
+                                 "frac": round(bwd_tf / peak, 4)}
+        if bwd_ms > fwd_ms:
+            dominant, dom = "k_bwd_main", kernels["k_bwd_main"]
+    out["kernels"] = kernels
     # the committed counters were taken on the default command (config 5 as defined, fused,
     # forward saving a and b for the backward)
     c5 = gen.CONFIGS[5]
-    traffic = read_traffic() if (not args.unfused and with_bwd and args.config == 5
-                                 and (cfg.M, cfg.S, cfg.comm_cus) == (c5.M, c5.S, c5.comm_cus)) else None
-    out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_fused" if not args.unfused else
-                       "forward (unfused launches)", "achieved": round(achieved, 2),
-                       "peak": peak, "unit": "TFLOP/s",
-                       "frac": round(achieved / peak, 4), "traffic": traffic}
-    mfma = read_mfma_counters() if traffic is not None else None
+    default_cmd = (not args.unfused and with_bwd and args.config == 5
+                   and (cfg.M, cfg.S, cfg.comm_cus) == (c5.M, c5.S, c5.comm_cus))
+    traffic = read_traffic() if default_cmd and dominant == "k_bwd_main" else None
+    out["roofline"] = {"bound": "mfma", "kernel": dominant, "achieved": dom["achieved_TFLOPs"],
+                       "peak": peak, "unit": "TFLOP/s", "frac": dom["frac"], "traffic": traffic}
+    mfma = read_mfma_counters() if default_cmd and dominant == "k_bwd_main" else None
     if mfma:
         # the counters' view: matrix cores busy per shader cycle, and the clock the card ran
         # at; peak_at_clock is the dense peak scaled to that clock
         out["roofline"].update(mfma_busy=mfma["mfma_busy"], clock_ghz=mfma["clock_ghz"],
                                peak_at_clock=round(peak * mfma["clock_ghz"] / 2.4, 1))
+    if not args.no_phases:
+        log("timing the forward's phases as separate launches (dispatch and combine rates)")
+        out["phases_unfused"] = phase_rates(cfg, t, R, 3)
     if not args.no_cold:
         log("timing cold-cache steps (1 GiB scrub before each)")
         out["cold_cache"] = time_cold(cfg, t, layer, min(args.steps, 5), with_bwd)
@@ -475,7 +572,7 @@ def main():
             cores = min(cores, int(omp))
         out["cpu_baseline"] = {
             "value": round((flops_fwd + flops_bwd) / dt / 1e12, 5), "unit": "TFLOP/s",
-            "cores": cores, "kind": "oracle",
+            "cores": cores, "cpu": cpu_model(), "kind": "oracle",
             "sample": f"the whole workload ({R} routed rows), "
                       f"{'forward+backward' if with_bwd else 'forward'} once in float64 "
                       f"NumPy: {dt:.1f} s"}

@@ -22,7 +22,11 @@
  *     asynchronously; no entry point synchronises except mok_read_device_status.
  *   - Host-side argument checks (null pointers, shapes, workspace size, unsupported
  *     modes) return an error code synchronously and enqueue nothing.  These checks run
- *     before any HIP runtime call, so they work on a machine without a GPU.
+ *     before any HIP runtime call, so they work on a machine without a GPU.  One check
+ *     needs the device: the fused forward's comm_cus must be below the number of
+ *     workgroups its persistent kernel runs (one per compute unit), so mok_moe_fwd first
+ *     queries the current device (device, attribute and occupancy queries only) and
+ *     returns MOK_E_SHAPE, with nothing enqueued, when comm_cus is too large.
  *   - Data-dependent faults are recorded in a sticky device status word inside the
  *     workspace (MOK_DEV_* bits), read back with mok_read_device_status.
  *   - Same inputs and descriptor give bitwise-identical outputs (fixed-order sums, no
@@ -104,7 +108,8 @@ typedef struct {
   int32_t num_local_experts; /* E_loc: local experts [e0, e0+E_loc), 1..1024            */
   int32_t minibatch_rows;    /* M: routed rows per minibatch / ring slot                */
   int32_t ring_slots;        /* S: slots in the ring (>= 1)                             */
-  int32_t comm_cus;          /* workgroups doing dispatch/combine in the fused kernel   */
+  int32_t comm_cus;          /* workgroups doing dispatch/combine in the fused kernel:
+                                1 .. (device CUs - 1), checked by mok_moe_fwd            */
   int32_t precision;         /* MOK_PREC_BF16 or MOK_PREC_MXFP8 (forward only)          */
   uint32_t flags;            /* MOK_FLAG_*                                              */
 } mok_desc_t;
@@ -198,6 +203,10 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
  *    ready, K loop (or sum) done, end, 0, 0], per workgroup [start, start, end, end, 0,
  *   tickets taken, 0, 0].  The region holds as many ticket records as the larger of the
  *   two launches has tickets.
+ * With MOK_FLAG_UNFUSED the forward writes instead, in the region's first 8 64-bit
+ * words, the earliest workgroup start and the latest workgroup end (64-bit values of the
+ * same clock; an end is taken once the workgroup's memory operations have completed) of
+ * its gather, GEMM1, GEMM2 and combine launches, in that order: the four phases' times.
  * The caller reads the region after the forward has completed.  Errors: MOK_E_NULL,
  * the descriptor's errors, MOK_E_UNSUPPORTED when the flag is not set. */
 #define MOK_TRACE_MAX_WORKGROUPS 1024

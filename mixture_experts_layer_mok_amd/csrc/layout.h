@@ -38,6 +38,8 @@ enum HdrWord : int {
   kHdrBwdTicket = 8,   // backward kernel: next ticket
   kHdrBwdDhDone = 9,   // backward kernel: dH tiles done
   kHdrBwdDxDone = 10,  // backward kernel: dX tiles done
+  kHdrArrive = 11,     // fused forward: workgroups started (each takes the next number)
+  kHdrFillTicket = 12, // fused forward: next chunk of minibatch 0's rows (the fill)
   kHdrWords = 64
 };
 

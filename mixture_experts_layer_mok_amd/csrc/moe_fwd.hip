@@ -13,8 +13,9 @@
 //   combine   — the final weighted sum: y[t] = sum_j gate[t,j] * o[t*k+j] over local
 //               slots in ascending j, fp32 (multiply, then add), rounded once to bf16.
 //
-// Fused form (one persistent cooperative kernel): the first comm_cus workgroups move
-// data (dispatch + combine), the rest run MFMA tiles.  Handoff data (slot rows, H, the
+// Fused form (one persistent kernel, one workgroup per CU): workgroups number
+// themselves in the order they start (an atomic counter); the first comm_cus move data
+// (dispatch + combine), the rest run MFMA tiles.  Handoff data (slot rows, H, the
 // result rows) is written and read at device scope (each MI355X XCD has its own L2),
 // and the counters are relaxed device-scope atomics bumped after a workgroup's stores
 // have completed:
@@ -28,8 +29,10 @@
 // (L = 0 otherwise), so a GEMM2 tile's H was normally finished a whole block earlier.
 // Every wait is on work with a smaller ticket (GEMM2 of mb on GEMM1 of mb) or on a
 // comm step that only depends on such work (the gather of mb on GEMM2 of mb - S, in
-// block mb - S + L < mb): no cycle, given all workgroups are co-resident (cooperative
-// launch).  A token is combined by the comm workgroup that
+// block mb - S + L < mb): no cycle.  Every role, ticket and chunk goes to a workgroup
+// that is already running, so no wait depends on a workgroup that has not started: the
+// kernel needs no co-residency guarantee (no cooperative launch), only that more than
+// comm_cus of its workgroups can run at once.  A token is combined by the comm workgroup that
 // owns its highest local row, right after that row's minibatch is done, so most of the
 // combine overlaps later minibatches' GEMMs.
 #include <algorithm>
@@ -99,8 +102,32 @@ __device__ __forceinline__ void combine_if_last(const FwdParams& p, int r) {
 // ------------------------------------------------------------------------------------
 // Unfused kernels: the same steps over full-size buffers, one launch per step.
 // ------------------------------------------------------------------------------------
+// With MOK_FLAG_TRACE, launch ph (0 gather, 1 GEMM1, 2 GEMM2, 3 combine) keeps the
+// earliest start and the latest end of its workgroups, 64-bit values of the 100 MHz
+// constant clock, in 64-bit words 2 ph and 2 ph + 1 of the trace region (k_phase_init
+// sets them to the largest value and 0 before the four launches).  A workgroup's end is
+// taken once its memory operations have completed.
+__global__ __launch_bounds__(64) void k_phase_init(uint32_t* trace) {
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(trace);
+  if (threadIdx.x < 8) w[threadIdx.x] = (threadIdx.x & 1) ? 0ull : ~0ull;
+}
+__device__ __forceinline__ void phase_start(const FwdParams& p, int ph) {
+  if (p.P.trace && threadIdx.x == 0)
+    atomicMin(reinterpret_cast<unsigned long long*>(p.P.trace) + 2 * ph,
+              (unsigned long long)wall_clock64());
+}
+__device__ __forceinline__ void phase_end(const FwdParams& p, int ph) {
+  if (!p.P.trace) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<unsigned long long*>(p.P.trace) + 2 * ph + 1,
+              (unsigned long long)wall_clock64());
+}
+
 template <bool MX>
 __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
+  phase_start(p, 0);
   const int R = int(p.P.hdr[kHdrR]);
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
@@ -112,10 +139,11 @@ __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
     else
       wave_copy_row<false>(reinterpret_cast<uint16_t*>(p.P.full_x) + int64_t(r) * p.D, src, p.D);
   }
+  phase_end(p, 0);
 }
 
 template <bool MX>
-__global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
+__device__ __forceinline__ void gemm1_tile_unfused(const FwdParams& p) {
   const int nt = blockIdx.x % p.nN1;
   const int f = blockIdx.x / p.nN1;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -143,7 +171,14 @@ __global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
 }
 
 template <bool MX>
-__global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
+__global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
+  phase_start(p, 1);
+  gemm1_tile_unfused<MX>(p);
+  phase_end(p, 1);
+}
+
+template <bool MX>
+__device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
   const int nt = blockIdx.x % p.nN2;
   const int f = blockIdx.x / p.nN2;
   const int mb = f / p.mt_max, i = f % p.mt_max;
@@ -166,9 +201,17 @@ __global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
   epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
 }
 
+template <bool MX>
+__global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
+  phase_start(p, 2);
+  gemm2_tile_unfused<MX>(p);
+  phase_end(p, 2);
+}
+
 // One wave per token; the next token's slot rows and gates are loaded while this one is
 // summed, so that the per-token lookups do not add a memory round trip each.
 __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
+  phase_start(p, 3);
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int lane = threadIdx.x & 63;
@@ -190,6 +233,7 @@ __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
     else
       wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
   }
+  phase_end(p, 3);
 }
 
 // ------------------------------------------------------------------------------------
@@ -202,6 +246,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep(FwdParams p) {
     p.P.hdr[kHdrFwdTicket] = 0;
     p.P.hdr[kHdrDrainTicket] = 0;
     p.P.hdr[kHdrAbort] = 0;
+    p.P.hdr[kHdrArrive] = 0;
+    p.P.hdr[kHdrFillTicket] = 0;
   }
 }
 
@@ -277,8 +323,48 @@ __device__ __forceinline__ void gather_mb(const FwdParams& p, int mb, int gw, in
   }
 }
 
-// Comm workgroups: gather minibatches 1.. into the ring (minibatch 0 is gathered by every
-// workgroup before the roles split), reusing a slot once the GEMM2 tiles of the minibatch
+// The fill: minibatch 0's rows go into slot 0 in chunks of one row per wave, taken from
+// a ticket by every workgroup as it starts, before the roles split; ready[0] counts the
+// rows done (the GEMM1 tiles of minibatch 0 wait for all of them).  Only running
+// workgroups take chunks, so the fill never waits for one that has not started.
+constexpr int kFillRows = kThreads / 64;
+
+template <bool MX>
+__device__ __forceinline__ void fill_mb0(const FwdParams& p, uint32_t* ready) {
+  uint32_t* hdr = p.P.hdr;
+  const int lo = p.P.mb_start[0], hi = p.P.mb_start[1];
+  const uint32_t chunks = uint32_t((hi - lo + kFillRows - 1) / kFillRows);
+  const int w = threadIdx.x >> 6;
+  uint8_t* slot = p.P.ring;
+  __shared__ uint32_t s_fk;
+  uint32_t rows = 0;
+  while (true) {
+    if (threadIdx.x == 0) s_fk = fetch_add_relaxed(hdr + kHdrFillTicket, 1u);
+    __syncthreads();
+    const uint32_t fk = s_fk;
+    __syncthreads();
+    if (fk >= chunks) break;
+    const int r0 = lo + int(fk) * kFillRows;
+    rows += uint32_t(min(kFillRows, hi - r0));
+    const int r = r0 + w;
+    if (r < hi) {
+      const uint16_t* src = p.a.x + int64_t(p.P.perm[r] / p.k) * p.D;
+      if (MX)
+        wave_quant_row<true>(slot + p.slot_x + int64_t(r - lo) * p.D,
+                             slot + p.slot_xs + int64_t(r - lo) * p.xs_ld, src, p.D);
+      else
+        wave_copy_row<true>(reinterpret_cast<uint16_t*>(slot + p.slot_x) + int64_t(r - lo) * p.D,
+                            src, p.D);
+    }
+  }
+  if (rows) {
+    perturb_pause(p.perturb, blockIdx.x);
+    wg_signal_add(ready, rows);
+  }
+}
+
+// Comm workgroups: gather minibatches 1.. into the ring (minibatch 0 is the fill, done by
+// every workgroup before the roles split), reusing a slot once the GEMM2 tiles of the minibatch
 // it held are done, and combine the tokens of that older minibatch.  The last S
 // minibatches are combined in the drain.
 template <bool MX>
@@ -387,8 +473,8 @@ __device__ __forceinline__ uint32_t drain(const FwdParams& p, const uint32_t* do
 }
 
 template <bool MX>
-__device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t* ready,
-                             uint32_t* done, uint32_t* hdone) {
+__device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
+                                             uint32_t* ready, uint32_t* done, uint32_t* hdone) {
   uint32_t* hdr = p.P.hdr;
   const uint32_t total = hdr[kHdrFwdTiles];
   const int n_mb = int(hdr[kHdrNmb]);
@@ -430,7 +516,8 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
     const int i = qq / nn, nt = qq % nn;
     uint32_t* hd = hdone + int64_t(mb) * p.mt_max + i;
     if (g1) {
-      if (!wg_wait_geq(ready + mb, mb == 0 ? gridDim.x : uint32_t(C), hdr, p.wait_ticks)) break;
+      const uint32_t need = mb == 0 ? uint32_t(p.P.mb_start[1] - p.P.mb_start[0]) : uint32_t(C);
+      if (!wg_wait_geq(ready + mb, need, hdr, p.wait_ticks)) break;
     } else {
       if (!wg_wait_geq(hd, uint32_t(p.nN1), hdr, p.wait_ticks)) break;
     }
@@ -452,7 +539,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
         const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(hd, 1);
-        if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
+        if (trace) trace_put(rec, uint32_t(vid), kind, t_tk, t_ready, t_k, trace_now(), t_e);
       } else {
         const MxOperands o = mx_ops_gemm2(p, slot + p.slot_h + int64_t(r0) * p.I,
                                           slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
@@ -462,7 +549,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
         const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(done + mb, 1);
-        if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
+        if (trace) trace_put(rec, uint32_t(vid), kind, t_tk, t_ready, t_k, trace_now(), t_e);
       }
       continue;
     }
@@ -487,7 +574,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int C, uint32_t
       perturb_pause(p.perturb, tk);
       wg_signal_add(done + mb, 1);
     }
-    if (trace) trace_put(rec, blockIdx.x, kind, t_tk, t_ready, t_k, trace_now(), t_e);
+    if (trace) trace_put(rec, uint32_t(vid), kind, t_tk, t_ready, t_k, trace_now(), t_e);
   }
 }
 
@@ -497,23 +584,22 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   uint32_t* done = ready + p.n_mb_max;
   uint32_t* hdone = done + p.n_mb_max;
   const int C = p.a.comm_cus;
-  const bool trace = p.P.trace != nullptr && blockIdx.x < MOK_TRACE_MAX_WORKGROUPS;
+  // the workgroup's number in order of arrival: roles go to running workgroups
+  __shared__ uint32_t s_vid;
+  if (threadIdx.x == 0) s_vid = fetch_add_relaxed(p.P.hdr + kHdrArrive, 1u);
+  __syncthreads();
+  const int vid = int(s_vid);
+  const bool trace = p.P.trace != nullptr && vid < MOK_TRACE_MAX_WORKGROUPS;
   const uint32_t t0 = trace ? trace_now() : 0u;
-  // fill: every workgroup gathers part of minibatch 0
-  if (p.P.hdr[kHdrNmb] > 0) {
-    gather_mb<MX>(p, 0, blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6),
-                  gridDim.x * (kThreads / 64));
-    perturb_pause(p.perturb, blockIdx.x);
-    wg_signal_add(ready, 1);
-  }
+  if (p.P.hdr[kHdrNmb] > 0) fill_mb0<MX>(p, ready);
   const uint32_t t1 = trace ? trace_now() : 0u;
-  if (int(blockIdx.x) < C) comm_role<MX>(p, blockIdx.x, C, ready, done);
-  else compute_role<MX>(p, C, ready, done, hdone);
+  if (vid < C) comm_role<MX>(p, vid, C, ready, done);
+  else compute_role<MX>(p, vid, C, ready, done, hdone);
   const uint32_t t2 = trace ? trace_now() : 0u;
   const uint32_t nd = drain(p, done);
   if (trace)
-    trace_put(p.P.trace + p.trace_tiles * 8 + int64_t(blockIdx.x) * 8, t0, t1, t2, trace_now(),
-              int(blockIdx.x) < C ? 1u : 0u, nd);
+    trace_put(p.P.trace + p.trace_tiles * 8 + int64_t(vid) * 8, t0, t1, t2, trace_now(),
+              vid < C ? 1u : 0u, nd);
 }
 
 // Weight scales with a row stride of K / 32 bytes, repacked to the tile's stride of one
@@ -579,6 +665,7 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
                        int(L.wds_ld));
   }
   if (L.unfused) {
+    if (P.trace) hipLaunchKernelGGL(k_phase_init, dim3(1), dim3(64), 0, st, P.trace);
     const unsigned gw = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
     const dim3 g1(unsigned(L.n_mb_max * L.mt_max * L.nN1)), g2(unsigned(L.n_mb_max * L.mt_max * L.nN2));
     if (L.mx) {
@@ -600,11 +687,11 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
   if (grid <= 0) return MOK_E_DEVICE;
   if (a.comm_cus >= grid) return MOK_E_SHAPE;
   hipLaunchKernelGGL(k_fwd_prep, dim3(64), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return MOK_E_LAUNCH;
-  void* args[] = {&p};
-  if (hipLaunchCooperativeKernel(kern, dim3(grid), dim3(kThreads), args, 0, st) != hipSuccess)
-    return MOK_E_LAUNCH;
-  return MOK_OK;
+  if (L.mx)
+    hipLaunchKernelGGL(k_fwd_fused<true>, dim3(grid), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(k_fwd_fused<false>, dim3(grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
 }
 
 }  // namespace mok

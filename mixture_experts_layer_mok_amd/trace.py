@@ -124,3 +124,20 @@ def summarize_bwd(recs: np.ndarray, wgs: np.ndarray) -> dict:
             "share": round(float((t_end - t_tk)[m].sum()) / tot, 4)}
     out["outside_tickets_share"] = round(1.0 - busy / tot, 4)
     return out
+
+
+PHASES = ("gather", "gemm1", "gemm2", "combine")
+
+
+def read_phases(layer) -> dict:
+    """Durations (us) of the gather, GEMM1, GEMM2 and combine launches of the last
+    unfused forward run with MOK_FLAG_TRACE on `layer`: the span from the earliest
+    workgroup start to the latest workgroup end of each launch; synchronises."""
+    import torch
+
+    from . import _lib as L
+    off, _ = L.mok_trace_layout(layer.desc)
+    torch.cuda.synchronize(layer.device)
+    raw = layer.ws[off:off + 64].cpu().numpy().view(np.uint64)
+    return {name: float(int(raw[2 * i + 1]) - int(raw[2 * i])) * TICK_US
+            for i, name in enumerate(PHASES)}

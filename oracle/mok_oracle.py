@@ -48,6 +48,9 @@ Readings taken where the pages are silent:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 E4M3_MAX = 448.0
@@ -342,36 +345,43 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int):
 # Sampled evaluation (full-size checks of selected outputs)
 # =================================================================================
 def forward_tokens(tokens, x, ids, gates, wg, wu, wd, *, e0: int, mxfp8: bool = False):
-    """Y rows for the listed tokens only, evaluated token by token (float64).  The
-    sum over slots runs in ascending j, skipping slots without a local expert."""
+    """Y rows for the listed tokens only (float64), without a schedule: for each local
+    expert, the listed tokens routed to it go through its FFN together; then each token's
+    gated expert outputs are summed over its slots in ascending j (slots without a local
+    expert add nothing).  With ``mxfp8`` the MX round trips sit where ``forward`` puts
+    them: X rows and the weights along their K, H along I from float32."""
+    tokens = np.asarray(tokens, dtype=np.int64)
     n_local = wg.shape[0]
+    k = ids.shape[1]
     D = np.asarray(x).shape[1]
-    out = np.zeros((len(tokens), D))
+    xs = np.asarray(x, np.float64)[tokens]
+    if mxfp8:
+        xs = mx_roundtrip(xs)
+    sel = np.asarray(ids)[tokens]
+    g = np.asarray(gates, np.float64)[tokens]
+    used = [e for e in range(n_local) if np.any(sel == e + e0)]
     deq = {}
-
-    def weights(e):
-        if e not in deq:
-            if mxfp8:
-                deq[e] = (mx_roundtrip(wg[e]), mx_roundtrip(wu[e]), mx_roundtrip(wd[e]))
-            else:
-                deq[e] = (wg[e], wu[e], wd[e])
-        return deq[e]
-
-    for n, t in enumerate(tokens):
-        xt = np.asarray(x[t], np.float64)[None, :]
+    if mxfp8:
+        # the weight round trips are independent: run them side by side (NumPy's array
+        # operations release the interpreter lock)
+        mats = [(e, n, w[e]) for e in used for n, w in (("g", wg), ("u", wu), ("d", wd))]
+        with cf.ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+            for (e, n, _), v in zip(mats, ex.map(lambda m: mx_roundtrip(m[2]), mats)):
+                deq[e, n] = v
+    contrib = np.zeros((len(tokens), k, D))     # gated output of (listed token n, slot j)
+    for e in used:
+        nn, jj = np.nonzero(sel == e + e0)
+        g_w, u_w, d_w = wg[e], wu[e], wd[e]
         if mxfp8:
-            xt = mx_roundtrip(xt)
-        for j in range(ids.shape[1]):
-            e = int(ids[t, j]) - e0
-            if e < 0 or e >= n_local:
-                continue
-            g_w, u_w, d_w = weights(e)
-            if mxfp8:
-                a = xt @ np.asarray(g_w, np.float64).T
-                b = xt @ np.asarray(u_w, np.float64).T
-                h = mx_roundtrip((silu(a) * b).astype(np.float32))
-                o = h @ np.asarray(d_w, np.float64).T
-            else:
-                _, _, _, o = expert_ffn(xt, g_w, u_w, d_w)
-            out[n] += float(gates[t, j]) * o[0]
+            g_w, u_w, d_w = deq[e, "g"], deq[e, "u"], deq[e, "d"]
+            a = xs[nn] @ np.asarray(g_w, np.float64).T
+            b = xs[nn] @ np.asarray(u_w, np.float64).T
+            h = mx_roundtrip((silu(a) * b).astype(np.float32))
+            o = h @ np.asarray(d_w, np.float64).T
+        else:
+            _, _, _, o = expert_ffn(xs[nn], g_w, u_w, d_w)
+        contrib[nn, jj] = g[nn, jj][:, None] * o
+    out = np.zeros((len(tokens), D))
+    for j in range(k):
+        out += contrib[:, j]
     return out

@@ -44,3 +44,17 @@ def rel_fro(a, b) -> float:
 
 def y_values(y: torch.Tensor) -> np.ndarray:
     return bf16_values(y)
+
+
+def row_errors(got, ref) -> tuple[float, float, int]:
+    """(relative Frobenius error, largest per-row relative error over rows whose reference
+    is non-zero, number of rows whose reference is zero but got is not).  A row's relative
+    error is ||got_t - ref_t|| / ||ref_t||."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rn = np.linalg.norm(ref, axis=1)
+    dn = np.linalg.norm(got - ref, axis=1)
+    nz = rn > 0
+    worst = float((dn[nz] / rn[nz]).max()) if nz.any() else 0.0
+    stray = int(np.count_nonzero(np.any(got[~nz] != 0, axis=1)))
+    return rel_fro(got, ref), worst, stray

@@ -9,7 +9,7 @@ import oracle as O
 from mixture_experts_layer_mok_amd import _lib as L
 from mixture_experts_layer_mok_amd import gen
 from mixture_experts_layer_mok_amd.layer import MoKLayer, bf16_values
-from tests.gpu_util import DevInputs, rel_fro, say
+from tests.gpu_util import DevInputs, rel_fro, row_errors, say
 
 pytestmark = pytest.mark.gpu
 TOL_BF16 = 1e-2
@@ -35,9 +35,12 @@ def _compare(cfg, d, ids, g, tag):
         "dwu": rel_fro(g["dwu"].cpu().numpy(), ref["dwu"]),
         "dwd": rel_fro(g["dwd"].cpu().numpy(), ref["dwd"]),
     }
-    say(f"  {tag} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    _, worst, stray = row_errors(bf16_values(g["dx"]), ref["dx"])
+    say(f"  {tag} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
+        f" dx worst row={worst:.2e}")
     for k, v in errs.items():
         assert v < TOL_BF16, (k, v)
+    assert worst < TOL_BF16 and stray == 0, (worst, stray)
     # non-local slots carry no gradient
     assert np.all(g["dg"].cpu().numpy()[ref["schedule"].pos.reshape(ids.shape) < 0] == 0)
     return ref
@@ -123,8 +126,9 @@ def test_backward_outputs_ordered_on_caller_stream():
 
 
 def test_backward_config5_full_and_deterministic():
-    """Config 5 against the oracle, then ten forward + backward runs in all, each on a new
-    workspace, bitwise equal in Y and every gradient."""
+    """Config 5 against the oracle (the whole Y row by row, every gradient), then ten
+    forward + backward runs in all, each on a new workspace, bitwise equal in Y and every
+    gradient."""
     cfg = gen.CONFIGS[5]
     say("[c5] generating")
     d = gen.make_inputs(cfg, with_dy=True)
@@ -132,6 +136,13 @@ def test_backward_config5_full_and_deterministic():
     y1, g1, layer = run_fwd_bwd(cfg, dev)
     assert layer.status() == 0
     del layer
+    say("[c5] oracle forward (float64)")
+    ref_y = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0,
+                      E=cfg.E, M=cfg.M)
+    fro, worst, stray = row_errors(bf16_values(y1), ref_y)
+    say(f"  c5 y rel_fro={fro:.3e} worst row={worst:.3e} stray rows={stray}")
+    assert fro < TOL_BF16 and worst < TOL_BF16 and stray == 0
+    del ref_y
     say("[c5] oracle backward (float64)")
     _compare(cfg, d, d["ids"], g1, "c5")
     for run in range(2, 11):

@@ -12,7 +12,7 @@ import oracle as O
 from mixture_experts_layer_mok_amd import _lib as L
 from mixture_experts_layer_mok_amd import gen
 from mixture_experts_layer_mok_amd.layer import MoKLayer
-from tests.gpu_util import DevInputs, rel_fro, run_forward, say, y_values
+from tests.gpu_util import DevInputs, rel_fro, row_errors, run_forward, say, y_values
 
 pytestmark = pytest.mark.gpu
 TOL_BF16 = 1e-2
@@ -133,18 +133,21 @@ def c3_inputs():
     return cfg, d, DevInputs(d)
 
 
-def test_forward_config3_sampled_and_deterministic(c3_inputs):
+def test_forward_config3_full_and_deterministic(c3_inputs):
+    """The whole config-3 output against the oracle, row by row: the relative Frobenius
+    error and the largest per-row relative error are both below 1e-2, and tokens without a
+    local slot are exactly zero.  Then bitwise repeats and invariance."""
     cfg, d, dev = c3_inputs
     y, layer = run_forward(cfg, dev)
     assert layer.status() == 0
     _check_schedule(cfg, d, d["ids"], layer)
-    rng = np.random.default_rng(33)
-    toks = np.sort(rng.choice(cfg.T, 48, replace=False))
-    ref = O.forward_tokens(toks, d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0)
-    yv = y_values(y)[toks]
-    err = rel_fro(yv, ref)
-    say(f"  c3 sampled rel_fro={err:.3e}")
-    assert err < TOL_BF16
+    say("[c3] oracle forward (float64)")
+    ref = O.forward(d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"], e0=0, E=cfg.E,
+                    M=cfg.M)
+    fro, worst, stray = row_errors(y_values(y), ref)
+    say(f"  c3 rel_fro={fro:.3e} worst row={worst:.3e} stray rows={stray}")
+    assert fro < TOL_BF16 and worst < TOL_BF16 and stray == 0
+    del ref
     y_again, _ = run_forward(cfg, dev)
     assert torch.equal(y, y_again)
     # per-row arithmetic does not depend on the minibatch split, the ring or the CU split

@@ -18,7 +18,7 @@ import oracle as O
 from mixture_experts_layer_mok_amd import _lib as L
 from mixture_experts_layer_mok_amd import gen
 from mixture_experts_layer_mok_amd.layer import MoKLayer, bf16_tensor
-from tests.gpu_util import DevInputs, rel_fro, say, y_values
+from tests.gpu_util import DevInputs, rel_fro, row_errors, say, y_values
 
 pytestmark = pytest.mark.gpu
 TOL_MX = 5e-2
@@ -136,6 +136,12 @@ def test_forward_mx_edge_cases():
 
 
 def test_forward_config4_sampled_and_deterministic():
+    """Config 4 (MXFP8, Zipf routing, about 86k routed rows) against the MX-emulating
+    oracle on sampled tokens: tokens of every local expert, and the tokens that own the
+    rows on both sides of every minibatch window boundary and of the first m-tile start
+    (256 rows from the expert's first row) at or after it; plus tokens with no local slot,
+    which must be exactly zero.  Relative Frobenius error and the largest per-row error
+    are both below 5e-2.  Then a bitwise repeat."""
     cfg = gen.CONFIGS[4]
     say("[c4] generating")
     d = gen.make_inputs(cfg)
@@ -146,19 +152,29 @@ def test_forward_config4_sampled_and_deterministic():
     say(f"[c4] routed rows {tab['R']}, per expert {tab['counts'].tolist()}")
     y2, _ = run_mx(cfg, dev)
     assert torch.equal(y, y2), "MXFP8 forward not deterministic"
-    # tokens whose local slots all sit in experts 0..2 (the hot ones), so the oracle
-    # quantises only three experts' weights; plus tokens with no local slot
     ids = d["ids"]
-    local = (ids >= cfg.e0) & (ids < cfg.e0 + cfg.n_local)
-    inside = np.all(~local | (ids < 3), axis=1) & local.any(axis=1)
+    s = O.schedule(ids, cfg.e0, cfg.n_local, cfg.E, cfg.M)
     rng = np.random.default_rng(44)
-    toks = np.sort(rng.choice(np.flatnonzero(inside), 24, replace=False))
-    none = np.flatnonzero(~local.any(axis=1))[:4]
+    rows = set()
+    for e in range(cfg.n_local):                      # every local expert
+        lo, hi = int(s.offsets[e]), int(s.offsets[e + 1])
+        if hi > lo:
+            rows.update(rng.integers(lo, hi, 4).tolist())
+            rows.update((lo, hi - 1))
+    for b in range(cfg.M, s.R, cfg.M):                # every minibatch window boundary
+        e = int(np.searchsorted(s.offsets, b, side="right")) - 1
+        t0 = int(s.offsets[e]) + -(-(b - int(s.offsets[e])) // 256) * 256
+        for r in (b - 1, b, t0 - 1, t0):
+            if 0 <= r < s.R:
+                rows.add(r)
+    toks = np.unique(s.perm[sorted(rows)] // cfg.k)
+    local = (ids >= cfg.e0) & (ids < cfg.e0 + cfg.n_local)
+    none = np.flatnonzero(~local.any(axis=1))[:8]
     say(f"[c4] oracle on {len(toks)} tokens")
     ref = O.forward_tokens(toks, d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0,
                            mxfp8=True)
     yv = y_values(y)
-    err = rel_fro(yv[toks], ref)
-    say(f"[c4] sampled rel_fro vs MX oracle {err:.3e}")
-    assert err < TOL_MX
+    fro, worst, stray = row_errors(yv[toks], ref)
+    say(f"[c4] sampled rel_fro vs MX oracle {fro:.3e}, worst row {worst:.3e}")
+    assert fro < TOL_MX and worst < TOL_MX and stray == 0
     assert np.all(yv[none] == 0)

@@ -278,6 +278,108 @@ def test_forward_mxfp8_oracle():
     assert np.array_equal(O.mx_dequantize(codes, scales), h)
 
 
+def _torch_mx_roundtrip(v: torch.Tensor) -> torch.Tensor:
+    """MX round trip written independently of the oracle, with torch's float8_e4m3fn cast:
+    blocks of 32 along the last axis; the shared scale is 2^n for the smallest integer n
+    with max|v| 2^-n <= 448 (the largest finite e4m3 value), n clamped to [-127, 127].
+    The block values are read as float32 (what the quantisers read)."""
+    v32 = v.to(torch.float32).to(torch.float64)
+    K = v32.shape[-1]
+    blk = v32.reshape(*v32.shape[:-1], K // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)                      # amax = m 2^e, m in [0.5, 1)
+    base = e.to(torch.int64) - 9                  # floor(log2 amax) - 8
+    n = base + 1                                  # always large enough
+    for cand in (base, base - 1):                 # keep the smallest n that still fits
+        ok = amax * torch.exp2(-cand.to(torch.float64)) <= 448.0
+        n = torch.where(ok, cand, n)
+    n = torch.clamp(n, -127, 127)
+    scale = torch.exp2(n.to(torch.float64))[..., None]
+    q = (blk / scale).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64) * scale
+    return q.reshape(v32.shape)
+
+
+def _torch_mx_layer(x, ids, gates, wg, wu, wd, e0, transposed=()):
+    """The MXFP8 layer as per-expert masked torch products (no schedule), with the MX round
+    trip applied where each GEMM reads its operands: X rows and W_gate / W_up along D (their
+    K), W_down along I (its K), and H along I after SwiGLU, from its float32 value.
+    `transposed` names quantisation points ("x", "wgu", "wd", "h") whose blocks are taken
+    along the other axis instead (a planted mistake, to show the comparison notices it)."""
+    def q(v, name):
+        if name not in transposed:
+            return _torch_mx_roundtrip(v)
+        n = v.shape[0]
+        pad = torch.zeros((v.shape[1], -n % 32), dtype=v.dtype)   # zeros leave amax as is
+        return _torch_mx_roundtrip(torch.cat([v.T, pad], dim=1))[:, :n].T
+
+    X = torch.tensor(x, dtype=torch.float64)
+    G = torch.tensor(gates, dtype=torch.float64)
+    Y = torch.zeros_like(X)
+    idt = torch.tensor(ids.astype(np.int64))
+    for e in range(wg.shape[0]):
+        tok, slot = torch.nonzero(idt == e + e0, as_tuple=True)
+        if tok.numel() == 0:
+            continue
+        Wg = q(torch.tensor(wg[e], dtype=torch.float64), "wgu")   # [I, D], K = D
+        Wu = q(torch.tensor(wu[e], dtype=torch.float64), "wgu")
+        Wd = q(torch.tensor(wd[e], dtype=torch.float64), "wd")    # [D, I], K = I
+        Xq = q(X[tok], "x")
+        hid = F.silu(F.linear(Xq, Wg)) * F.linear(Xq, Wu)
+        out = F.linear(q(hid.to(torch.float32).to(torch.float64), "h"), Wd) * G[tok, slot][:, None]
+        Y = Y.index_add(0, tok, out)
+    return Y
+
+
+def _wide_range_inputs(d):
+    """Rescale an input set so that every 32-block along each GEMM's K spans many binades.
+    With power-of-two block scales, e4m3 rounds normal-range values the same whatever the
+    block, so only the values that a block's scale pushes into the subnormal range (or
+    flushes) show which axis the blocks run along; and such a value must meet a large
+    partner in its product to reach the output.  So the two operands of each GEMM get
+    complementary patterns along K: X columns 2^-(d mod 24), W_gate / W_up columns
+    2^-((d + 12) mod 24); W_gate / W_up rows 2^-floor((i mod 24) / 2), which makes H span
+    about 24 binades along I; W_down columns 2^-((i + 12) mod 24)."""
+    out = dict(d)
+    D, I = d["wg"].shape[2], d["wg"].shape[1]
+    dd, ii = np.arange(D), np.arange(I)
+    px = np.ldexp(1.0, -(dd % 24)).astype(np.float32)
+    pwd = np.ldexp(1.0, -((dd + 12) % 24)).astype(np.float32)
+    pwi = np.ldexp(1.0, -((ii % 24) // 2)).astype(np.float32)
+    pdi = np.ldexp(1.0, -((ii + 12) % 24)).astype(np.float32)
+    out["x"] = (d["x"] * px[None, :]).astype(np.float32)
+    out["wg"] = (d["wg"] * pwd[None, None, :] * pwi[None, :, None]).astype(np.float32)
+    out["wu"] = (d["wu"] * pwd[None, None, :] * pwi[None, :, None]).astype(np.float32)
+    out["wd"] = (d["wd"] * pdi[None, None, :]).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("args", [dict(T=40, D=64, I=64, E=4, k=2),
+                                  dict(T=64, D=256, I=96, E=8, k=3, e0=2, nl=4, zipf=1.2)])
+def test_forward_mxfp8_composition_vs_torch_float8(args):
+    """The oracle's MXFP8 forward equals an emulation built from torch's float8 cast and
+    per-32-block power-of-two scales along each GEMM's K, on inputs whose blocks span 24
+    binades.  Taking any one of the four quantisation points along the other axis moves
+    the emulation far beyond the 1e-12 bound, so a wrong block axis (or a missing round
+    trip) in the oracle would fail here."""
+    cfg, d = _small(**args)
+    d = _wide_range_inputs(d)
+    ids = gen.mask_ids(d["ids"], 0.1, seed=4)
+    y = O.forward(d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0, E=cfg.E,
+                  M=cfg.M, mxfp8=True)
+    args_t = (d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], cfg.e0)
+    ref = _torch_mx_layer(*args_t).numpy()
+    nref = np.linalg.norm(ref)
+    assert np.linalg.norm(y - ref) <= 1e-12 * nref
+    for point in ("x", "wgu", "wd", "h"):
+        alt = _torch_mx_layer(*args_t, transposed=(point,)).numpy()
+        assert np.linalg.norm(alt - ref) > 1e-9 * nref, point
+    # the emulation's quantiser itself agrees with the oracle's codes and scales
+    v = np.random.default_rng(3).standard_normal((8, 96)).astype(np.float32) * 7.0
+    v *= np.ldexp(1.0, -(np.arange(96) % 24)).astype(np.float32)
+    np.testing.assert_array_equal(_torch_mx_roundtrip(torch.tensor(v)).numpy(),
+                                  O.mx_roundtrip(v))
+
+
 # ---------------------------------------------------------------------------------
 # backward
 # ---------------------------------------------------------------------------------
