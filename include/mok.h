@@ -203,10 +203,11 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
  *    ready, K loop (or sum) done, end, 0, 0], per workgroup [start, start, end, end, 0,
  *   tickets taken, 0, 0].  The region holds as many ticket records as the larger of the
  *   two launches has tickets.
- * With MOK_FLAG_UNFUSED the forward writes instead, in the region's first 8 64-bit
- * words, the earliest workgroup start and the latest workgroup end (64-bit values of the
- * same clock; an end is taken once the workgroup's memory operations have completed) of
- * its gather, GEMM1, GEMM2 and combine launches, in that order: the four phases' times.
+ * With MOK_FLAG_UNFUSED the forward writes instead: words 0-3 = the number of
+ * workgroups g0..g3 of its gather, GEMM1, GEMM2 and combine launches, words 4-7 = 0;
+ * then, launch after launch, one record per workgroup of two 64-bit values of the same
+ * clock (not truncated): its start and its end (taken once its memory operations have
+ * completed).  A launch's time is its latest end minus its earliest start.
  * The caller reads the region after the forward has completed.  Errors: MOK_E_NULL,
  * the descriptor's errors, MOK_E_UNSUPPORTED when the flag is not set. */
 #define MOK_TRACE_MAX_WORKGROUPS 1024

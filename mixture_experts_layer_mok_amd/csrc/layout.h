@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/mok.h"
 
 namespace mok {
@@ -71,6 +73,8 @@ struct Layout {
   size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
   size_t off_trace, trace_words, trace_tickets;  // MOK_FLAG_TRACE: ticket records, then
                                                 // workgroup records
+  // workgroups of the unfused gather, GEMM1, GEMM2 and combine launches
+  int64_t unf_grid[4];
   size_t total;
 };
 
@@ -184,6 +188,10 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_dyb = o; o = align_up(o + TK * 4, A);
     L->off_xb = o; o = align_up(o + TK * 4, A);
   }
+  L->unf_grid[0] = std::min<int64_t>((L->TK + 3) / 4, 1 << 20);
+  L->unf_grid[1] = L->n_mb_max * L->mt_max * L->nN1;
+  L->unf_grid[2] = L->n_mb_max * L->mt_max * L->nN2;
+  L->unf_grid[3] = std::min<int64_t>((T + 3) / 4, 1 << 20);
   L->off_trace = L->trace_words = L->trace_tickets = 0;
   if (L->trace) {
     // records for every forward tile ticket, or every backward ticket (dH, dX, dW tiles
@@ -194,6 +202,13 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
                        size_t((T + 31) / 32);
     L->trace_tickets = fwd > bwd ? fwd : bwd;
     L->trace_words = L->trace_tickets * 8 + size_t(MOK_TRACE_MAX_WORKGROUPS) * 8;
+    if (L->unfused) {
+      // the unfused forward's launches: 8 header words (their workgroup counts), then per
+      // launch and workgroup two 64-bit timestamps
+      size_t w = 8;
+      for (int ph = 0; ph < 4; ++ph) w += size_t(L->unf_grid[ph]) * 4;
+      if (w > L->trace_words) L->trace_words = w;
+    }
     L->off_trace = o; o = align_up(o + L->trace_words * 4, A);
   }
   L->total = o;

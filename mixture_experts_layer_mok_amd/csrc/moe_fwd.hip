@@ -48,6 +48,7 @@ struct FwdParams {
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int perturb;          // MOK_FLAG_PERTURB
   int64_t trace_tiles;  // MOK_FLAG_TRACE: tile records before the workgroup records
+  int64_t ph_rec[4];    // MOK_FLAG_TRACE, unfused: first 64-bit word of each launch's records
   int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
   // MXFP8: scale row strides of X / H rows and of the weight scales the tiles read, and
   // those weight scales (the caller's, or repacked copies in the workspace)
@@ -102,32 +103,34 @@ __device__ __forceinline__ void combine_if_last(const FwdParams& p, int r) {
 // ------------------------------------------------------------------------------------
 // Unfused kernels: the same steps over full-size buffers, one launch per step.
 // ------------------------------------------------------------------------------------
-// With MOK_FLAG_TRACE, launch ph (0 gather, 1 GEMM1, 2 GEMM2, 3 combine) keeps the
-// earliest start and the latest end of its workgroups, 64-bit values of the 100 MHz
-// constant clock, in 64-bit words 2 ph and 2 ph + 1 of the trace region (k_phase_init
-// sets them to the largest value and 0 before the four launches).  A workgroup's end is
-// taken once its memory operations have completed.
-__global__ __launch_bounds__(64) void k_phase_init(uint32_t* trace) {
-  unsigned long long* w = reinterpret_cast<unsigned long long*>(trace);
-  if (threadIdx.x < 8) w[threadIdx.x] = (threadIdx.x & 1) ? 0ull : ~0ull;
+// With MOK_FLAG_TRACE, every workgroup of launch ph (0 gather, 1 GEMM1, 2 GEMM2,
+// 3 combine) writes its start and end, 64-bit values of the 100 MHz constant clock, to
+// its own record: 64-bit words ph_rec[ph] + 2 blockIdx.x and + 1 of the trace region (no
+// atomics, so the records do not slow the launch down).  The end is taken once the
+// workgroup's memory operations have completed.  k_phase_init writes the four launches'
+// workgroup counts into the region's first words.
+__global__ __launch_bounds__(64) void k_phase_init(uint32_t* trace, uint32_t g0, uint32_t g1,
+                                                   uint32_t g2, uint32_t g3) {
+  if (threadIdx.x < 8) trace[threadIdx.x] = threadIdx.x == 0 ? g0 : threadIdx.x == 1 ? g1 :
+                                            threadIdx.x == 2 ? g2 : threadIdx.x == 3 ? g3 : 0u;
 }
-__device__ __forceinline__ void phase_start(const FwdParams& p, int ph) {
-  if (p.P.trace && threadIdx.x == 0)
-    atomicMin(reinterpret_cast<unsigned long long*>(p.P.trace) + 2 * ph,
-              (unsigned long long)wall_clock64());
+__device__ __forceinline__ uint64_t phase_start(const FwdParams& p) {
+  return p.P.trace ? wall_clock64() : 0ull;
 }
-__device__ __forceinline__ void phase_end(const FwdParams& p, int ph) {
+__device__ __forceinline__ void phase_end(const FwdParams& p, int ph, uint64_t t0) {
   if (!p.P.trace) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
-    atomicMax(reinterpret_cast<unsigned long long*>(p.P.trace) + 2 * ph + 1,
-              (unsigned long long)wall_clock64());
+  if (threadIdx.x == 0) {
+    uint64_t* rec = reinterpret_cast<uint64_t*>(p.P.trace) + p.ph_rec[ph] + 2 * int64_t(blockIdx.x);
+    rec[0] = t0;
+    rec[1] = wall_clock64();
+  }
 }
 
 template <bool MX>
 __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
-  phase_start(p, 0);
+  const uint64_t t0 = phase_start(p);
   const int R = int(p.P.hdr[kHdrR]);
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256) void k_gather_all(FwdParams p) {
     else
       wave_copy_row<false>(reinterpret_cast<uint16_t*>(p.P.full_x) + int64_t(r) * p.D, src, p.D);
   }
-  phase_end(p, 0);
+  phase_end(p, 0, t0);
 }
 
 template <bool MX>
@@ -172,9 +175,9 @@ __device__ __forceinline__ void gemm1_tile_unfused(const FwdParams& p) {
 
 template <bool MX>
 __global__ __launch_bounds__(512) void k_gemm1_all(FwdParams p) {
-  phase_start(p, 1);
+  const uint64_t t0 = phase_start(p);
   gemm1_tile_unfused<MX>(p);
-  phase_end(p, 1);
+  phase_end(p, 1, t0);
 }
 
 template <bool MX>
@@ -203,15 +206,15 @@ __device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
 
 template <bool MX>
 __global__ __launch_bounds__(512) void k_gemm2_all(FwdParams p) {
-  phase_start(p, 2);
+  const uint64_t t0 = phase_start(p);
   gemm2_tile_unfused<MX>(p);
-  phase_end(p, 2);
+  phase_end(p, 2, t0);
 }
 
 // One wave per token; the next token's slot rows and gates are loaded while this one is
 // summed, so that the per-token lookups do not add a memory round trip each.
 __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
-  phase_start(p, 3);
+  const uint64_t t0 = phase_start(p);
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int lane = threadIdx.x & 63;
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
     else
       wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
   }
-  phase_end(p, 3);
+  phase_end(p, 3, t0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -629,6 +632,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
   p.trace_tiles = int64_t(L.trace_tickets);
+  for (int ph = 0, w = 4; ph < 4; w += 2 * int(L.unf_grid[ph]), ++ph) p.ph_rec[ph] = w;
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);
   p.slot_xs = int64_t(L.slot_xs); p.slot_h = int64_t(L.slot_h); p.slot_hs = int64_t(L.slot_hs);
   p.slot_ab = int64_t(L.slot_ab);
@@ -665,9 +669,10 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
                        int(L.wds_ld));
   }
   if (L.unfused) {
-    if (P.trace) hipLaunchKernelGGL(k_phase_init, dim3(1), dim3(64), 0, st, P.trace);
-    const unsigned gw = unsigned(std::min<int64_t>((L.TK + 3) / 4, 1 << 20));
-    const dim3 g1(unsigned(L.n_mb_max * L.mt_max * L.nN1)), g2(unsigned(L.n_mb_max * L.mt_max * L.nN2));
+    const unsigned gw = unsigned(L.unf_grid[0]), gc = unsigned(L.unf_grid[3]);
+    const dim3 g1(unsigned(L.unf_grid[1])), g2(unsigned(L.unf_grid[2]));
+    if (P.trace)
+      hipLaunchKernelGGL(k_phase_init, dim3(1), dim3(64), 0, st, P.trace, gw, g1.x, g2.x, gc);
     if (L.mx) {
       hipLaunchKernelGGL(k_gather_all<true>, dim3(gw), dim3(256), 0, st, p);
       hipLaunchKernelGGL(k_gemm1_all<true>, g1, dim3(kThreads), 0, st, p);
@@ -677,8 +682,7 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
       hipLaunchKernelGGL(k_gemm1_all<false>, g1, dim3(kThreads), 0, st, p);
       hipLaunchKernelGGL(k_gemm2_all<false>, g2, dim3(kThreads), 0, st, p);
     }
-    hipLaunchKernelGGL(k_combine_all, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 1 << 20))),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_combine_all, dim3(gc), dim3(256), 0, st, p);
     return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
   }
   const void* kern = L.mx ? reinterpret_cast<const void*>(k_fwd_fused<true>)

@@ -131,13 +131,19 @@ PHASES = ("gather", "gemm1", "gemm2", "combine")
 
 def read_phases(layer) -> dict:
     """Durations (us) of the gather, GEMM1, GEMM2 and combine launches of the last
-    unfused forward run with MOK_FLAG_TRACE on `layer`: the span from the earliest
-    workgroup start to the latest workgroup end of each launch; synchronises."""
+    unfused forward run with MOK_FLAG_TRACE on `layer`: per launch, the latest workgroup
+    end minus the earliest workgroup start; synchronises."""
     import torch
 
     from . import _lib as L
-    off, _ = L.mok_trace_layout(layer.desc)
+    off, words = L.mok_trace_layout(layer.desc)
     torch.cuda.synchronize(layer.device)
-    raw = layer.ws[off:off + 64].cpu().numpy().view(np.uint64)
-    return {name: float(int(raw[2 * i + 1]) - int(raw[2 * i])) * TICK_US
-            for i, name in enumerate(PHASES)}
+    raw = layer.ws[off:off + words * 4].cpu().numpy()
+    grids = raw[:16].view(np.uint32)[:4].astype(np.int64)
+    rec = raw[32:].view(np.uint64).astype(np.int64)
+    out, w = {}, 0
+    for name, g in zip(PHASES, grids):
+        r = rec[w:w + 2 * g].reshape(g, 2)
+        out[name] = float(r[:, 1].max() - r[:, 0].min()) * TICK_US
+        w += 2 * g
+    return out
