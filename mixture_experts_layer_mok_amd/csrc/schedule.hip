@@ -9,12 +9,14 @@
 //
 // Three launches, no host synchronisation:
 //   count  — each wave builds an LDS histogram of its 1024-pair sub-chunk;
-//   scan   — one workgroup turns the per-sub-chunk counts into absolute bases
-//            (expert-major, sub-chunk-minor), the offsets, R, the minibatch count and
-//            the m-tile table;
+//   scan   — one workgroup turns the per-sub-chunk counts into absolute bases with one
+//            parallel prefix sum in expert-major order, and writes the offsets, R, the
+//            minibatch count and the m-tile table;
 //   place  — each wave walks its sub-chunk 64 pairs at a time; lanes routed to the
 //            same expert are grouped with a ballot and ranked with a prefix popcount,
 //            which keeps ascending (token, slot) order inside every expert.
+// Each wave issues all loads of its sub-chunk before using any: these kernels are
+// bound by memory latency, not bandwidth.
 #include "device.h"
 #include "launch.h"
 
@@ -29,11 +31,18 @@ __global__ __launch_bounds__(256) void sched_count(const int32_t* __restrict__ i
   __syncthreads();
   const int64_t sub = int64_t(blockIdx.x) * 4 + w;
   const int64_t p0 = sub * kSchedSub;
+  // all of the wave's loads first (one memory latency, not one per group of 64)
+  constexpr int kG = kSchedSub / 64;
+  int idv[kG];
+#pragma unroll
+  for (int u = 0; u < kG; ++u) {
+    const int64_t p = p0 + 64 * u + lane;
+    idv[u] = p < TK ? ids[p] : -1;
+  }
   int bad = 0;
-  for (int i = lane; i < kSchedSub; i += 64) {
-    const int64_t p = p0 + i;
-    if (p >= TK) break;
-    const int id = ids[p];
+#pragma unroll
+  for (int u = 0; u < kG; ++u) {
+    const int id = idv[u];
     if (id < -1 || id >= E) {
       ++bad;
     } else if (id >= e0 && id < e0 + nl) {
@@ -45,64 +54,70 @@ __global__ __launch_bounds__(256) void sched_count(const int32_t* __restrict__ i
   for (int e = lane; e <= nl; e += 64) blk[sub * (nl + 1) + e] = hist[w][e];
 }
 
-// One workgroup of 1024 threads.
+// Inclusive sum over the 1024 threads of the workgroup (wave prefix sums by shuffles,
+// then the 16 wave totals); *total receives the sum of all 1024 values.
+__device__ __forceinline__ int32_t block_incl_scan(int32_t v, int32_t* s_wave, int32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) s_wave[w] = v;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int32_t t = s_wave[i];
+    before += i < w ? t : 0;
+    all += t;
+  }
+  __syncthreads();  // s_wave may be rewritten by the next call
+  *total = all;
+  return v + before;
+}
+
+// One workgroup of 1024 threads.  The absolute first row of expert e's pairs in
+// sub-chunk s is an exclusive prefix sum in expert-major order, q = e * NS + s, of the
+// per-sub-chunk counts: it adds the rows of every earlier expert (the expert's offset)
+// and of the expert's earlier sub-chunks.  One parallel scan over those nl * NS counts,
+// in passes of 1024, gives every base, the offsets (the bases at s = 0) and R.
 __global__ __launch_bounds__(1024) void sched_scan(Ptrs P, int64_t NS, int nl, int M, int mt_max,
                                                    int nN1, int nN2) {
-  __shared__ int32_t s_cnt[kMaxLocalExperts + 1];
   __shared__ int32_t s_off[kMaxLocalExperts + 1];
-  __shared__ int32_t s_bad;
-  __shared__ int32_t s_part[1024];
+  __shared__ int32_t s_wave[16];
   const int tid = threadIdx.x;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  // per expert: running sum over sub-chunks (relative bases), total count
-  for (int e = tid; e < nl; e += 1024) {
-    int32_t run = 0;
-    for (int64_t s = 0; s < NS; ++s) {
-      const int32_t c = P.blk[s * (nl + 1) + e];
-      P.blk[s * (nl + 1) + e] = run;
-      run += c;
+  const int64_t n = int64_t(nl) * NS;
+  int32_t carry = 0, total = 0;
+  for (int64_t q0 = 0; q0 < n; q0 += 1024) {
+    const int64_t q = q0 + tid;
+    const int64_t e = q / NS, sc = q - e * NS;
+    int32_t* cell = P.blk + sc * (nl + 1) + e;
+    const int32_t v = q < n ? *cell : 0;
+    const int32_t excl = carry + block_incl_scan(v, s_wave, &total) - v;
+    if (q < n) {
+      *cell = excl;
+      if (sc == 0) s_off[e] = excl;
     }
-    s_cnt[e] = run;
+    carry += total;
   }
-  {
-    int32_t b = 0;
-    for (int64_t s = tid; s < NS; s += 1024) b += P.blk[s * (nl + 1) + nl];
-    if (b) atomicAdd(&s_bad, b);
-  }
+  // ids outside [-1, E): one counter per sub-chunk in column nl
+  int32_t bad = 0;
+  for (int64_t sc = tid; sc < NS; sc += 1024) bad += P.blk[sc * (nl + 1) + nl];
+  block_incl_scan(bad, s_wave, &bad);
+  if (tid == 0) s_off[nl] = carry;
   __syncthreads();
-  // exclusive scan of counts -> offsets (nl <= 1024: one element per thread)
-  {
-    int32_t v = tid < nl ? s_cnt[tid] : 0;
-    s_part[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      int32_t add = tid >= d ? s_part[tid - d] : 0;
-      __syncthreads();
-      s_part[tid] += add;
-      __syncthreads();
-    }
-    if (tid < nl) s_off[tid] = s_part[tid] - v;
-    if (tid == 0) s_off[nl] = s_part[1023];
-  }
-  __syncthreads();
-  const int32_t R = s_off[nl];
-  const int32_t n_mb = (R + M - 1) / M;
   for (int e = tid; e < nl; e += 1024) {
-    P.counts[e] = s_cnt[e];
+    P.counts[e] = s_off[e + 1] - s_off[e];
     P.offsets[e] = s_off[e];
   }
+  const int32_t R = s_off[nl];
+  const int32_t n_mb = (R + M - 1) / M;
   if (tid == 0) {
     P.offsets[nl] = R;
-    P.hdr[kHdrStatus] = s_bad ? MOK_DEV_BAD_ID : 0u;
+    P.hdr[kHdrStatus] = bad ? MOK_DEV_BAD_ID : 0u;
     P.hdr[kHdrR] = uint32_t(R);
     P.hdr[kHdrNmb] = uint32_t(n_mb);
-  }
-  // absolute bases per (sub-chunk, expert)
-  for (int64_t idx = tid; idx < NS * nl; idx += 1024) {
-    const int64_t s = idx / nl;
-    const int e = int(idx % nl);
-    P.blk[s * (nl + 1) + e] += s_off[e];
   }
   // m-tile table.  Expert e's rows are cut into m-tiles [off_e + kBM*q, +kBM) (the last
   // one may be short); minibatch mb holds the m-tiles whose first row lies in its
@@ -135,36 +150,32 @@ __global__ __launch_bounds__(1024) void sched_scan(Ptrs P, int64_t NS, int nl, i
     P.mt_cnt[mb] = cnt;
   }
   if (tid == 0) P.mb_start[n_mb] = R;
+  __threadfence();
   __syncthreads();
-  __threadfence_block();
-  // tile_base: prefix over minibatches of m-tiles * (nN1 + nN2); total m-tiles
-  {
-    int32_t carry = 0, carry_mt = 0;
-    for (int base = 0; base < n_mb; base += 1024) {
-      const int mb = base + tid;
-      const int32_t c = mb < n_mb ? P.mt_cnt[mb] : 0;
-      s_part[tid] = c;
-      __syncthreads();
-      for (int d = 1; d < 1024; d <<= 1) {
-        int32_t add = tid >= d ? s_part[tid - d] : 0;
-        __syncthreads();
-        s_part[tid] += add;
-        __syncthreads();
-      }
-      if (mb < n_mb) P.tile_base[mb] = (carry_mt + s_part[tid] - c) * (nN1 + nN2);
-      const int32_t tot = s_part[1023];
-      __syncthreads();
-      carry_mt += tot;
-      (void)carry;
-    }
-    if (tid == 0) {
-      P.tile_base[n_mb] = carry_mt * (nN1 + nN2);
-      P.hdr[kHdrMtiles] = uint32_t(carry_mt);
-      P.hdr[kHdrFwdTiles] = uint32_t(carry_mt * (nN1 + nN2));
-    }
+  // tile_base: prefix over minibatches of m-tiles * (nN1 + nN2); total m-tiles.  The
+  // counts were written by other threads of this workgroup: device-scope loads.
+  int32_t carry_mt = 0;
+  for (int base = 0; base < n_mb; base += 1024) {
+    const int mb = base + tid;
+    const int32_t c = mb < n_mb ? int32_t(__hip_atomic_load(P.mt_cnt + mb, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)) : 0;
+    int32_t tot = 0;
+    const int32_t incl = block_incl_scan(c, s_wave, &tot);
+    if (mb < n_mb) P.tile_base[mb] = (carry_mt + incl - c) * (nN1 + nN2);
+    carry_mt += tot;
+  }
+  if (tid == 0) {
+    P.tile_base[n_mb] = carry_mt * (nN1 + nN2);
+    P.hdr[kHdrMtiles] = uint32_t(carry_mt);
+    P.hdr[kHdrFwdTiles] = uint32_t(carry_mt * (nN1 + nN2));
   }
 }
 
+// Each wave places its 1024-pair sub-chunk 64 pairs at a time, in ascending pair order:
+// the lanes routed to one expert are found with a ballot (one round per distinct expert
+// among the 64) and ranked with a prefix popcount.  The wave's next free row of every
+// expert starts at the scanned base; with at most 64 local experts lane e keeps expert
+// e's in a register (no LDS round trip per round), otherwise it lives in LDS.
 __global__ __launch_bounds__(256) void sched_place(const int32_t* __restrict__ ids, int64_t TK,
                                                    int e0, int nl,
                                                    const int32_t* __restrict__ blk,
@@ -173,29 +184,47 @@ __global__ __launch_bounds__(256) void sched_place(const int32_t* __restrict__ i
   __shared__ int32_t base[4][kMaxLocalExperts];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t sub = int64_t(blockIdx.x) * 4 + w;
-  for (int e = lane; e < nl; e += 64) base[w][e] = blk[sub * (nl + 1) + e];
-  __syncthreads();
   const int64_t p0 = sub * kSchedSub;
-  for (int step = 0; step < kSchedSub / 64; ++step) {
-    const int64_t p = p0 + step * 64 + lane;
+  const bool in_regs = nl <= 64;
+  int32_t base_v = 0;
+  if (in_regs) {
+    base_v = lane < nl ? blk[sub * (nl + 1) + lane] : 0;
+  } else {
+    for (int e = lane; e < nl; e += 64) base[w][e] = blk[sub * (nl + 1) + e];
+  }
+  constexpr int kG = kSchedSub / 64;
+  int idv[kG];
+#pragma unroll
+  for (int u = 0; u < kG; ++u) {
+    const int64_t p = p0 + 64 * u + lane;
+    idv[u] = p < TK ? ids[p] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int step = 0; step < kG; ++step) {
     if (p0 + step * 64 >= TK) break;  // wave-uniform
+    const int64_t p = p0 + step * 64 + lane;
     const bool valid = p < TK;
-    const int id = valid ? ids[p] : -1;
+    const int id = idv[step];
     const bool local = valid && id >= e0 && id < e0 + nl;
     const int e = id - e0;
     int32_t row = -1;
     uint64_t todo = __ballot(local);
     while (todo) {
       const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int el = __shfl(e, leader);
+      const int el = __builtin_amdgcn_readfirstlane(__shfl(e, leader));
       const uint64_t m = __ballot(local && e == el);
-      const int32_t b = base[w][el];
+      const int32_t b = in_regs ? __builtin_amdgcn_readlane(base_v, el) : base[w][el];
       if (local && e == el) {
         const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
                                                          __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
         row = b + int32_t(below);
       }
-      if (lane == leader) base[w][el] = b + __popcll(m);
+      if (in_regs) {
+        if (lane == el) base_v = b + __popcll(m);
+      } else if (lane == leader) {
+        base[w][el] = b + __popcll(m);
+      }
       todo &= ~m;
     }
     if (valid) {
