@@ -213,6 +213,26 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
 #define MOK_TRACE_MAX_WORKGROUPS 1024
 mok_status_t mok_trace_layout(const mok_desc_t* desc, size_t* offset_bytes, size_t* words);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mok_schedule followed by mok_moe_fwd
+ * in one call, same kernels and results, with the workspace taken from a static device
+ * area of MOK_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on, from
+ * the first call there until the process ends.  The call allocates nothing.
+ * Arguments as for mok_moe_fwd (bf16 or MXFP8, same alignment rules), plus dev_status:
+ * NULL, or a 4-byte-aligned device word that receives the call's MOK_DEV_* status bits.
+ * Errors (returned before anything is enqueued): those of mok_moe_fwd; MOK_E_WORKSPACE
+ * when mok_workspace_size(desc) exceeds MOK_NOALLOC_SCRATCH_BYTES; MOK_E_UNSUPPORTED with
+ * MOK_FLAG_SAVE_FOR_BWD or MOK_FLAG_TRACE (their results would stay in the area).
+ * Every call on a GPU uses that GPU's one area, which keeps the last call's contents:
+ * calls that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Asynchronous on stream. */
+#define MOK_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+mok_status_t mok_moe_fwd_noalloc(const mok_desc_t* desc, const void* x, const int32_t* topk_ids,
+                                 const float* topk_w, const void* w_gate, const void* w_up,
+                                 const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                 const uint8_t* s_down, void* y, uint32_t* dev_status,
+                                 void* stream);
+
 /* Synchronise `stream`, then read the sticky device status word (MOK_DEV_* bits). */
 mok_status_t mok_read_device_status(const void* ws, void* stream, uint32_t* out);
 

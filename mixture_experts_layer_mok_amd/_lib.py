@@ -36,7 +36,7 @@ MOK_DEV_TIMEOUT = 0x2
 EXPORTS = (
     "mok_workspace_size", "mok_schedule", "mok_schedule_tables", "mok_quantize_mx",
     "mok_moe_fwd", "mok_moe_bwd", "mok_read_device_status", "mok_status_string",
-    "mok_device_cus", "mok_trace_layout",
+    "mok_device_cus", "mok_trace_layout", "mok_moe_fwd_noalloc",
 )
 
 
@@ -92,6 +92,8 @@ def load() -> ctypes.CDLL:
         "mok_device_cus": (ctypes.c_int32, []),
         "mok_trace_layout": (ctypes.c_int, [D, ctypes.POINTER(ctypes.c_size_t),
                                             ctypes.POINTER(ctypes.c_size_t)]),
+        "mok_moe_fwd_noalloc": (ctypes.c_int, [D, vp, i32p, f32p, vp, vp, vp, u8p, u8p, u8p, vp,
+                                               vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -192,6 +194,14 @@ def mok_moe_bwd(desc, dy, x, topk_ids, topk_w, w_gate, w_up, w_down, dx, d_topk_
         ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), _ptr(dx), _ptr(d_topk_w), _ptr(dw_gate), _ptr(dw_up),
         _ptr(dw_down), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mok_moe_fwd_noalloc(desc, x, topk_ids, topk_w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                        y, dev_status=None, stream=None) -> None:
+    _check("mok_moe_fwd_noalloc", load().mok_moe_fwd_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(dev_status),
+        _stream(stream)))
 
 
 def mok_read_device_status(ws, stream=None) -> int:

@@ -1,0 +1,85 @@
+"""mok_moe_fwd_noalloc: schedule + forward with the workspace in the library's static
+device area, for callers that cannot allocate.  Two calls in a row on the same area (the
+second with a smaller input) must each equal mok_schedule + mok_moe_fwd on a caller-owned
+workspace bit for bit, in bf16 and MXFP8; the status word reaches the caller's pointer;
+requests the area cannot serve are refused before anything is enqueued."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_mok_amd import _lib as L
+from mixture_experts_layer_mok_amd import gen
+from mixture_experts_layer_mok_amd.layer import MoKLayer
+from tests.gpu_util import DevInputs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _reference(cfg, dev, precision, w, sc):
+    layer = MoKLayer(L.desc_from_config(cfg, precision=precision))
+    layer.schedule(dev.ids)
+    y = layer.forward(dev.x, dev.ids, dev.gates, *w, scales=sc)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    return y
+
+
+def _weights(cfg, dev, precision):
+    if precision == L.MOK_PREC_BF16:
+        return (dev.wg, dev.wu, dev.wd), (None, None, None)
+    q = MoKLayer(L.desc_from_config(cfg, precision=precision))
+    cs = [q.quantize_weights(t) for t in (dev.wg, dev.wu, dev.wd)]
+    return tuple(c for c, _ in cs), tuple(s for _, s in cs)
+
+
+@pytest.mark.parametrize("precision", [L.MOK_PREC_BF16, L.MOK_PREC_MXFP8], ids=["bf16", "mxfp8"])
+def test_noalloc_matches_workspace_forward_twice(precision):
+    cases = [gen.CONFIGS[2],
+             gen.small_config("smaller", T=300, D=192, I=192, E=6, k=2, M=96, S=2, comm_cus=8)]
+    status = torch.full((1,), 0xFFFF, dtype=torch.int32, device="cuda")
+    for i, cfg in enumerate(cases):
+        say(f"[noalloc] call {i}: {cfg.name} precision={precision}")
+        d = gen.make_inputs(cfg, seed=40 + i)
+        dev = DevInputs(d)
+        w, sc = _weights(cfg, dev, precision)
+        ref = _reference(cfg, dev, precision, w, sc)
+        y = torch.full((cfg.T, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        L.mok_moe_fwd_noalloc(L.desc_from_config(cfg, precision=precision), dev.x, dev.ids,
+                              dev.gates, *w, *sc, y, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert torch.equal(y, ref), f"call {i} differs from the workspace forward"
+
+
+def test_noalloc_status_and_refusals():
+    cfg = gen.small_config("bad-ids", T=200, D=128, I=128, E=8, k=2, M=64, S=2, comm_cus=8)
+    d = gen.make_inputs(cfg, seed=5)
+    ids = d["ids"].copy()
+    ids[::7, 0] = cfg.E + 3
+    dev = DevInputs(d, ids=ids)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device="cuda")
+    L.mok_moe_fwd_noalloc(L.desc_from_config(cfg), dev.x, dev.ids, dev.gates, dev.wg, dev.wu,
+                          dev.wd, None, None, None, y, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == L.MOK_DEV_BAD_ID
+    layer = MoKLayer(L.desc_from_config(cfg))
+    layer.schedule(dev.ids)
+    ref = layer.forward(dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd)
+    torch.cuda.synchronize()
+    assert layer.status() == L.MOK_DEV_BAD_ID
+    assert torch.equal(y, ref)
+    # refusals, each before anything is enqueued (y keeps its sentinel)
+    y.fill_(1.0)
+    big = gen.CONFIGS[3]  # its workspace (about 2 GB) exceeds the static area
+    for desc, code in ((L.desc_from_config(big), L.MOK_E_WORKSPACE),
+                       (L.desc_from_config(cfg, flags=L.MOK_FLAG_SAVE_FOR_BWD),
+                        L.MOK_E_UNSUPPORTED),
+                       (L.desc_from_config(cfg, flags=L.MOK_FLAG_TRACE), L.MOK_E_UNSUPPORTED)):
+        with pytest.raises(L.MokError) as ei:
+            L.mok_moe_fwd_noalloc(desc, dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd, None,
+                                  None, None, y, status)
+        assert ei.value.code == code
+    torch.cuda.synchronize()
+    assert bool((y == 1.0).all())
+    assert np.isfinite(y.float().cpu().numpy()).all()
