@@ -70,7 +70,9 @@ typedef enum {
 
 /* flags */
 #define MOK_FLAG_SAVE_FOR_BWD 0x1u  /* forward keeps X and the gate/up pre-activations of
-                                       the resident minibatches for mok_moe_bwd          */
+                                       the resident minibatches for mok_moe_bwd (MXFP8:
+                                       the pre-activations of every routed row, for
+                                       mok_moe_bwd_mx)                                   */
 #define MOK_FLAG_UNFUSED 0x2u       /* run the same steps as separate kernels over
                                        full-size buffers (comparison / phase timing)     */
 #define MOK_FLAG_SHORT_WAITS 0x4u   /* bounded waits of the fused forward and of the
@@ -110,7 +112,7 @@ typedef struct {
   int32_t ring_slots;        /* S: slots in the ring (>= 1)                             */
   int32_t comm_cus;          /* workgroups doing dispatch/combine in the fused kernel:
                                 1 .. (device CUs - 1), checked by mok_moe_fwd            */
-  int32_t precision;         /* MOK_PREC_BF16 or MOK_PREC_MXFP8 (forward only)          */
+  int32_t precision;         /* MOK_PREC_BF16 or MOK_PREC_MXFP8                         */
   uint32_t flags;            /* MOK_FLAG_*                                              */
 } mok_desc_t;
 
@@ -171,7 +173,8 @@ mok_status_t mok_moe_fwd(const mok_desc_t* desc, const void* x, const int32_t* t
                          const uint8_t* s_down, void* y, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* Backward (bf16) ([L] section 02: reverse-combine pulls dY, reverse-dispatch pushes dX;
+/* Backward (bf16; MXFP8: mok_moe_bwd_mx) ([L] section 02: reverse-combine pulls dY,
+ * reverse-dispatch pushes dX;
  * [M] design decisions: the ring is walked in reverse to limit replay of forward
  * activations, and the router-weight gradient is formed inside the SwiGLU backward).
  * Needs the workspace of a preceding mok_moe_fwd run with MOK_FLAG_SAVE_FOR_BWD and the
@@ -188,6 +191,46 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
                          float* dw_gate, float* dw_up, float* dw_down, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Transposing MXFP8 quantiser for the backward's weight operands, whose contraction runs
+ * over the stored rows ([L] section 03: the MXFP8 mode).  src [batch, rows, cols] bf16
+ * (rows a multiple of 32) -> codes[b][c][r] = e4m3 code of src[b][r][c] at
+ * codes + (b * cols + c) * ld_codes + r, and one e8m0 scale per 32 consecutive r at
+ * scales + (b * cols + c) * ld_scales + r / 32; the same rule as mok_quantize_mx, so the
+ * result equals mok_quantize_mx of each transposed matrix.  ld_codes >= rows and a
+ * multiple of 16, ld_scales >= rows / 32; codes 16-byte aligned (MOK_E_SHAPE otherwise).
+ * The MXFP8 backward takes
+ *   wd_t  = W_down^T: mok_quantize_mx_t(w_down, E_loc, D, I, codes, D, scales, D / 32)
+ *           -> codes [E_loc, I, D], scales [E_loc, I, D / 32];
+ *   wgu_t = [W_gate; W_up]^T, row d = W_gate[:, d] then W_up[:, d]: two calls,
+ *           (w_gate, E_loc, I, D, codes, 2I, scales, 2I / 32) and
+ *           (w_up, E_loc, I, D, codes + I, 2I, scales + I / 32, 2I / 32)
+ *           -> codes [E_loc, D, 2I], scales [E_loc, D, 2I / 32].
+ * Asynchronous on stream; the caller owns every buffer. */
+mok_status_t mok_quantize_mx_t(const void* src_bf16, int64_t batch, int32_t rows, int32_t cols,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                               int64_t ld_scales, void* stream);
+
+/* MXFP8 backward ([L] section 03: MXFP8 forward and backward; [L] section 02 and [M]
+ * design decisions as for mok_moe_bwd).  Needs the workspace of a preceding MXFP8
+ * mok_moe_fwd run with MOK_FLAG_SAVE_FOR_BWD (which keeps a, b of every routed row) and
+ * the same inputs; outputs and their layouts as for mok_moe_bwd.  The two data-gradient
+ * GEMMs run on scaled e4m3 MFMA with fp32 accumulation, each operand quantised along
+ * that GEMM's K in blocks of 32: u = dY W_down with dY rows quantised along D (inside the
+ * call) and W_down^T codes wd_t / wd_t_scales; dx = [da | db] [W_gate; W_up] with
+ * [da | db] rows quantised along I (inside the call) and wgu_t / wgu_t_scales (layouts
+ * above, from mok_quantize_mx_t).  dG, da, db are formed from u as in mok_moe_bwd; the
+ * weight gradients dW_gate = da^T x, dW_up = db^T x, dW_down = (g dY)^T h run in bf16
+ * on the unquantised rows (x, dY bf16; da, db, g h rounded to bf16), fp32 accumulation.
+ * dy, x, dx and the codes 16-byte aligned, the scales 4-byte aligned.  Errors as for
+ * mok_moe_bwd; MOK_E_UNSUPPORTED unless desc is MXFP8 with MOK_FLAG_SAVE_FOR_BWD.
+ * Asynchronous on stream. */
+mok_status_t mok_moe_bwd_mx(const mok_desc_t* desc, const void* dy, const void* x,
+                            const int32_t* topk_ids, const float* topk_w, const uint8_t* wd_t,
+                            const uint8_t* wd_t_scales, const uint8_t* wgu_t,
+                            const uint8_t* wgu_t_scales, void* dx, float* d_topk_w,
+                            float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Where the trace of a forward run with MOK_FLAG_TRACE lies in the workspace (host
  * only): *offset_bytes from the workspace start, *words uint32 words.  Timestamps are
  * the low 32 bits of the GPU's 100 MHz constant clock (10 ns units).  The region holds
@@ -199,7 +242,8 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
  *     [start, minibatch 0 gathered (fill done), role done, drain done,
  *      role (1 comm, 0 compute), drain chunks taken, 0, 0].
  * The backward's records (which replace the forward's) use the same layout: per ticket
- *   [workgroup, kind (0 dH, 1 dX, 2 dW tile, 3 row-sum chunk), ticket taken, inputs
+ *   [workgroup, kind (0 dH, 1 dX, 2 dW tile, 3 row-sum chunk, 4 MXFP8 quantisation of an
+ *    m-tile's [da | db] rows), ticket taken, inputs
  *    ready, K loop (or sum) done, end, 0, 0], per workgroup [start, start, end, end, 0,
  *   tickets taken, 0, 0].  The region holds as many ticket records as the larger of the
  *   two launches has tickets.

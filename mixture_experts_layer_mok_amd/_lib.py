@@ -36,7 +36,8 @@ MOK_DEV_TIMEOUT = 0x2
 EXPORTS = (
     "mok_workspace_size", "mok_schedule", "mok_schedule_tables", "mok_quantize_mx",
     "mok_moe_fwd", "mok_moe_bwd", "mok_read_device_status", "mok_status_string",
-    "mok_device_cus", "mok_trace_layout", "mok_moe_fwd_noalloc",
+    "mok_device_cus", "mok_trace_layout", "mok_moe_fwd_noalloc", "mok_quantize_mx_t",
+    "mok_moe_bwd_mx",
 )
 
 
@@ -94,6 +95,10 @@ def load() -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_size_t)]),
         "mok_moe_fwd_noalloc": (ctypes.c_int, [D, vp, i32p, f32p, vp, vp, vp, u8p, u8p, u8p, vp,
                                                vp, vp]),
+        "mok_quantize_mx_t": (ctypes.c_int, [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             u8p, ctypes.c_int64, u8p, ctypes.c_int64, vp]),
+        "mok_moe_bwd_mx": (ctypes.c_int, [D, vp, vp, i32p, f32p, u8p, u8p, u8p, u8p, vp, f32p,
+                                          f32p, f32p, f32p, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -202,6 +207,22 @@ def mok_moe_fwd_noalloc(desc, x, topk_ids, topk_w, w_gate, w_up, w_down, s_gate,
         ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(dev_status),
         _stream(stream)))
+
+
+def mok_quantize_mx_t(src, batch, rows, cols, codes, ld_codes, scales, ld_scales,
+                      stream=None) -> None:
+    _check("mok_quantize_mx_t", load().mok_quantize_mx_t(
+        _ptr(src), int(batch), int(rows), int(cols), _ptr(codes), int(ld_codes), _ptr(scales),
+        int(ld_scales), _stream(stream)))
+
+
+def mok_moe_bwd_mx(desc, dy, x, topk_ids, topk_w, wd_t, wd_t_scales, wgu_t, wgu_t_scales, dx,
+                   d_topk_w, dw_gate, dw_up, dw_down, ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("mok_moe_bwd_mx", load().mok_moe_bwd_mx(
+        ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(wd_t),
+        _ptr(wd_t_scales), _ptr(wgu_t), _ptr(wgu_t_scales), _ptr(dx), _ptr(d_topk_w),
+        _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mok_read_device_status(ws, stream=None) -> int:

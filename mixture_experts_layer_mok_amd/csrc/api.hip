@@ -126,7 +126,8 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
   mok_status_t s = make_layout(desc, &L);
   if (s != MOK_OK) return s;
   if ((s = check_ws(L, ws, ws_bytes)) != MOK_OK) return s;
-  if (!L.save || L.mx) return MOK_E_UNSUPPORTED;  // needs a bf16 forward that saved
+  if (!L.save || L.mx) return MOK_E_UNSUPPORTED;  // needs a bf16 forward that saved (MXFP8:
+                                                  // mok_moe_bwd_mx)
   if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
       !aligned(w_down, 16) || !aligned(dx, 16))
     return MOK_E_SHAPE;
@@ -143,7 +144,55 @@ mok_status_t mok_moe_bwd(const mok_desc_t* desc, const void* dy, const void* x,
   a.dwg = dw_gate;
   a.dwu = dw_up;
   a.dwd = dw_down;
+  a.wdt = a.wdts = a.wgut = a.wguts = nullptr;
   return launch_backward(L, make_ptrs(L, ws), a, static_cast<hipStream_t>(stream));
+}
+
+mok_status_t mok_moe_bwd_mx(const mok_desc_t* desc, const void* dy, const void* x,
+                            const int32_t* topk_ids, const float* topk_w, const uint8_t* wd_t,
+                            const uint8_t* wd_t_scales, const uint8_t* wgu_t,
+                            const uint8_t* wgu_t_scales, void* dx, float* d_topk_w,
+                            float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!desc || !dy || !x || !topk_ids || !topk_w || !wd_t || !wd_t_scales || !wgu_t ||
+      !wgu_t_scales || !dx || !d_topk_w || !dw_gate || !dw_up || !dw_down)
+    return MOK_E_NULL;
+  Layout L;
+  mok_status_t s = make_layout(desc, &L);
+  if (s != MOK_OK) return s;
+  if ((s = check_ws(L, ws, ws_bytes)) != MOK_OK) return s;
+  if (!L.save || !L.mx) return MOK_E_UNSUPPORTED;  // needs a MXFP8 forward that saved
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(wd_t, 16) || !aligned(wgu_t, 16) ||
+      !aligned(dx, 16) || !aligned(wd_t_scales, 4) || !aligned(wgu_t_scales, 4))
+    return MOK_E_SHAPE;
+  BwdArgs a;
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = topk_ids;
+  a.gates = topk_w;
+  a.wg = a.wu = a.wd = nullptr;
+  a.dx = static_cast<uint16_t*>(dx);
+  a.dg = d_topk_w;
+  a.dwg = dw_gate;
+  a.dwu = dw_up;
+  a.dwd = dw_down;
+  a.wdt = wd_t;
+  a.wdts = wd_t_scales;
+  a.wgut = wgu_t;
+  a.wguts = wgu_t_scales;
+  return launch_backward(L, make_ptrs(L, ws), a, static_cast<hipStream_t>(stream));
+}
+
+mok_status_t mok_quantize_mx_t(const void* src_bf16, int64_t batch, int32_t rows, int32_t cols,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                               int64_t ld_scales, void* stream) {
+  if (!src_bf16 || !codes || !scales) return MOK_E_NULL;
+  if (batch < 0 || rows < 32 || rows % 32 != 0 || cols < 1 || ld_codes < rows ||
+      ld_codes % 16 != 0 || ld_scales < rows / 32)
+    return MOK_E_SHAPE;
+  if (!aligned(src_bf16, 2) || !aligned(codes, 16)) return MOK_E_SHAPE;
+  return launch_quantize_mx_t(static_cast<const uint16_t*>(src_bf16), batch, rows, cols, codes,
+                              ld_codes, scales, ld_scales, static_cast<hipStream_t>(stream));
 }
 
 mok_status_t mok_read_device_status(const void* ws, void* stream, uint32_t* out) {

@@ -37,6 +37,11 @@ struct Ptrs {
   uint16_t* gh;       // [T*k, I] gate weight times h per routed row (dW_down operand)
   uint32_t* dyb;      // [T*k] byte offset of each routed row's dY row in dy
   uint32_t* xb;       // [T*k] byte offset of each routed row's X row (ring or x)
+  uint8_t* dyq;       // MXFP8 backward: dY rows quantised along D, [T*k, D] codes
+  uint8_t* dyqs;      //   and [T*k, xs_ld] scales
+  uint8_t* dabq;      //   [da | db] rows quantised along I: [T*k, 2I] codes
+  uint8_t* dabqs;     //   and [T*k, 2I / 32] scales
+  uint8_t* wdts;      //   W_down^T scales repacked to the tile's stride (D % 128 != 0)
   uint32_t* trace;    // MOK_FLAG_TRACE: tile records, then workgroup records; else null
 };
 
@@ -73,6 +78,12 @@ inline Ptrs make_ptrs(const Layout& L, void* ws) {
   P.dyb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_dyb) : nullptr;
   P.xb = L.save ? reinterpret_cast<uint32_t*>(b + L.off_xb) : nullptr;
   P.trace = L.trace ? reinterpret_cast<uint32_t*>(b + L.off_trace) : nullptr;
+  const bool mxb = L.mx && L.save;
+  P.dyq = mxb ? b + L.off_dyq : nullptr;
+  P.dyqs = mxb ? b + L.off_dyqs : nullptr;
+  P.dabq = mxb ? b + L.off_dabq : nullptr;
+  P.dabqs = mxb ? b + L.off_dabqs : nullptr;
+  P.wdts = L.repack_wdt ? b + L.off_wdts : nullptr;
   return P;
 }
 
@@ -108,8 +119,21 @@ struct BwdArgs {
   float* dwg;
   float* dwu;
   float* dwd;
+  // MXFP8 backward: W_down^T codes [E_loc, I, D] + scales [E_loc, I, D/32], and
+  // [W_gate; W_up]^T codes [E_loc, D, 2I] + scales [E_loc, D, 2I/32] (null for bf16)
+  const uint8_t* wdt;
+  const uint8_t* wdts;
+  const uint8_t* wgut;
+  const uint8_t* wguts;
 };
 mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, hipStream_t st);
+// Weight scale rows of src_ld bytes copied to rows of dst_ld >= src_ld bytes (the MX
+// tile's stride of one dword per 128-wide K step), padding with 127 (scale 1).
+void launch_mx_repack(const uint8_t* src, int64_t rows, int src_ld, uint8_t* dst, int dst_ld,
+                      hipStream_t st);
+mok_status_t launch_quantize_mx_t(const uint16_t* src, int64_t batch, int32_t rows, int32_t cols,
+                                  uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                                  hipStream_t st);
 mok_status_t launch_quantize_mx(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
                                 uint8_t* scales, hipStream_t st);
 

@@ -71,6 +71,13 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
   size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
+  // MXFP8 backward (MXFP8 forward that saves): dY rows gathered and quantised along D
+  // (codes [T*k, D], scales [T*k, xs_ld]), [da | db] rows quantised along I per half
+  // (codes [T*k, 2I], scales [T*k, 2I / 32]), and W_down^T's scales repacked to the
+  // tile's stride when D % 128 != 0
+  size_t off_dyq, off_dyqs, off_dabq, off_dabqs, off_wdts;
+  int64_t abq_ld;
+  bool repack_wdt;
   size_t off_trace, trace_words, trace_tickets;  // MOK_FLAG_TRACE: ticket records, then
                                                 // workgroup records
   // workgroups of the unfused gather, GEMM1, GEMM2 and combine launches
@@ -105,7 +112,6 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->short_waits = (d->flags & MOK_FLAG_SHORT_WAITS) != 0;
   L->perturb = (d->flags & MOK_FLAG_PERTURB) != 0;
   L->trace = (d->flags & MOK_FLAG_TRACE) != 0;
-  if (L->mx && L->save) return MOK_E_UNSUPPORTED;  // MXFP8 backward is not built
   L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
   L->NS = L->NB * (kSchedChunk / kSchedSub);
   L->n_mb_max = (L->TK + M - 1) / M;
@@ -149,7 +155,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->slot_xs = so; so = align_up(so + (L->mx ? SR * L->xs_ld : 0), A);
   L->slot_h = so; so = align_up(so + SR * I * (L->mx ? 1 : 2), A);
   L->slot_hs = so; so = align_up(so + (L->mx ? SR * L->hs_ld : 0), A);
-  L->slot_ab = so; so = align_up(so + (L->save ? SR * 2 * I * 2 : 0), A);
+  L->slot_ab = so; so = align_up(so + (L->save && !L->mx ? SR * 2 * I * 2 : 0), A);
   L->slot_bytes = so;
   L->off_ring = o; o = align_up(o + L->slot_bytes * S, A);
   // full-size buffers for the unfused path
@@ -188,6 +194,17 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     L->off_dyb = o; o = align_up(o + TK * 4, A);
     L->off_xb = o; o = align_up(o + TK * 4, A);
   }
+  L->off_dyq = L->off_dyqs = L->off_dabq = L->off_dabqs = L->off_wdts = 0;
+  L->abq_ld = 2 * I / 32;  // I % 64 == 0: 2I is a whole number of 128-wide steps
+  L->repack_wdt = L->mx && L->save && D % 128 != 0;
+  if (L->mx && L->save) {
+    const size_t TK = size_t(L->TK);
+    L->off_dyq = o; o = align_up(o + TK * D, A);
+    L->off_dyqs = o; o = align_up(o + TK * L->xs_ld, A);
+    L->off_dabq = o; o = align_up(o + TK * 2 * I, A);
+    L->off_dabqs = o; o = align_up(o + TK * L->abq_ld, A);
+    if (L->repack_wdt) { L->off_wdts = o; o = align_up(o + size_t(nl) * I * L->xs_ld, A); }
+  }
   L->unf_grid[0] = std::min<int64_t>((L->TK + 3) / 4, 1 << 20);
   L->unf_grid[1] = L->n_mb_max * L->mt_max * L->nN1;
   L->unf_grid[2] = L->n_mb_max * L->mt_max * L->nN2;
@@ -198,8 +215,8 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
     // and row-sum chunks of 32 tokens), whichever is more
     const size_t nDt = size_t((D + kBN2 - 1) / kBN2), nIt = size_t((I + kBN2 - 1) / kBN2);
     const size_t fwd = size_t(L->n_mb_max) * L->mt_max * (L->nN1 + L->nN2);
-    const size_t bwd = size_t(L->n_mb_max) * L->mt_max * (nIt + nDt) + size_t(nl) * 3 * nDt * nIt +
-                       size_t((T + 31) / 32);
+    const size_t bwd = size_t(L->n_mb_max) * L->mt_max * (nIt + nDt + (L->mx ? 1 : 0)) +
+                       size_t(nl) * 3 * nDt * nIt + size_t((T + 31) / 32);
     L->trace_tickets = fwd > bwd ? fwd : bwd;
     L->trace_words = L->trace_tickets * 8 + size_t(MOK_TRACE_MAX_WORKGROUPS) * 8;
     if (L->unfused) {

@@ -23,6 +23,16 @@
 // epilogue reads their a, b there), and only minibatches whose slot was recycled,
 // mb < n_mb - S, are replayed into a row buffer.  An unfused forward that saves for the
 // backward writes a, b of every row, and nothing is replayed.
+//
+// MXFP8 (Leiphone article on MoK, section 03: the MXFP8 mode covers the backward too):
+// the two GEMMs that produce data gradients run on the scaled MFMA tile, each operand
+// quantised along that GEMM's K in blocks of 32 — dH: dY rows along D (gathered and
+// quantised by k_bwd_dyq) times W_down^T along D; dX: [da | db] rows along I (quantised
+// per m-tile inside the persistent launch, once its dH tiles are done) times
+// [W_gate; W_up]^T along I.  The transposed weight codes are made before the layer
+// (mok_quantize_mx_t), as the forward's are.  The weight-gradient GEMMs stay bf16 with
+// fp32 accumulation, on the same bf16 rows as the bf16 backward.  The MXFP8 forward that
+// saves keeps a, b of every row, so nothing is replayed.
 #include <algorithm>
 
 #include "tile_ops.h"
@@ -41,6 +51,11 @@ struct BwdParams {
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int perturb;          // MOK_FLAG_PERTURB
   int64_t trace_tickets; // MOK_FLAG_TRACE: ticket records before the workgroup records
+  // MXFP8: scale row strides of the dY rows (xs_ld), of the [da | db] rows and the
+  // [W_gate; W_up]^T rows (abq_ld = 2I / 32), and the W_down^T scales the tiles read
+  // (the caller's, or repacked in the workspace) with their stride
+  int64_t xs_ld, abq_ld, wdts_ld;
+  const uint8_t* wdts;
 };
 
 // a, b of the rows of m-tile e in minibatch mb: in the ring slot while the minibatch is
@@ -94,6 +109,16 @@ __global__ __launch_bounds__(256) void k_bwd_rows(BwdParams p) {
   }
 }
 
+// MXFP8: dY row perm[r] / k of every routed row r, quantised along D into row r of the
+// dY code buffer (one wave per row).
+__global__ __launch_bounds__(256) void k_bwd_dyq(BwdParams p) {
+  const int R = int(p.P.hdr[kHdrR]);
+  const int nw = gridDim.x * 4;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += nw)
+    wave_quant_row<false>(p.P.dyq + int64_t(r) * p.D, p.P.dyqs + int64_t(r) * p.xs_ld,
+                          p.a.dy + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+}
+
 // ------------------------------------------------------------------------------------
 // GEMM kernels (one m-tile of the schedule's table per workgroup row)
 // ------------------------------------------------------------------------------------
@@ -144,18 +169,31 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
 // dH tile (m-tile g, column tile nt): u = dY rows x W_down[e] (K = D over the rows of
 // W_down, read K-major), fused SwiGLU backward and dG partials.  da, db are stored at
 // device scope: dX tiles on other XCDs read them in the same launch.
+template <bool MX>
 __device__ __forceinline__ uint32_t dh_tile(const BwdParams& p, int g, int nt) {
   const int64_t wsz = int64_t(p.I) * p.D;
   int4 e;
   int mb;
   mtile_at(p, g, e, mb);
   const int n0 = nt * kBN2;
-  const uint16_t* wd = p.a.wd + e.z * wsz;
-  KmOp a, b;
-  km_init_kc_gather(a, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y);
-  km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
   TileAcc acc;
-  tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
+  if (MX) {
+    // A = the m-tile's quantised dY rows (written by the previous launch), B = W_down^T
+    // codes of the expert: rows n0 .. n0 + 255 of [I, D], K = D
+    const uint8_t* B = p.a.wdt + int64_t(e.z) * wsz;
+    const uint8_t* Bs = p.wdts + int64_t(e.z) * p.I * p.wdts_ld;
+    MxSrc src;
+    mx_src_init(src, geom::kSplit, p.P.dyq + int64_t(e.x) * p.D,
+                p.P.dyqs + int64_t(e.x) * p.xs_ld, p.D, p.xs_ld, e.y, B, Bs, B, Bs, p.D,
+                p.wdts_ld, n0, n0 + 128, p.I, p.D);
+    mx_gemm<false>(src, p.D, acc);
+  } else {
+    const uint16_t* wd = p.a.wd + e.z * wsz;
+    KmOp a, b;
+    km_init_kc_gather(a, p.a.dy, p.D, p.P.perm + e.x, p.k, e.y);
+    km_init_weights(b, wd, wd, p.D, p.I, n0, p.I);
+    tile_gemm_km<kKC, kKW>(a, b, p.D / kBK, acc);
+  }
   const uint32_t t_k = uint32_t(wall_clock64());
   epi_dh<kCpolDev>(acc, e.y, e.x, n0, p.I, ab_rows(p, e, mb), p.a.gates, p.P.perm, p.P.bdab,
                    p.P.gh, p.P.dgpart, nt, p.nNdh);
@@ -166,6 +204,7 @@ __device__ __forceinline__ uint32_t dh_tile(const BwdParams& p, int g, int nt) {
 // the rows of W_gate, then W_up, read K-major), pushed to their pairs.  The da, db rows
 // come from dH tiles of the same launch, so they are read at device scope, and the dx
 // rows are stored at device scope for the row sums of the same launch.
+template <bool MX>
 __device__ __forceinline__ uint32_t dx_tile(const BwdParams& p, int g, int nt) {
   const int64_t K = 2 * int64_t(p.I);
   const int64_t wsz = int64_t(p.I) * p.D;
@@ -173,14 +212,41 @@ __device__ __forceinline__ uint32_t dx_tile(const BwdParams& p, int g, int nt) {
   int mb;
   mtile_at(p, g, e, mb);
   const int n0 = nt * kBN2;
-  KmOp a, b;
-  km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
-  km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
   TileAcc acc;
-  tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
+  if (MX) {
+    // A = the m-tile's quantised [da | db] rows (written by this launch on other XCDs:
+    // device-scope loads), B = [W_gate; W_up]^T codes of the expert: rows n0 .. n0 + 255
+    // of [D, 2I], K = 2I
+    const uint8_t* B = p.a.wgut + int64_t(e.z) * 2 * wsz;
+    const uint8_t* Bs = p.a.wguts + int64_t(e.z) * p.D * p.abq_ld;
+    MxSrc src;
+    mx_src_init(src, geom::kSplit, p.P.dabq + int64_t(e.x) * K, p.P.dabqs + int64_t(e.x) * p.abq_ld,
+                K, p.abq_ld, e.y, B, Bs, B, Bs, K, p.abq_ld, n0, n0 + 128, p.D, int(K));
+    mx_gemm<true>(src, int(K), acc);
+  } else {
+    KmOp a, b;
+    km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
+    km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
+    tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
+  }
   const uint32_t t_k = uint32_t(wall_clock64());
   epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf);
   return t_k;
+}
+
+// MXFP8: the [da | db] rows of m-tile g quantised along I (blocks of 32; I % 32 == 0, so
+// a block never mixes da and db), one wave per row.  The rows come from this launch's dH
+// tiles and go to its dX tiles, on other XCDs: device-scope loads and stores.
+__device__ __forceinline__ void quant_dab_rows(const BwdParams& p, int g) {
+  int4 e;
+  int mb;
+  mtile_at(p, g, e, mb);
+  const int64_t K = 2 * int64_t(p.I);
+  for (int r = threadIdx.x >> 6; r < e.y; r += kThreads / 64) {
+    const int64_t row = int64_t(e.x) + r;
+    wave_quant_row<true, kCpolDev>(p.P.dabq + row * K, p.P.dabqs + row * p.abq_ld,
+                                   p.P.bdab + row * K, int(K));
+  }
 }
 
 // dW GEMMs, K over the expert's routed rows in ascending order, both operands read
@@ -251,8 +317,10 @@ __device__ __forceinline__ void sum_chunk(const BwdParams& p, int c) {
 // Workgroups take tickets in this order:
 //   1. every dH tile, m-tiles slowest and in reverse row order: the last minibatch first,
 //      as the ring is walked backwards (its slots hold the most recent minibatches);
+//   1b. MXFP8 only: one quantisation of [da | db] per m-tile, in the same order; one of
+//      m-tile g waits until the dH tiles of g have signalled, then signals g once more;
 //   2. every dX tile, m-tiles in the same order; one of m-tile g waits until the dH tiles
-//      of g have signalled;
+//      (and in MXFP8 the quantisation) of g have signalled;
 //   3. the first two rounds of dW tiles; a workgroup's first dW tile waits until every
 //      dH tile has signalled;
 //   4. the row-sum chunks; a workgroup's first chunk waits until every dX tile has
@@ -262,16 +330,20 @@ __device__ __forceinline__ void sum_chunk(const BwdParams& p, int c) {
 // idle tails between the steps, and the dW epilogues (256 KB of fp32 stores a tile) no
 // longer start on every CU at once: the CUs reach their dW tiles at different times.
 // Waits are bounded and every loop exits once the abort word is set.
+template <bool MX>
 __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
   uint32_t* hdr = p.P.hdr;
   uint32_t* hd = p.P.bsync;
   const uint32_t mt = hdr[kHdrMtiles];
   const uint32_t nh = mt * uint32_t(p.nNdh);
+  const uint32_t nq = MX ? mt : 0u;  // MXFP8: one [da | db] quantisation per m-tile
   const uint32_t nx = mt * uint32_t(p.nDt);
   const uint32_t nw = uint32_t(p.nl) * 3u * uint32_t(p.nDt) * uint32_t(p.nIt);
   const uint32_t ns = uint32_t((p.T + kSumTokens - 1) / kSumTokens);
   const uint32_t w1 = min(nw, 2u * gridDim.x);
-  const uint32_t b_x = nh, b_w1 = b_x + nx, b_s = b_w1 + w1, b_w2 = b_s + ns;
+  const uint32_t b_q = nh, b_x = b_q + nq, b_w1 = b_x + nx, b_s = b_w1 + w1, b_w2 = b_s + ns;
+  // a dX tile of m-tile g waits for its dH tiles, and in MXFP8 for its quantisation too
+  const uint32_t dx_need = uint32_t(p.nNdh) + (MX ? 1u : 0u);
   const uint32_t total = b_w2 + (nw - w1);
   bool dh_all = false, dx_all = false;
   const bool trace = p.P.trace != nullptr;
@@ -287,10 +359,10 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
     ++n_taken;
     const uint32_t t_tk = trace ? uint32_t(wall_clock64()) : 0u;
     uint32_t t_ready = t_tk, t_k = 0u, kind;
-    if (tk < b_x) {
+    if (tk < b_q) {
       kind = 0;
       const int g = int(mt) - 1 - int(tk) / p.nNdh;
-      t_k = dh_tile(p, g, int(tk) % p.nNdh);
+      t_k = dh_tile<MX>(p, g, int(tk) % p.nNdh);
       perturb_pause(p.perturb, tk);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -298,13 +370,22 @@ __global__ __launch_bounds__(512) void k_bwd_main(BwdParams p) {
         fetch_add_relaxed(hd + g, 1u);
         fetch_add_relaxed(hdr + kHdrBwdDhDone, 1u);
       }
+    } else if (tk < b_x) {
+      kind = 4;
+      const int g = int(mt) - 1 - int(tk - b_q);
+      if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
+      t_ready = trace ? uint32_t(wall_clock64()) : 0u;
+      quant_dab_rows(p, g);
+      t_k = trace ? uint32_t(wall_clock64()) : 0u;
+      perturb_pause(p.perturb, tk);
+      wg_signal_add(hd + g, 1u);
     } else if (tk < b_w1) {
       kind = 1;
       const int q = int(tk - b_x);
       const int g = int(mt) - 1 - q / p.nDt;
-      if (!wg_wait_geq(hd + g, uint32_t(p.nNdh), hdr, p.wait_ticks)) break;
+      if (!wg_wait_geq(hd + g, dx_need, hdr, p.wait_ticks)) break;
       t_ready = trace ? uint32_t(wall_clock64()) : 0u;
-      t_k = dx_tile(p, g, q % p.nDt);
+      t_k = dx_tile<MX>(p, g, q % p.nDt);
       perturb_pause(p.perturb, tk);
       wg_signal_add(hdr + kHdrBwdDxDone, 1u);
     } else if (tk >= b_s && tk < b_w2) {
@@ -354,13 +435,18 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   p.S = int(L.S);
   p.slot_bytes = int64_t(L.slot_bytes);
   p.slot_ab = int64_t(L.slot_ab);
-  p.ab_saved = L.unfused ? 1 : 0;
+  // an unfused forward and a MXFP8 forward that save write a, b of every row
+  p.ab_saved = (L.unfused || L.mx) ? 1 : 0;
   p.slot_x = int64_t(L.slot_x);
   p.ring_2g = int64_t(L.S) * int64_t(L.slot_bytes) < (int64_t(1) << 31) ? 1 : 0;
   p.per_mt = int(L.nN1 + L.nN2);
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
   p.trace_tickets = int64_t(L.trace_tickets);
+  p.xs_ld = L.xs_ld;
+  p.abq_ld = L.abq_ld;
+  p.wdts_ld = L.repack_wdt ? L.xs_ld : L.D / 32;
+  p.wdts = L.repack_wdt ? P.wdts : a.wdts;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -369,8 +455,15 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
   const dim3 tiles_grid = dim3(unsigned(cus));  // one 512-thread tile workgroup fits a CU
   hipLaunchKernelGGL(k_bwd_rows, dim3(unsigned(std::min<int64_t>((L.TK + 255) / 256, 4096))),
                      dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL(k_bwd_main, tiles_grid, dim3(kThreads), 0, st, p);
+  if (L.mx) {
+    if (L.repack_wdt) launch_mx_repack(a.wdts, L.nl * L.I, int(L.D / 32), P.wdts, int(L.xs_ld), st);
+    hipLaunchKernelGGL(k_bwd_dyq, dim3(unsigned(std::min<int64_t>((L.TK + 3) / 4, 65536))),
+                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_bwd_main<true>, tiles_grid, dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(k_bwd_gemm1, tiles_grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(k_bwd_main<false>, tiles_grid, dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
 }
 

@@ -158,7 +158,8 @@ __device__ __forceinline__ void gemm1_tile_unfused(const FwdParams& p) {
                                       p.P.full_xs + int64_t(e.x) * p.xs_ld, e.z);
     run_tile_mx<false>(true, o, e.y, nt * kBN1, p.D, p.I, acc);
     epi_swiglu_mx<false>(acc, e.y, nt * kBN1, p.I, p.P.full_h + int64_t(e.x) * p.I, p.I,
-                         p.P.full_hs + int64_t(e.x) * p.hs_ld, p.hs_ld);
+                         p.P.full_hs + int64_t(e.x) * p.hs_ld, p.hs_ld,
+                         p.save ? p.P.bab + int64_t(e.x) * 2 * p.I : nullptr);
     return;
   }
   const uint16_t* X = reinterpret_cast<const uint16_t*>(p.P.full_x);
@@ -537,8 +538,11 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
                                           slot + p.slot_xs + int64_t(r0) * p.xs_ld, e.z);
         run_tile_mx<true>(true, o, e.y, n0, p.D, p.I, acc);
         const uint32_t t_k = trace ? trace_now() : 0u;
+        // saving for the backward: a, b of every row go to the row buffer (the MXFP8
+        // backward reads them there, so no minibatch is replayed)
         epi_swiglu_mx<true>(acc, e.y, n0, p.I, slot + p.slot_h + int64_t(r0) * p.I, p.I,
-                            slot + p.slot_hs + int64_t(r0) * p.hs_ld, p.hs_ld);
+                            slot + p.slot_hs + int64_t(r0) * p.hs_ld, p.hs_ld,
+                            p.save ? p.P.bab + int64_t(e.x) * 2 * p.I : nullptr);
         const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(hd, 1);
@@ -605,20 +609,6 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
               vid < C ? 1u : 0u, nd);
 }
 
-// Weight scales with a row stride of K / 32 bytes, repacked to the tile's stride of one
-// dword per 128-wide K step (used when K % 128 == 64); the pad byte is 127 (scale 1)
-// and is never multiplied.
-__global__ __launch_bounds__(256) void k_mx_repack(const uint8_t* __restrict__ src, int64_t rows,
-                                                   int src_ld, uint8_t* __restrict__ dst,
-                                                   int dst_ld) {
-  const int64_t n = rows * dst_ld;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
-    const int64_t r = i / dst_ld;
-    const int c = int(i - r * dst_ld);
-    dst[i] = c < src_ld ? src[r * src_ld + c] : uint8_t(127);
-  }
-}
-
 // ------------------------------------------------------------------------------------
 // host
 // ------------------------------------------------------------------------------------
@@ -655,19 +645,10 @@ static int fused_grid_size(const void* kernel) {
 mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st) {
   FwdParams p = make_params(L, P, a);
   if (L.repack_wg) {
-    const int64_t rows = L.nl * L.I;
-    const unsigned g = unsigned(std::min<int64_t>((rows * L.wgs_ld + 255) / 256, 4096));
-    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.sg, rows, int(L.D / 32), P.wsg,
-                       int(L.wgs_ld));
-    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.su, rows, int(L.D / 32), P.wsu,
-                       int(L.wgs_ld));
+    launch_mx_repack(a.sg, L.nl * L.I, int(L.D / 32), P.wsg, int(L.wgs_ld), st);
+    launch_mx_repack(a.su, L.nl * L.I, int(L.D / 32), P.wsu, int(L.wgs_ld), st);
   }
-  if (L.repack_wd) {
-    const int64_t rows = L.nl * L.D;
-    const unsigned g = unsigned(std::min<int64_t>((rows * L.wds_ld + 255) / 256, 4096));
-    hipLaunchKernelGGL(k_mx_repack, dim3(g), dim3(256), 0, st, a.sd, rows, int(L.I / 32), P.wsd,
-                       int(L.wds_ld));
-  }
+  if (L.repack_wd) launch_mx_repack(a.sd, L.nl * L.D, int(L.I / 32), P.wsd, int(L.wds_ld), st);
   if (L.unfused) {
     const unsigned gw = unsigned(L.unf_grid[0]), gc = unsigned(L.unf_grid[3]);
     const dim3 g1(unsigned(L.unf_grid[1])), g2(unsigned(L.unf_grid[2]));

@@ -102,8 +102,10 @@ __device__ __forceinline__ void quant_store_pass(const v4u (&raw)[kQuantBatch], 
 
 // One wave quantises one row of D bf16 values (D a multiple of 32) into MX: codes[0..D)
 // and scales[0..D/32), kQuantBatch chunks per lane loaded before any is quantised.  With
-// kCoherent the outputs are written at device scope (handoff data).
-template <bool kCoherent>
+// kCoherent the outputs are written at device scope (handoff data); kLdPol is the cache
+// policy of the source loads (kCpolDev for rows written by other workgroups of the same
+// launch).
+template <bool kCoherent, int kLdPol = kCpolPlain>
 __device__ __forceinline__ void wave_quant_row(uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                const uint16_t* __restrict__ src, int D) {
@@ -116,7 +118,7 @@ __device__ __forceinline__ void wave_quant_row(uint8_t* __restrict__ codes,
     v4u raw[kQuantBatch];
 #pragma unroll
     for (int u = 0; u < kQuantBatch; ++u)
-      raw[u] = buf_ld16<kCpolPlain>(rs, (b + lane + 64 * u) * 16);
+      raw[u] = buf_ld16<kLdPol>(rs, (b + lane + 64 * u) * 16);
     quant_store_pass<kCoherent ? kCpolDev : kCpolPlain>(raw, rc, rsc, b);
   }
 }

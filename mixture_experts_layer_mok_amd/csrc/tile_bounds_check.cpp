@@ -9,8 +9,8 @@
 // valid offset below 2^31 (the range of its buffer resource; setting bit 31 makes a load
 // out of range).  The backward's K-major operands are checked too: weight offsets over
 // every K step, the column clamps of routed-row loads, and that each staged K row gets
-// all of its chunks once.  Built with the host compiler only; exits non-zero on a
-// violation.
+// all of its chunks once, and so are the MXFP8 backward's two scaled tiles (dH over D,
+// dX over 2I).  Built with the host compiler only; exits non-zero on a violation.
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
@@ -129,6 +129,16 @@ int main(int argc, char** argv) {
       for (int n0 = 0; n0 < D; n0 += kBN2)
         bad += check_mx("gemm2-mx", mok::geom::kSplit, I, I, hs_ld, rows, I, wds_ld, D, n0,
                         n0 + 128);
+      // MXFP8 backward: dH (A = quantised dY rows [rows, D] with X-style padded scales,
+      // B = W_down^T codes [I, D] with D / 32 or repacked scales) and dX (A = quantised
+      // [da | db] rows [rows, 2I], B = [W_gate; W_up]^T codes [D, 2I], scales 2I / 32)
+      const int64_t wdts_ld = D % 128 ? xs_ld : D / 32, ab_ld = 2 * I / 32;
+      for (int n0 = 0; n0 < I; n0 += kBN2)
+        bad += check_mx("dh-mx", mok::geom::kSplit, D, D, xs_ld, rows, D, wdts_ld, I, n0,
+                        n0 + 128);
+      for (int n0 = 0; n0 < D; n0 += kBN2)
+        bad += check_mx("dx-mx", mok::geom::kSplit, 2 * I, 2 * I, ab_ld, rows, 2 * I, ab_ld, D,
+                        n0, n0 + 128);
     }
   }
   // K-major weights: dH reads W_down [D rows, I columns], dX W_gate / W_up [I rows, D

@@ -168,23 +168,13 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
 // ------------------------------------------------------------------------------------
 // GEMM tiles
 // ------------------------------------------------------------------------------------
-// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
-// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
-// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
-// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
-// Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
-// [rows, 2I]: gate in [0, I), up in [I, 2I).  h is formed from the fp32 accumulators.
-// Each output is staged in LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255
-// in the B stages) and then written as whole row segments, 8 bytes a lane.  Staged
-// columns are XOR-swizzled in 16-column groups by (up half, bit 2 of the row), so that
-// the four lane groups of an MFMA block that write at once hit different banks.  With
-// kCoherent both are written at device scope: in the fused kernel a ring slot is
-// rewritten by workgroups on other XCDs within one launch, and a plain store would leave
-// a dirty line in one XCD's L2 that could be written back after a newer one from another
-// XCD.  Ends with a barrier.
+// The gate/up pre-activations of a GEMM1 tile (paired layout, as in epi_swiglu) stored
+// as bf16 rows [rows, 2I] at AB: gate in [0, I), up in [I, 2I).  Staged in LDS as rows of
+// 256 columns (tile rows 0..127 in the A stages, 128..255 in the B stages), then written
+// as whole row segments, 8 bytes a lane.  Ends with a barrier.
 template <bool kCoherent>
-__device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
-                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
+__device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n0, int I,
+                                             uint16_t* AB) {
   constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
   constexpr int W = kThreads / 64;
   const int tid = opaque(threadIdx.x);
@@ -198,7 +188,7 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
   const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
   lds_u16_t* st = stage16(w >> 2);
   auto stage_row = [](int r) { return stage16(r >> 7); };
-  if (AB) {
+  {
     // rows of 256 columns: gate 0..127, up 128..255
     const int sw = ((gate_lane ? 0 : 2) | rbit) << 4;
 #pragma unroll
@@ -230,6 +220,39 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
     }
     __syncthreads();
   }
+}
+
+// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
+// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
+// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
+// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
+// Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
+// [rows, 2I]: gate in [0, I), up in [I, 2I).  h is formed from the fp32 accumulators.
+// Each output is staged in LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255
+// in the B stages) and then written as whole row segments, 8 bytes a lane.  Staged
+// columns are XOR-swizzled in 16-column groups by (up half, bit 2 of the row), so that
+// the four lane groups of an MFMA block that write at once hit different banks.  With
+// kCoherent both are written at device scope: in the fused kernel a ring slot is
+// rewritten by workgroups on other XCDs within one launch, and a plain store would leave
+// a dirty line in one XCD's L2 that could be written back after a newer one from another
+// XCD.  Ends with a barrier.
+template <bool kCoherent>
+__device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
+                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
+  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int W = kThreads / 64;
+  const int tid = opaque(threadIdx.x);
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wn = w & 3;
+  const int wr = __builtin_amdgcn_readfirstlane(w);
+  const bool gate_lane = (lane & 16) == 0;
+  const int rbit = lane >> 5;  // bit 2 of every row this lane holds
+  const int l32 = lane & 31, half = lane >> 5;
+  const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
+  lds_u16_t* st = stage16(w >> 2);
+  auto stage_row = [](int r) { return stage16(r >> 7); };
+  if (AB) epi_store_ab<kCoherent>(acc, rows, n0, I, AB);
   if (H) {
     // rows of 128 columns.  A gate lane and its up lane (l ^ 16) split the 16 rows of
     // their column: one gfx950 v_permlane16_swap per row pair hands the up lane's value
@@ -345,11 +368,13 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
 // the four lane groups of a write hit different banks; scales after them), then written
 // as 128-byte row segments, 4 bytes a lane, and one byte per row and block.  Writes codes
 // Hc[row * ldh + col] and scales Hs[row * hs_ld + col / 32]; I is a multiple of 32, so a
-// block is wholly inside or outside [0, I).  Ends with a barrier.
+// block is wholly inside or outside [0, I).  With AB, the gate/up pre-activations are
+// stored first, as bf16 rows (epi_store_ab).  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int n0, int I,
                                               uint8_t* Hc, int64_t ldh, uint8_t* Hs,
-                                              int64_t hs_ld) {
+                                              int64_t hs_ld, uint16_t* AB = nullptr) {
+  if (AB) epi_store_ab<kCoherent>(acc, rows, n0, I, AB);  // bf16 a, b for the backward
   constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
   constexpr int W = kThreads / 64;
   typedef __attribute__((address_space(3))) uint8_t lds_u8_t;

@@ -52,6 +52,36 @@ class MoKLayer:
                       self.ws_bytes, stream)
         return dict(dx=dx, dg=dg, dwg=dwg, dwu=dwu, dwd=dwd)
 
+    def backward_mx(self, dy, x, ids, gates, wt, stream=None):
+        """MXFP8 backward; wt = (wd_t, wd_t_scales, wgu_t, wgu_t_scales) from
+        quantize_weights_bwd."""
+        d = self.desc
+        T, D, I, k, nl = d.num_tokens, d.hidden, d.intermediate, d.top_k, d.num_local_experts
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=self.device)
+        dg = torch.empty((T, k), dtype=torch.float32, device=self.device)
+        dwg = torch.empty((nl, I, D), dtype=torch.float32, device=self.device)
+        dwu = torch.empty((nl, I, D), dtype=torch.float32, device=self.device)
+        dwd = torch.empty((nl, D, I), dtype=torch.float32, device=self.device)
+        L.mok_moe_bwd_mx(d, dy, x, ids, gates, *wt, dx, dg, dwg, dwu, dwd, self.ws,
+                         self.ws_bytes, stream)
+        return dict(dx=dx, dg=dg, dwg=dwg, dwu=dwu, dwd=dwd)
+
+    def quantize_weights_bwd(self, wg, wu, wd, stream=None):
+        """The MXFP8 backward's weight operands: W_down^T codes [E_loc, I, D] with scales
+        [E_loc, I, D/32], and [W_gate; W_up]^T codes [E_loc, D, 2I] with scales
+        [E_loc, D, 2I/32] (blocks of 32 along each GEMM's K)."""
+        nl, I, D = wg.shape
+        dev = self.device
+        wdt = torch.empty((nl, I, D), dtype=torch.uint8, device=dev)
+        wdts = torch.empty((nl, I, D // 32), dtype=torch.uint8, device=dev)
+        wgut = torch.empty((nl, D, 2 * I), dtype=torch.uint8, device=dev)
+        wguts = torch.empty((nl, D, 2 * I // 32), dtype=torch.uint8, device=dev)
+        L.mok_quantize_mx_t(wd, nl, D, I, wdt, D, wdts, D // 32, stream)
+        L.mok_quantize_mx_t(wg, nl, I, D, wgut, 2 * I, wguts, 2 * I // 32, stream)
+        L.mok_quantize_mx_t(wu, nl, I, D, wgut.data_ptr() + I, 2 * I, wguts.data_ptr() + I // 32,
+                            2 * I // 32, stream)
+        return wdt, wdts, wgut, wguts
+
     def tables(self, stream=None) -> dict:
         d = self.desc
         TK = d.num_tokens * d.top_k

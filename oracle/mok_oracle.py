@@ -29,7 +29,8 @@ What each function follows:
                   gate-weighted sum is a step of its own)
   forward         the four steps above, in order
   backward        [L] §02 (reverse-combine then reverse-dispatch) and [M] 三个重要的设计决策
-                  (router-weight gradient computed inside the SwiGLU backward)
+                  (router-weight gradient computed inside the SwiGLU backward); the MXFP8
+                  backward: [L] §03 (MXFP8 forward and backward)
   mx_quantize     [L] §02 (MXFP8 activations quantised inside dispatch, grouped GEMM
                   and SwiGLU); scale rule: the ceil reading (see ``mx_scale_exponent``)
 
@@ -44,7 +45,10 @@ Readings taken where the pages are silent:
   * tokens with no local slot get Y = 0, dX = 0 and dG = 0;
   * MXFP8 mode quantises X (along D), W_gate/W_up (along D), W_down (along I) and
     H (along I, from its float32 value); all arithmetic between those points is exact
-    float64 on the dequantised values.
+    float64 on the dequantised values;
+  * the MXFP8 backward quantises the operands of the two data-gradient GEMMs along
+    their K: dY and W_down along D (for u), da, db (from float32) and W_gate, W_up
+    along I (for dx); the weight gradients and dG use unquantised values.
 """
 from __future__ import annotations
 
@@ -291,7 +295,7 @@ def forward(x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: bool =
     return y
 
 
-def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int):
+def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: bool = False):
     """Gradients of the layer output with respect to x, the gates and the three
     weight tensors, for an upstream gradient dy [T, D].
 
@@ -301,6 +305,11 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int):
       dh = g u;  da = dh * b * s(a) (1 + a (1 - s(a)));  db = dh * silu(a)
       dW_down[e] += (g dy[t])^T h;  dW_gate[e] += da^T x;  dW_up[e] += db^T x
       dx_row = da W_gate[e] + db W_up[e];   dX[t] = sum over local slots of dx_row
+    With ``mxfp8`` (the MXFP8 mode covers the backward, [L] §03): a and b are those of the
+    MXFP8 forward, and the two GEMMs that produce data gradients read MX round-tripped
+    operands, each quantised along that GEMM's K: u from dy rows and W_down quantised
+    along D; dx_row from da, db (from float32) and W_gate, W_up quantised along I.  dG
+    and the weight gradients use the unquantised u, h, da, db, x and dy.
     Returns dict(dx [T, D], dg [T, k], dwg, dwu [n_local, I, D], dwd [n_local, D, I])."""
     T, k = ids.shape
     n_local, I, D = wg.shape
@@ -319,10 +328,19 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int):
             continue
         pairs = sch.perm[r0:r1]
         xe = xd[r0:r1]
-        a, b, h, _ = expert_ffn(xe, wg[e], wu[e], wd[e])
         dye = dy64[pairs // k]
+        wg_e, wu_e, wd_e = (np.asarray(w[e], np.float64) for w in (wg, wu, wd))
+        if mxfp8:
+            xq = mx_roundtrip(xe)
+            a = xq @ mx_roundtrip(wg_e).T
+            b = xq @ mx_roundtrip(wu_e).T
+            h = silu(a) * b
+            # W_down [D, I] quantised along D: the round trip of its transpose
+            u = mx_roundtrip(dye) @ mx_roundtrip(wd_e.T).T
+        else:
+            a, b, h, _ = expert_ffn(xe, wg_e, wu_e, wd_e)
+            u = dye @ wd_e
         g = g_all[pairs][:, None]
-        u = dye @ np.asarray(wd[e], np.float64)
         dg[pairs] = np.sum(u * h, axis=1)
         dh = g * u
         s = sigmoid(a)
@@ -331,7 +349,12 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int):
         dwd[e] = (g * dye).T @ h
         dwg[e] = da.T @ xe
         dwu[e] = db.T @ xe
-        dxr[r0:r1] = da @ np.asarray(wg[e], np.float64) + db @ np.asarray(wu[e], np.float64)
+        if mxfp8:
+            # W_gate, W_up [I, D] quantised along I: the round trips of their transposes
+            dxr[r0:r1] = (mx_roundtrip(da.astype(np.float32)) @ mx_roundtrip(wg_e.T).T +
+                          mx_roundtrip(db.astype(np.float32)) @ mx_roundtrip(wu_e.T).T)
+        else:
+            dxr[r0:r1] = da @ wg_e + db @ wu_e
     dx = np.zeros((T, D))
     pos = sch.pos.reshape(T, k)
     for j in range(k):

@@ -49,7 +49,6 @@ def _ws_code(desc):
     (dict(e0=3, E_loc=2), L.MOK_E_SHAPE), (dict(M=0), L.MOK_E_SHAPE), (dict(S=0), L.MOK_E_SHAPE),
     (dict(comm_cus=0), L.MOK_E_SHAPE), (dict(T=0), L.MOK_E_SHAPE),
     (dict(precision=7), L.MOK_E_UNSUPPORTED), (dict(flags=0x80), L.MOK_E_UNSUPPORTED),
-    (dict(precision=1, flags=L.MOK_FLAG_SAVE_FOR_BWD), L.MOK_E_UNSUPPORTED),
 ])
 def test_workspace_size_rejects(kw, code):
     assert _ws_code(_desc(**kw))[0] == code
@@ -110,6 +109,27 @@ def test_entry_points_fail_before_touching_memory():
     assert lib.mok_moe_bwd(dp, *bw, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOK_E_NULL
     assert lib.mok_moe_bwd(dp, *bw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small, None) == \
         L.MOK_E_WORKSPACE
+    # the MXFP8 backward: its own entry point, on a MXFP8 workspace that saved
+    dmxs = _desc(precision=1, flags=L.MOK_FLAG_SAVE_FOR_BWD)
+    ok, need_mxs = _ws_code(dmxs)
+    assert ok == L.MOK_OK and need_mxs > _ws_code(dmx)[1]
+    bmx = [FAKE] * 9
+    assert lib.mok_moe_bwd(ctypes.byref(dmxs), *bw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_mxs,
+                           None) == L.MOK_E_UNSUPPORTED
+    assert lib.mok_moe_bwd_mx(dp, *bmx, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == \
+        L.MOK_E_UNSUPPORTED
+    assert lib.mok_moe_bwd_mx(ctypes.byref(dmxs), *bmx, FAKE, FAKE, FAKE, None, FAKE, need_mxs,
+                              None) == L.MOK_E_NULL
+    assert lib.mok_moe_bwd_mx(ctypes.byref(dmxs), *bmx, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              need_mxs - 256, None) == L.MOK_E_WORKSPACE
+    assert lib.mok_moe_bwd_mx(ctypes.byref(dmxs), *bmx[:7], FAKE + 1, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, need_mxs, None) == L.MOK_E_SHAPE
+    # the transposing quantiser's shape checks
+    assert lib.mok_quantize_mx_t(FAKE, 2, 48, 64, FAKE, 48, FAKE, 2, None) == L.MOK_E_SHAPE
+    assert lib.mok_quantize_mx_t(FAKE, 2, 64, 64, FAKE, 72, FAKE, 2, None) == L.MOK_E_SHAPE
+    assert lib.mok_quantize_mx_t(FAKE, 2, 64, 64, FAKE, 64, FAKE, 1, None) == L.MOK_E_SHAPE
+    assert lib.mok_quantize_mx_t(FAKE, 2, 64, 64, FAKE + 8, 64, FAKE, 2, None) == L.MOK_E_SHAPE
+    assert lib.mok_quantize_mx_t(None, 2, 64, 64, FAKE, 64, FAKE, 2, None) == L.MOK_E_NULL
 
 
 def test_trace_layout():

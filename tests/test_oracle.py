@@ -445,3 +445,100 @@ def test_two_waves_rule_reproduces_printed_floor():
                              g["intermediate"]) == g["min_minibatch"]
     # more compute units or a bigger tile raise the floor proportionally
     assert layer_two_wave_min_rows(256, 32, 2048) == 2 * 224 * 256 * 256 / 4096
+
+
+def _torch_mx_backward(dy, x, ids, gates, wg, wu, wd, e0, transposed=()):
+    """The MXFP8 backward as per-expert masked torch products (no schedule), written apart
+    from the oracle: a, b from the MX forward's operands; u from dY rows and W_down^T
+    round-tripped along D; dx rows from da, db (float32) and W_gate^T, W_up^T round-tripped
+    along I; dG and the weight gradients from the unquantised values.  `transposed` names
+    quantisation points ("dy", "wdt", "dab", "wgut") taken along the other axis instead."""
+    def q(v, name):
+        if name not in transposed:
+            return _torch_mx_roundtrip(v)
+        n = v.shape[0]
+        pad = torch.zeros((v.shape[1], -n % 32), dtype=v.dtype)
+        return _torch_mx_roundtrip(torch.cat([v.T, pad], dim=1))[:, :n].T
+
+    X = torch.tensor(x, dtype=torch.float64)
+    DY = torch.tensor(dy, dtype=torch.float64)
+    G = torch.tensor(gates, dtype=torch.float64)
+    nl = wg.shape[0]
+    dX, dG = torch.zeros_like(X), torch.zeros_like(G)
+    dWg, dWu = torch.zeros(wg.shape, dtype=torch.float64), torch.zeros(wu.shape, dtype=torch.float64)
+    dWd = torch.zeros(wd.shape, dtype=torch.float64)
+    idt = torch.tensor(ids.astype(np.int64))
+    for e in range(nl):
+        tok, slot = torch.nonzero(idt == e + e0, as_tuple=True)
+        if tok.numel() == 0:
+            continue
+        Wg, Wu, Wd = (torch.tensor(w[e], dtype=torch.float64) for w in (wg, wu, wd))
+        Xq = _torch_mx_roundtrip(X[tok])
+        a = F.linear(Xq, _torch_mx_roundtrip(Wg))
+        b = F.linear(Xq, _torch_mx_roundtrip(Wu))
+        h = F.silu(a) * b
+        u = F.linear(q(DY[tok], "dy"), q(Wd.T, "wdt"))          # [n, I]
+        g = G[tok, slot][:, None]
+        dG[tok, slot] = (u * h).sum(dim=1)
+        sg = torch.sigmoid(a)
+        da = g * u * b * sg * (1.0 + a * (1.0 - sg))
+        db = g * u * a * sg
+        dWd[e] = (g * DY[tok]).T @ h
+        dWg[e] = da.T @ X[tok]
+        dWu[e] = db.T @ X[tok]
+        daq = q(da.to(torch.float32).to(torch.float64), "dab")
+        dbq = q(db.to(torch.float32).to(torch.float64), "dab")
+        dx = F.linear(daq, q(Wg.T, "wgut")) + F.linear(dbq, q(Wu.T, "wgut"))
+        dX = dX.index_add(0, tok, dx)
+    return dict(dx=dX.numpy(), dg=dG.numpy(), dwg=dWg.numpy(), dwu=dWu.numpy(), dwd=dWd.numpy())
+
+
+def _wide_range_bwd_inputs(d):
+    """Inputs whose blocks along each backward GEMM's K span many binades, with
+    complementary partners (see _wide_range_inputs): dY columns 2^-(d mod 24) against
+    W_down rows 2^-((d + 12) mod 24) along D; W_down columns 2^-floor((i mod 24) / 2), so
+    that u, da and db vary widely along I, against W_gate / W_up rows 2^-((i + 12) mod 24)."""
+    out = dict(d)
+    D, I = d["wg"].shape[2], d["wg"].shape[1]
+    dd, ii = np.arange(D), np.arange(I)
+    f = lambda v: np.ldexp(1.0, -v).astype(np.float32)  # noqa: E731
+    out["dy"] = (d["dy"] * f(dd % 24)[None, :]).astype(np.float32)
+    out["wd"] = (d["wd"] * f((dd + 12) % 24)[None, :, None] * f((ii % 24) // 2)[None, None, :]
+                 ).astype(np.float32)
+    out["wg"] = (d["wg"] * f((ii + 12) % 24)[None, :, None]).astype(np.float32)
+    out["wu"] = (d["wu"] * f((ii + 12) % 24)[None, :, None]).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("args", [dict(T=40, D=64, I=64, E=4, k=2),
+                                  dict(T=64, D=128, I=96, E=8, k=3, e0=2, nl=4, zipf=1.2)])
+def test_backward_mxfp8_vs_torch_float8(args):
+    """The oracle's MXFP8 backward equals an independent torch-float8 emulation to 1e-12
+    on every gradient, on inputs whose blocks span many binades; taking any one of the
+    backward's four quantisation points along the other axis moves some gradient far
+    beyond that bound, so a wrong block axis in the oracle would fail here.  Without the
+    quantisation points (plain inputs) it also stays close to the unquantised backward."""
+    cfg, d = _small(**args)
+    d = _wide_range_bwd_inputs(d)
+    ids = gen.mask_ids(d["ids"], 0.1, seed=6)
+    got = O.backward(d["dy"], d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0,
+                     E=cfg.E, M=cfg.M, mxfp8=True)
+    targs = (d["dy"], d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], cfg.e0)
+    ref = _torch_mx_backward(*targs)
+    for name in ("dx", "dg", "dwg", "dwu", "dwd"):
+        assert np.linalg.norm(got[name] - ref[name]) <= 1e-12 * np.linalg.norm(ref[name]), name
+    for point in ("dy", "wdt", "dab", "wgut"):
+        alt = _torch_mx_backward(*targs, transposed=(point,))
+        moved = max(np.linalg.norm(alt[n] - ref[n]) / np.linalg.norm(ref[n]) for n in ref)
+        assert moved > 1e-9, point
+
+
+def test_backward_mxfp8_near_plain():
+    """On ordinary inputs the MX backward is the plain backward up to MX rounding."""
+    cfg, d = _small(T=48, D=64, I=64, E=4, k=2)
+    args = (d["dy"], d["x"], d["ids"], d["gates"], d["wg"], d["wu"], d["wd"])
+    mx = O.backward(*args, e0=0, E=4, M=16, mxfp8=True)
+    plain = O.backward(*args, e0=0, E=4, M=16)
+    for name in ("dx", "dg", "dwg", "dwu", "dwd"):
+        rel = np.linalg.norm(mx[name] - plain[name]) / np.linalg.norm(plain[name])
+        assert 1e-4 < rel < 0.2, (name, rel)
