@@ -25,7 +25,10 @@ HBM byte count read from the committed FETCH_SIZE / WRITE_SIZE counter summary, 
 the copy calibration, and null when the kernel sources changed since the counters were
 taken.  `phases_unfused` times the forward's four steps as separate launches with the
 in-kernel phase clock: dispatch and combine against HBM bandwidth, GEMM1 and GEMM2
-against the MFMA peak.  `mxfp8_fwd` does the same for the MXFP8 forward (config 4).
+against the MFMA peak.  `mxfp8_fwd` does the same for the MXFP8 forward (config 4), and
+`mxfp8_fwd_bwd` times forward + backward on that workload in MXFP8 and in bf16.
+`macrobatch` compares successive forwards run one after another with the same forwards
+interleaved as macrobatches (MOK_FLAG_OVERLAP_NEXT, two workspaces and streams).
 `cpu_baseline` times the float64 NumPy oracle (forward + backward) on this host's cores.
 """
 from __future__ import annotations
@@ -66,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
+    ap.add_argument("--no-macrobatch", action="store_true",
+                    help="skip the macrobatch interleave figure")
     ap.add_argument("--no-phases", action="store_true",
                     help="skip the per-phase rates of the forward as separate launches")
     ap.add_argument("--trace", action="store_true",
@@ -166,7 +171,10 @@ def setup(cfg, unfused, save, device):
     flags = (L.MOK_FLAG_UNFUSED if unfused else 0) | (L.MOK_FLAG_SAVE_FOR_BWD if save else 0)
     layer = MoKLayer(L.desc_from_config(cfg, flags=flags), device=device)
     if cfg.precision == L.MOK_PREC_MXFP8:
-        # weights are quantised once, before the layer (not part of a step)
+        # weights are quantised once, before the layer (not part of a step): along each
+        # forward GEMM's K, and for the backward transposed, along its GEMMs' K
+        if save:
+            t["wt"] = layer.quantize_weights_bwd(t["wg"], t["wu"], t["wd"])
         for n in ("wg", "wu", "wd"):
             t[n], t["s" + n[1]] = layer.quantize_weights(t[n])
         torch.cuda.synchronize()
@@ -191,8 +199,11 @@ def time_layer(cfg, t, layer, steps, warmup, with_bwd):
         if ev is not None:
             ev[2].record(stream)
         if with_bwd:
-            grads.update(layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"],
-                                        t["wu"], t["wd"]))
+            if "wt" in t:
+                grads.update(layer.backward_mx(t["dy"], t["x"], t["ids"], t["gates"], t["wt"]))
+            else:
+                grads.update(layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"],
+                                            t["wu"], t["wd"]))
             if ev is not None:
                 ev[3].record(stream)
 
@@ -242,7 +253,10 @@ def time_cold(cfg, t, layer, steps, with_bwd):
         if with_bwd:
             scrub.fill_((i + 128) & 0xFF)
             ev[2].record(stream)
-            layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
+            if "wt" in t:
+                layer.backward_mx(t["dy"], t["x"], t["ids"], t["gates"], t["wt"])
+            else:
+                layer.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
             ev.append(torch.cuda.Event(enable_timing=True))
             ev[3].record(stream)
         torch.cuda.synchronize()
@@ -385,6 +399,115 @@ def mx_forward_figure(args):
     return res
 
 
+def mx_backward_figure(args):
+    """Forward + backward in MXFP8 on the Zipf-skewed config-4 workload, beside the same
+    workload in bf16: the backward's time in each precision (the pages compare MXFP8 and
+    BF16 backward speedups).  The backward's rate counts 12 D I flops per routed row, of
+    which the dH and dX GEMMs (6 D I) run on scaled e4m3 MFMA and the dW GEMMs in bf16."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+    dev = torch.device("cuda:0")
+    out = {}
+    for prec in (L.MOK_PREC_MXFP8, L.MOK_PREC_BF16):
+        cfg = gen.CONFIGS[4].replace(precision=prec)
+        d, t, layer = setup(cfg, False, True, dev)
+        R = routed_rows(cfg, d["ids"])
+        name = "mxfp8" if prec == L.MOK_PREC_MXFP8 else "bf16"
+        log(f"timing the {name} forward + backward on {cfg.name} ({R} routed rows)")
+        r = time_layer(cfg, t, layer, args.steps, args.warmup, True)
+        bwd = float(np.mean(r["bwd_ms"]))
+        out[name] = {"fwd_ms": stats(r["fwd_ms"]), "bwd_ms": stats(r["bwd_ms"]),
+                     "bwd_tflops": round(12.0 * cfg.D * cfg.I * R / (bwd * 1e-3) / 1e12, 2)}
+        del layer, t, d
+        torch.cuda.empty_cache()
+    out["workload"] = "c4 shape, Zipf(1.2) routing, forward saving for the backward"
+    out["bwd_speedup_mxfp8_vs_bf16"] = round(out["bf16"]["bwd_ms"]["mean"] /
+                                             out["mxfp8"]["bwd_ms"]["mean"], 3)
+    return out
+
+
+def macrobatch_figure(args, n=4):
+    """Macrobatch interleave on the config-3 workload (four ring slots, eight minibatches,
+    so slots recycle): n forwards one after another on one stream and workspace, against
+    the same n as interleaved macrobatches (two workspaces and two streams with
+    MOK_FLAG_OVERLAP_NEXT, each combine overlapping the next dispatch).  Times are HIP
+    events around each whole sequence; `overlap_us` comes from a traced pair of calls: how
+    long the second call's workgroups ran before the first call's last workgroup ended."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+    from mixture_experts_layer_mok_amd.layer import MoKLayer, forward_macrobatches
+    cfg = gen.CONFIGS[3]
+    dev = torch.device("cuda:0")
+    d, t, _ = setup(cfg, False, False, dev)
+    batch = (t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
+    ys = [torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    seq = MoKLayer(L.desc_from_config(cfg), device=dev)
+    ilv = [MoKLayer(L.desc_from_config(cfg, flags=L.MOK_FLAG_OVERLAP_NEXT), device=dev)
+           for _ in range(2)]
+
+    def run_seq():
+        for i in range(n):
+            seq.schedule(t["ids"], stream=s0)
+            seq.forward(*batch, y=ys[i], stream=s0)
+
+    def run_ilv():
+        forward_macrobatches(ilv, (s0, s1), [batch] * n, ys)
+
+    def timed(fn, reps):
+        out = []
+        for r in range(reps + 2):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            torch.cuda.synchronize()
+            e0.record(s0)
+            s1.wait_event(e0)
+            fn()
+            e1.record(s1)
+            s0.wait_event(e1)
+            e2.record(s0)
+            torch.cuda.synchronize()
+            if r >= 2:
+                out.append(e0.elapsed_time(e2) / n)
+        return out
+
+    log(f"timing {n} macrobatches, sequential and interleaved")
+    seq_ms = timed(run_seq, max(3, args.steps // 2))
+    ilv_ms = timed(run_ilv, max(3, args.steps // 2))
+    for lay in [seq] + ilv:
+        if lay.status() != 0:
+            raise SystemExit(f"device status {lay.status():#x} in the macrobatch runs")
+    # one traced pair: when did the second call start against the first call's end
+    tr = [MoKLayer(L.desc_from_config(cfg, flags=L.MOK_FLAG_OVERLAP_NEXT | L.MOK_FLAG_TRACE),
+                   device=dev) for _ in range(2)]
+    for _ in range(2):
+        forward_macrobatches(tr, (s0, s1), [batch] * 2, ys[:2])
+    torch.cuda.synchronize()
+    cus = L.mok_device_cus()
+    recs = []
+    for lay in tr:
+        off, words = L.mok_trace_layout(lay.desc)
+        raw = lay.ws[off:off + words * 4].cpu().numpy().view(np.uint32)
+        cap = (words - L.MOK_TRACE_MAX_WORKGROUPS * 8) // 8
+        recs.append(raw[cap * 8:cap * 8 + cus * 8].reshape(cus, 8).astype(np.int64))
+    base = int(recs[0][:, 0].min())
+    rel = lambda v: (v - base) & 0xFFFFFFFF  # noqa: E731  (10 ns ticks)
+    end0 = int(rel(recs[0][:, 3]).max())
+    start1 = int(rel(recs[1][:, 0]).min())
+    del seq, ilv, tr, t, d
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: {n} macrobatches of the same shape (M={cfg.M}, "
+                        f"S={cfg.S}, comm_cus={cfg.comm_cus})",
+            "sequential_ms_per_macrobatch": stats(seq_ms),
+            "interleaved_ms_per_macrobatch": stats(ilv_ms),
+            "speedup": round(float(np.median(seq_ms)) / float(np.median(ilv_ms)), 4),
+            "overlap_us": round(max(0, end0 - start1) * 0.01, 1),
+            "first_call_us": round(end0 * 0.01, 1)}
+
+
 def trace_forward(args):
     """Warm-up forwards, then one forward with MOK_FLAG_TRACE on the same workload, decoded
     into where the compute and data-mover workgroups spent the kernel's span."""
@@ -457,7 +580,7 @@ def main():
     over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}
     cfg = cfg.replace(**over)
     mx = cfg.precision == L.MOK_PREC_MXFP8
-    with_bwd = not args.fwd_only and not mx  # the MXFP8 backward is not built
+    with_bwd = not args.fwd_only
     dev = torch.device("cuda:0")
     d, t, layer = setup(cfg, args.unfused, with_bwd, dev)
     R = routed_rows(cfg, d["ids"])
@@ -556,6 +679,9 @@ def main():
         out["cold_cache"] = time_cold(cfg, t, layer, min(args.steps, 5), with_bwd)
     if not mx and not args.no_mx and args.config == 5:
         out["mxfp8_fwd"] = mx_forward_figure(args)
+        out["mxfp8_fwd_bwd"] = mx_backward_figure(args)
+    if not args.no_macrobatch and args.config == 5:
+        out["macrobatch"] = macrobatch_figure(args)
     if not args.no_cpu_baseline:
         import oracle as O
         log("timing the float64 oracle on the host")

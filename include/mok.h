@@ -86,6 +86,16 @@ typedef enum {
                                        0-28 us.  Changes the interleaving of the persistent
                                        kernels only: outputs must stay bitwise the same
                                        (tests the handoffs for ordering races)           */
+#define MOK_FLAG_OVERLAP_NEXT 0x20u /* macrobatch interleave ([L] section 02: the combine of
+                                       one macrobatch runs while the next is dispatched):
+                                       the fused forward's compute workgroups leave as soon
+                                       as no tile is left instead of helping with the final
+                                       combine, which the comm_cus data movers finish; a
+                                       forward of the next macrobatch, launched on another
+                                       stream with its own workspace, starts on the freed
+                                       compute units and dispatches while this one still
+                                       combines.  Outputs are bitwise the same as without
+                                       the flag                                          */
 #define MOK_FLAG_TRACE 0x10u        /* the fused forward and the backward's persistent
                                        launch write timestamps of every ticket and
                                        workgroup into a trace region of the workspace

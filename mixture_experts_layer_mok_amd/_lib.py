@@ -28,6 +28,7 @@ MOK_FLAG_UNFUSED = 0x2
 MOK_FLAG_SHORT_WAITS = 0x4
 MOK_FLAG_PERTURB = 0x8
 MOK_FLAG_TRACE = 0x10
+MOK_FLAG_OVERLAP_NEXT = 0x20
 MOK_TRACE_MAX_WORKGROUPS = 1024
 MOK_DEV_BAD_ID = 0x1
 MOK_DEV_TIMEOUT = 0x2

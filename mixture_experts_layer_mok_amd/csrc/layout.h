@@ -55,7 +55,7 @@ struct Layout {
   int64_t n_mb_max;  // ceil(T*k / M)
   int64_t mt_max;    // m-tiles per minibatch, upper bound
   int64_t nN1, nN2;  // n-tiles of GEMM1 (over I) and GEMM2 (over D)
-  bool mx, save, unfused, short_waits, perturb, trace;
+  bool mx, save, unfused, short_waits, perturb, trace, overlap_next;
   // MXFP8: bytes per scale row of the layer's own X and H buffers (one dword per 128-wide
   // K step), and of the weight scales the tiles read (the caller's K / 32 when K % 128
   // == 0, else a repacked copy in the workspace with the padded stride)
@@ -102,7 +102,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   if (d->comm_cus < 1) return MOK_E_SHAPE;
   if (d->precision != MOK_PREC_BF16 && d->precision != MOK_PREC_MXFP8) return MOK_E_UNSUPPORTED;
   if (d->flags & ~(MOK_FLAG_SAVE_FOR_BWD | MOK_FLAG_UNFUSED | MOK_FLAG_SHORT_WAITS |
-                   MOK_FLAG_PERTURB | MOK_FLAG_TRACE))
+                   MOK_FLAG_PERTURB | MOK_FLAG_TRACE | MOK_FLAG_OVERLAP_NEXT))
     return MOK_E_UNSUPPORTED;
   L->T = T; L->D = D; L->I = I; L->E = E; L->k = k; L->e0 = e0; L->nl = nl; L->M = M; L->S = S;
   L->TK = T * k;
@@ -112,6 +112,7 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->short_waits = (d->flags & MOK_FLAG_SHORT_WAITS) != 0;
   L->perturb = (d->flags & MOK_FLAG_PERTURB) != 0;
   L->trace = (d->flags & MOK_FLAG_TRACE) != 0;
+  L->overlap_next = (d->flags & MOK_FLAG_OVERLAP_NEXT) != 0;
   L->NB = (L->TK + kSchedChunk - 1) / kSchedChunk;
   L->NS = L->NB * (kSchedChunk / kSchedSub);
   L->n_mb_max = (L->TK + M - 1) / M;

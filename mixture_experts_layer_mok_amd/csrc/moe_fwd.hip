@@ -47,6 +47,7 @@ struct FwdParams {
   int T, D, I, k, M, S, mt_max, nN1, nN2, n_mb_max, save;
   uint64_t wait_ticks;  // limit of a bounded wait (100 MHz ticks)
   int perturb;          // MOK_FLAG_PERTURB
+  int overlap_next;     // MOK_FLAG_OVERLAP_NEXT: compute workgroups skip the drain
   int64_t trace_tiles;  // MOK_FLAG_TRACE: tile records before the workgroup records
   int64_t ph_rec[4];    // MOK_FLAG_TRACE, unfused: first 64-bit word of each launch's records
   int64_t slot_bytes, slot_x, slot_xs, slot_h, slot_hs, slot_ab;
@@ -428,7 +429,8 @@ __device__ __forceinline__ void trace_put(uint32_t* rec, uint32_t a, uint32_t b,
 }
 
 // Drain, run by every workgroup once its role is done, so that the compute CUs help with
-// the data movement left at the end.  Work comes in chunks from a ticket: first the
+// the data movement left at the end (with MOK_FLAG_OVERLAP_NEXT only the data movers run
+// it, and the compute CUs go to the next macrobatch's forward).  Work comes in chunks from a ticket: first the
 // token chunks (y = 0 for tokens without a local row), then, minibatch by minibatch, the
 // row chunks of the last S minibatches.  A row chunk of minibatch cm combines the tokens
 // whose last row it holds; their other rows lie in minibatches before cm, whose GEMM2
@@ -603,7 +605,9 @@ __global__ __launch_bounds__(512) void k_fwd_fused(FwdParams p) {
   if (vid < C) comm_role<MX>(p, vid, C, ready, done);
   else compute_role<MX>(p, vid, C, ready, done, hdone);
   const uint32_t t2 = trace ? trace_now() : 0u;
-  const uint32_t nd = drain(p, done);
+  // macrobatch interleave: a compute workgroup leaves once no tile is left, so that the
+  // next macrobatch's forward can start on its CU while the data movers drain this one
+  const uint32_t nd = (p.overlap_next && vid >= C) ? 0u : drain(p, done);
   if (trace)
     trace_put(p.P.trace + p.trace_tiles * 8 + int64_t(vid) * 8, t0, t1, t2, trace_now(),
               vid < C ? 1u : 0u, nd);
@@ -621,6 +625,7 @@ static FwdParams make_params(const Layout& L, const Ptrs& P, const FwdArgs& a) {
   p.n_mb_max = int(L.n_mb_max); p.save = L.save ? 1 : 0;
   p.wait_ticks = L.short_waits ? kShortWaitTicks : kWaitTicks;
   p.perturb = L.perturb ? 1 : 0;
+  p.overlap_next = L.overlap_next ? 1 : 0;
   p.trace_tiles = int64_t(L.trace_tickets);
   for (int ph = 0, w = 4; ph < 4; w += 2 * int(L.unf_grid[ph]), ++ph) p.ph_rec[ph] = w;
   p.slot_bytes = int64_t(L.slot_bytes); p.slot_x = int64_t(L.slot_x);

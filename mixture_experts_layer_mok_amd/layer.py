@@ -113,3 +113,29 @@ class MoKLayer:
                              device=self.device)
         L.mok_quantize_mx(w, rows, cols, codes, scales, stream)
         return codes, scales
+
+
+def forward_macrobatches(layers, streams, batches, ys):
+    """Forwards of successive macrobatches with the combine of each overlapping the
+    dispatch of the next: macrobatch i runs on layers[i % 2] (their own workspaces, built
+    with MOK_FLAG_OVERLAP_NEXT) and streams[i % 2], so a workspace is reused only by the
+    next call on its own stream.  Each schedule is issued ahead of the previous
+    macrobatch's forward, so it never waits behind it.  batches[i] = (x, ids, gates, wg,
+    wu, wd[, scales]); ys[i] receives the output.  Returns without synchronising."""
+    n = len(batches)
+
+    def args(i):
+        b = batches[i]
+        return b[:6], (b[6] if len(b) > 6 else (None, None, None))
+
+    if n == 0:
+        return ys
+    layers[0].schedule(batches[0][1], stream=streams[0])
+    for i in range(n):
+        if i + 1 < n:
+            j = (i + 1) % 2
+            layers[j].schedule(batches[i + 1][1], stream=streams[j])
+        (x, ids, gates, wg, wu, wd), sc = args(i)
+        layers[i % 2].forward(x, ids, gates, wg, wu, wd, scales=sc, y=ys[i],
+                              stream=streams[i % 2])
+    return ys
