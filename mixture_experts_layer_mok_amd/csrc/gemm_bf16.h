@@ -104,6 +104,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(0) lgkmcnt(0): every load of this wave has landed, global and LDS.
+// Before the barrier that frees a stage this matters for the LDS reads too: once past
+// the barrier, other waves start direct-to-LDS loads into the stage those reads use.
+__device__ __forceinline__ void wait_loads_and_lds() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (0 << 14));
+}
+
 struct TileAcc {
   f32x16_t c[4][2];
 };
@@ -272,7 +279,7 @@ __device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa
   frag_mma(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if (kb + 1 < nk) {
-    wait_vmcnt<0>();
+    wait_loads_and_lds();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
@@ -604,7 +611,7 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
   frag_mma(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if (kb + 1 < nk) {
-    wait_vmcnt<0>();
+    wait_loads_and_lds();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (kb + 2 < nk) {

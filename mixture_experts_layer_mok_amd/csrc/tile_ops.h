@@ -69,9 +69,10 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // once to bf16; g_j = gates[q0 + j], or 1 without gates.  rows holds pair-indexed rows of
 // D bf16.  One wave per destination row; lane l owns the 16-byte chunks l, l + 64, ....
 // With a single slot (the usual case of an even expert share) the row is processed in
-// passes of kRowBatch chunks per lane; otherwise the wave loads kCombChunks chunks of
-// kSlots slots at a time (8 kSlots loads per lane in flight; the forward's data movers
-// take 4, which their registers allow beside the tile code of the same kernel).  Source
+// passes of kRowBatch chunks per lane; otherwise the wave loads kChunks chunks of kSlots
+// slots at a time (kChunks kSlots loads per lane in flight; the forward's data movers
+// take 4 slots of kCombChunks, which their registers allow beside the tile code of the
+// same kernel).  Source
 // loads use the cache policy kPol (device scope for rows written by other workgroups of
 // a running kernel); every access goes through a row-length buffer resource.
 constexpr int kCombChunks = 8;
@@ -92,7 +93,7 @@ __device__ __forceinline__ v4u pack_acc(const float (&acc)[8]) {
 // The same with the slots' rows and gates already loaded: lane j < k holds my_pos =
 // pos[q0 + j] and my_g = gates[q0 + j] (1 without gates); other lanes -1 and 0.  A caller
 // that walks tokens loads the next token's values while this one is summed.
-template <int kPol, int kSlots>
+template <int kPol, int kSlots, int kChunks = kCombChunks>
 __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16_t* rows,
                                                      int64_t q0, int D, int32_t my_pos,
                                                      float my_g) {
@@ -117,10 +118,10 @@ __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16
     }
     return;
   }
-  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kCombChunks) {
-    float acc[kCombChunks][8];
+  for (uint32_t b0 = 0; b0 < bytes; b0 += 64 * 16 * kChunks) {
+    float acc[kChunks][8];
 #pragma unroll
-    for (int c = 0; c < kCombChunks; ++c)
+    for (int c = 0; c < kChunks; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
     uint64_t m = has;
@@ -135,9 +136,9 @@ __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16
         if (m) m &= m - 1;
         rs[u] = row_rsrc(rows + (q0 + (js[u] >= 0 ? js[u] : 0)) * D, js[u] >= 0 ? bytes : 0u);
       }
-      v4u v[kSlots][kCombChunks];
+      v4u v[kSlots][kChunks];
 #pragma unroll
-      for (int c = 0; c < kCombChunks; ++c)
+      for (int c = 0; c < kChunks; ++c)
 #pragma unroll
         for (int u = 0; u < kSlots; ++u) v[u][c] = buf_ld16<kPol>(rs[u], b0 + (lane + 64 * c) * 16);
 #pragma unroll
@@ -145,12 +146,12 @@ __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16
         if (js[u] >= 0) {  // wave-uniform
           const float g = __shfl(my_g, js[u]);
 #pragma unroll
-          for (int c = 0; c < kCombChunks; ++c) acc_gated(acc[c], v[u][c], g);
+          for (int c = 0; c < kChunks; ++c) acc_gated(acc[c], v[u][c], g);
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < kCombChunks; ++c)
+    for (int c = 0; c < kChunks; ++c)
       buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
   }
 }

@@ -30,6 +30,30 @@ def _check_schedule(cfg, d, ids, layer):
     return tab
 
 
+@pytest.mark.parametrize("T,k,E,e0,nl", [
+    (3000, 4, 64, 3, 40),      # 17..64 local experts: ranking rounds, bases in registers
+    (2000, 6, 300, 10, 200),   # more than 64: bases in LDS
+    (70000, 8, 32, 0, 16),     # count table above the fused-scan size: separate scan launch
+    (70000, 8, 128, 5, 40),    # the same with ranking rounds
+], ids=["nl40", "nl200", "big-nl16", "big-nl40"])
+def test_schedule_paths_bit_exact(T, k, E, e0, nl):
+    """mok_schedule against the oracle bit for bit on every placement path: one ballot per
+    expert (<= 16 local experts, the other tests), ranking rounds with the next rows in
+    registers (<= 64) or in LDS (more), and count tables too large for the scan to be
+    folded into the place kernel; with masked and out-of-range ids."""
+    rng = np.random.default_rng(T + nl)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids = gen.mask_ids(ids, 0.05, seed=nl)
+    ids[::97, 0] = E + 1  # out of range: flagged and skipped
+    cfg = gen.small_config("sched", T=T, D=64, I=64, E=E, k=k, e0=e0, E_loc=nl, M=512, S=2)
+    say(f"[schedule] T={T} k={k} E={E} nl={nl}")
+    layer = MoKLayer(L.desc_from_config(cfg))
+    layer.schedule(torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    tab = _check_schedule(cfg, None, ids, layer)
+    assert tab["status"] == L.MOK_DEV_BAD_ID
+
+
 SMALL = [
     gen.CONFIGS[1],
     gen.small_config("ragged", T=300, D=192, I=192, E=6, k=2, M=96, S=2, comm_cus=8),
