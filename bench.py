@@ -29,6 +29,8 @@ against the MFMA peak.  `mxfp8_fwd` does the same for the MXFP8 forward (config 
 `mxfp8_fwd_bwd` times forward + backward on that workload in MXFP8 and in bf16.
 `macrobatch` compares successive forwards run one after another with the same forwards
 interleaved as macrobatches (MOK_FLAG_OVERLAP_NEXT, two workspaces and streams).
+`ring_recycling` times the step again with 4 and 2 ring slots (fewer than the
+minibatches): slots recycle inside the forward and the backward replays GEMM1.
 `cpu_baseline` times the float64 NumPy oracle (forward + backward) on this host's cores.
 """
 from __future__ import annotations
@@ -69,6 +71,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward figure")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the step timed with fewer ring slots than minibatches")
     ap.add_argument("--no-macrobatch", action="store_true",
                     help="skip the macrobatch interleave figure")
     ap.add_argument("--no-phases", action="store_true",
@@ -508,6 +512,40 @@ def macrobatch_figure(args, n=4):
             "first_call_us": round(end0 * 0.01, 1)}
 
 
+def ring_figure(args):
+    """The config-5 step (forward + backward) with fewer ring slots than minibatches, so
+    that the timed step recycles slots inside the forward and replays GEMM1 for the
+    recycled minibatches in the backward (the headline keeps every minibatch resident).
+    The replay's flops are not counted in the rate."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import _lib as L
+    from mixture_experts_layer_mok_amd import gen
+    from mixture_experts_layer_mok_amd.layer import MoKLayer
+    base = gen.CONFIGS[5]
+    dev = torch.device("cuda:0")
+    d, t, _ = setup(base, False, True, dev)
+    R = routed_rows(base, d["ids"])
+    n_mb = -(-R // base.M)
+    out = {"workload": f"{base.name}, M={base.M}: {n_mb} minibatches", "slots": {}}
+    for S in (base.S, 4, 2):
+        cfg = base.replace(S=S)
+        layer = MoKLayer(L.desc_from_config(cfg, flags=L.MOK_FLAG_SAVE_FOR_BWD), device=dev)
+        log(f"timing the step with {S} ring slots")
+        r = time_layer(cfg, t, layer, max(3, args.steps // 2), args.warmup, True)
+        ms = r["ms_per_step"]
+        out["slots"][str(S)] = {
+            "replayed_minibatches": max(0, n_mb - S), "ms_per_step": round(ms, 4),
+            "fwd_ms": stats(r["fwd_ms"]), "bwd_ms": stats(r["bwd_ms"]),
+            "tflops": round(18.0 * cfg.D * cfg.I * R / (ms * 1e-3) / 1e12, 2),
+            "workspace_GB": round(L.mok_workspace_size(layer.desc) / 1e9, 3)}
+        del layer
+        torch.cuda.empty_cache()
+    del t, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def trace_forward(args):
     """Warm-up forwards, then one forward with MOK_FLAG_TRACE on the same workload, decoded
     into where the compute and data-mover workgroups spent the kernel's span."""
@@ -682,6 +720,8 @@ def main():
         out["mxfp8_fwd_bwd"] = mx_backward_figure(args)
     if not args.no_macrobatch and args.config == 5:
         out["macrobatch"] = macrobatch_figure(args)
+    if not args.no_ring and args.config == 5:
+        out["ring_recycling"] = ring_figure(args)
     if not args.no_cpu_baseline:
         import oracle as O
         log("timing the float64 oracle on the host")
