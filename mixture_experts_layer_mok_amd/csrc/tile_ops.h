@@ -172,7 +172,7 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
 // The gate/up pre-activations of a GEMM1 tile (paired layout, as in epi_swiglu) stored
 // as bf16 rows [rows, 2I] at AB: gate in [0, I), up in [I, 2I).  Staged in LDS as rows of
 // 256 columns (tile rows 0..127 in the A stages, 128..255 in the B stages), then written
-// as whole row segments, 8 bytes a lane.  Ends with a barrier.
+// as whole row segments, 16 bytes a lane.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n0, int I,
                                              uint16_t* AB) {
@@ -185,8 +185,6 @@ __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n
   const int wr = __builtin_amdgcn_readfirstlane(w);
   const bool gate_lane = (lane & 16) == 0;
   const int rbit = lane >> 5;  // bit 2 of every row this lane holds
-  const int l32 = lane & 31, half = lane >> 5;
-  const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
   lds_u16_t* st = stage16(w >> 2);
   auto stage_row = [](int r) { return stage16(r >> 7); };
   {
@@ -202,22 +200,25 @@ __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n
           st[(acc_row(tid, i, v) & 127) * 256 + c] = f32_to_bf16(acc.c[i][j][v]);
       }
     __syncthreads();
-    // wave w: rows w, w + 8, ..; lanes 0..31 write the gate segment, 32..63 the up one
-    constexpr int kRows = 256 / W;
-    uint64_t val[kRows];
+    // wave w: row pairs 2w, 2w + 1, 2w + 16, ..: lanes 0..31 write one row, 32..63 the
+    // next; in each half-wave 16 lanes write the gate segment and 16 the up segment
+    constexpr int kPairs = 128 / W;
+    const int rs = lane >> 5, seg = (lane >> 4) & 1, l16 = lane & 15;
+    const bool col16_ok = n0 + 8 * l16 < I;  // I % 64 == 0: an 8-column group is all in or out
+    v4u val[kPairs];
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const int r = wr + W * k;
-      const int c = (4 * l32 + 128 * half) ^ (((half << 1) | ((r >> 2) & 1)) << 4);
-      val[k] = *reinterpret_cast<lds_cu64_t*>(stage_row(r) + (r & 127) * 256 + c);
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * (wr + W * k) + rs;
+      const int c = (8 * l16 + 128 * seg) ^ (((seg << 1) | ((r >> 2) & 1)) << 4);
+      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 256 + c);
     }
     const rsrc_t rab = row_rsrc(AB, uint32_t(rows) * uint32_t(2 * I) * 2u);
-    const uint32_t coff = uint32_t((half ? I : 0) + n0 + 4 * l32) * 2u;
+    const uint32_t coff = uint32_t((seg ? I : 0) + n0 + 8 * l16) * 2u;
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const int r = wr + W * k;
-      if (r >= rows) break;  // wave-uniform
-      if (col_ok) buf_st8<kPol>(rab, uint32_t(r) * uint32_t(2 * I) * 2u + coff, val[k]);
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * (wr + W * k) + rs;
+      if (2 * (wr + W * k) >= rows) break;  // wave-uniform; the odd row is checked below
+      if (col16_ok && r < rows) buf_st16<kPol>(rab, uint32_t(r) * uint32_t(2 * I) * 2u + coff, val[k]);
     }
     __syncthreads();
   }
@@ -230,7 +231,7 @@ __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n
 // Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
 // [rows, 2I]: gate in [0, I), up in [I, 2I).  h is formed from the fp32 accumulators.
 // Each output is staged in LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255
-// in the B stages) and then written as whole row segments, 8 bytes a lane.  Staged
+// in the B stages) and then written as whole row segments, 16 bytes a lane.  Staged
 // columns are XOR-swizzled in 16-column groups by (up half, bit 2 of the row), so that
 // the four lane groups of an MFMA block that write at once hit different banks.  With
 // kCoherent both are written at device scope: in the fused kernel a ring slot is
@@ -249,8 +250,6 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
   const int wr = __builtin_amdgcn_readfirstlane(w);
   const bool gate_lane = (lane & 16) == 0;
   const int rbit = lane >> 5;  // bit 2 of every row this lane holds
-  const int l32 = lane & 31, half = lane >> 5;
-  const bool col_ok = n0 + 4 * l32 < I;  // I % 64 == 0: a 4-column group is all in or out
   lds_u16_t* st = stage16(w >> 2);
   auto stage_row = [](int r) { return stage16(r >> 7); };
   if (AB) epi_store_ab<kCoherent>(acc, rows, n0, I, AB);
@@ -279,22 +278,24 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
         }
       }
     __syncthreads();
-    // wave w: row pairs w, w + 8, ..; a 256-byte segment is 32 lanes: two rows a store
-    constexpr int kPairs = 128 / W;
-    uint64_t val[kPairs];
+    // wave w: row quads w, w + 8, ..; a 256-byte segment is 16 lanes: four rows a store
+    constexpr int kQuads = 64 / W;
+    const int rq = lane >> 4, l16 = lane & 15;
+    const bool col16_ok = n0 + 8 * l16 < I;
+    v4u val[kQuads];
 #pragma unroll
-    for (int k = 0; k < kPairs; ++k) {
-      const int r = 2 * (wr + W * k) + half;
-      const int c = (4 * l32) ^ (((r >> 2) & 1) << 4) ^ (((r >> 4) & 1) << 3);
-      val[k] = *reinterpret_cast<lds_cu64_t*>(stage_row(r) + (r & 127) * 128 + c);
+    for (int k = 0; k < kQuads; ++k) {
+      const int r = 4 * (wr + W * k) + rq;
+      const int c = (8 * l16) ^ (((r >> 2) & 1) << 4) ^ (((r >> 4) & 1) << 3);
+      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 128 + c);
     }
     const rsrc_t rh = row_rsrc(H, uint32_t(rows) * uint32_t(ldh) * 2u);
-    const uint32_t coff = uint32_t(n0 + 4 * l32) * 2u;
+    const uint32_t coff = uint32_t(n0 + 8 * l16) * 2u;
 #pragma unroll
-    for (int k = 0; k < kPairs; ++k) {
-      const int r = 2 * (wr + W * k) + half;
-      if (2 * (wr + W * k) >= rows) break;  // wave-uniform; the odd row is checked below
-      if (col_ok && r < rows) buf_st8<kPol>(rh, uint32_t(r) * uint32_t(ldh) * 2u + coff, val[k]);
+    for (int k = 0; k < kQuads; ++k) {
+      const int r = 4 * (wr + W * k) + rq;
+      if (4 * (wr + W * k) >= rows) break;  // wave-uniform; later rows are checked below
+      if (col16_ok && r < rows) buf_st16<kPol>(rh, uint32_t(r) * uint32_t(ldh) * 2u + coff, val[k]);
     }
     __syncthreads();
   }
