@@ -89,6 +89,32 @@ __device__ __forceinline__ void mx_src_init(MxSrc& s, int layout, const uint8_t*
   s.half_last = (K & 127) != 0;
 }
 
+// As mx_src_init with the A rows gathered: tile row r (clamped to rows_valid - 1) is row
+// rowmap[r] / k of the code matrix A [*, lda] and of its scales As [*, as_ld] (A holds
+// fewer than 2^31 bytes, checked on the host).
+__device__ __forceinline__ void mx_src_init_gather(MxSrc& s, int layout, const uint8_t* A,
+                                                   const uint8_t* As, int64_t lda, int64_t as_ld,
+                                                   const int32_t* rowmap, int k, int rows_valid,
+                                                   const uint8_t* B0, const uint8_t* B0s,
+                                                   const uint8_t* B1, const uint8_t* B1s,
+                                                   int64_t ldb, int64_t bs_ld, int nb0, int nb1,
+                                                   int N, int K) {
+  mx_src_init(s, layout, A, As, lda, as_ld, rows_valid, B0, B0s, B1, B1s, ldb, bs_ld, nb0, nb1,
+              N, K);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < geom::kLoads; ++p) {
+    int r = geom::dma_row(p, w, l);
+    if (r > rows_valid - 1) r = rows_valid - 1;
+    s.data.oa[p] = uint32_t(int64_t(rowmap[r] / k) * lda + geom::dma_chunk(w, l) * 16);
+  }
+  if (w < 4) {
+    int r = geom::mx_scale_row(w, l);
+    if (r > rows_valid - 1) r = rows_valid - 1;
+    s.scale = As + int64_t(rowmap[r] / k) * as_ld;
+  }
+}
+
 // Loads of step ks into stage STAGE: 4 A + 4 B data loads and one scale load per lane,
 // with no branches (a branch here lets the compiler move the MFMAs around it).
 //   valid = false: the step does not exist; the data loads are made out of range (no

@@ -71,8 +71,9 @@ struct Layout {
   // backward (present with MOK_FLAG_SAVE_FOR_BWD)
   int64_t nNdh;     // n-tiles of the dH GEMM (over I)
   size_t off_bab, off_bdab, off_dxbuf, off_dgpart, off_gh, off_dyb, off_xb;
-  // MXFP8 backward (MXFP8 forward that saves): dY rows gathered and quantised along D
-  // (codes [T*k, D], scales [T*k, xs_ld]), [da | db] rows quantised along I per half
+  // MXFP8 backward (MXFP8 forward that saves): dY quantised along D once per token
+  // (codes [T, D], scales [T, xs_ld]; the dH tiles gather them by token), [da | db] rows
+  // quantised along I per half
   // (codes [T*k, 2I], scales [T*k, 2I / 32]), and W_down^T's scales repacked to the
   // tile's stride when D % 128 != 0
   size_t off_dyq, off_dyqs, off_dabq, off_dabqs, off_wdts;
@@ -200,8 +201,8 @@ inline mok_status_t make_layout(const mok_desc_t* d, Layout* L) {
   L->repack_wdt = L->mx && L->save && D % 128 != 0;
   if (L->mx && L->save) {
     const size_t TK = size_t(L->TK);
-    L->off_dyq = o; o = align_up(o + TK * D, A);
-    L->off_dyqs = o; o = align_up(o + TK * L->xs_ld, A);
+    L->off_dyq = o; o = align_up(o + size_t(L->T) * D, A);
+    L->off_dyqs = o; o = align_up(o + size_t(L->T) * L->xs_ld, A);
     L->off_dabq = o; o = align_up(o + TK * 2 * I, A);
     L->off_dabqs = o; o = align_up(o + TK * L->abq_ld, A);
     if (L->repack_wdt) { L->off_wdts = o; o = align_up(o + size_t(nl) * I * L->xs_ld, A); }

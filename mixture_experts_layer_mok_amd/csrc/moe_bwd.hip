@@ -112,11 +112,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows(BwdParams p) {
 // MXFP8: dY row perm[r] / k of every routed row r, quantised along D into row r of the
 // dY code buffer (one wave per row).
 __global__ __launch_bounds__(256) void k_bwd_dyq(BwdParams p) {
-  const int R = int(p.P.hdr[kHdrR]);
   const int nw = gridDim.x * 4;
-  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += nw)
-    wave_quant_row<false>(p.P.dyq + int64_t(r) * p.D, p.P.dyqs + int64_t(r) * p.xs_ld,
-                          p.a.dy + int64_t(p.P.perm[r] / p.k) * p.D, p.D);
+  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < p.T; t += nw)
+    wave_quant_row<false>(p.P.dyq + int64_t(t) * p.D, p.P.dyqs + int64_t(t) * p.xs_ld,
+                          p.a.dy + int64_t(t) * p.D, p.D);
 }
 
 // ------------------------------------------------------------------------------------
@@ -178,14 +177,14 @@ __device__ __forceinline__ uint32_t dh_tile(const BwdParams& p, int g, int nt) {
   const int n0 = nt * kBN2;
   TileAcc acc;
   if (MX) {
-    // A = the m-tile's quantised dY rows (written by the previous launch), B = W_down^T
-    // codes of the expert: rows n0 .. n0 + 255 of [I, D], K = D
+    // A = the quantised dY rows of the m-tile's tokens (quantised once per token by the
+    // previous launch), gathered; B = W_down^T codes of the expert: rows n0 .. n0 + 255
+    // of [I, D], K = D
     const uint8_t* B = p.a.wdt + int64_t(e.z) * wsz;
     const uint8_t* Bs = p.wdts + int64_t(e.z) * p.I * p.wdts_ld;
     MxSrc src;
-    mx_src_init(src, geom::kSplit, p.P.dyq + int64_t(e.x) * p.D,
-                p.P.dyqs + int64_t(e.x) * p.xs_ld, p.D, p.xs_ld, e.y, B, Bs, B, Bs, p.D,
-                p.wdts_ld, n0, n0 + 128, p.I, p.D);
+    mx_src_init_gather(src, geom::kSplit, p.P.dyq, p.P.dyqs, p.D, p.xs_ld, p.P.perm + e.x, p.k,
+                       e.y, B, Bs, B, Bs, p.D, p.wdts_ld, n0, n0 + 128, p.I, p.D);
     mx_gemm<false>(src, p.D, acc);
   } else {
     const uint16_t* wd = p.a.wd + e.z * wsz;
@@ -457,7 +456,7 @@ mok_status_t launch_backward(const Layout& L, const Ptrs& P, const BwdArgs& a, h
                      dim3(256), 0, st, p);
   if (L.mx) {
     if (L.repack_wdt) launch_mx_repack(a.wdts, L.nl * L.I, int(L.D / 32), P.wdts, int(L.xs_ld), st);
-    hipLaunchKernelGGL(k_bwd_dyq, dim3(unsigned(std::min<int64_t>((L.TK + 3) / 4, 65536))),
+    hipLaunchKernelGGL(k_bwd_dyq, dim3(unsigned(std::min<int64_t>((L.T + 3) / 4, 65536))),
                        dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_bwd_main<true>, tiles_grid, dim3(kThreads), 0, st, p);
   } else {
