@@ -253,18 +253,6 @@ def mx_roundtrip(v: np.ndarray) -> np.ndarray:
     return mx_dequantize(*mx_quantize(v))
 
 
-def mx_roundtrip_rows(v: np.ndarray) -> np.ndarray:
-    """MX round trip of v [n, c] along its first axis: for each column, blocks of 32
-    consecutive rows from row 0; a short last block is quantised as if padded with zeros
-    (zeros change neither the block's largest magnitude nor the other codes)."""
-    v = np.asarray(v, dtype=np.float64)
-    n = v.shape[0]
-    if n == 0:
-        return v.copy()
-    vt = np.concatenate([v.T, np.zeros((v.shape[1], -n % MX_BLOCK))], axis=1)
-    return mx_roundtrip(vt)[:, :n].T
-
-
 # =================================================================================
 # Forward and backward
 # =================================================================================
@@ -318,12 +306,10 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
       dW_down[e] += (g dy[t])^T h;  dW_gate[e] += da^T x;  dW_up[e] += db^T x
       dx_row = da W_gate[e] + db W_up[e];   dX[t] = sum over local slots of dx_row
     With ``mxfp8`` (the MXFP8 mode covers the backward, [L] §03): a and b are those of the
-    MXFP8 forward, and every backward GEMM reads MX round-tripped operands, each quantised
-    along that GEMM's K: u from dy rows and W_down quantised along D; dx_row from da, db
-    and W_gate, W_up quantised along I; the weight gradients, whose K is the expert's
-    rows, from dy, g h, da, db and x quantised along those rows (blocks of 32 rows from
-    the expert's first row).  da, db and g h are quantised from their float32 values;
-    dG uses the unquantised u and h.
+    MXFP8 forward, and the two GEMMs that produce data gradients read MX round-tripped
+    operands, each quantised along that GEMM's K: u from dy rows and W_down quantised
+    along D; dx_row from da, db (from float32) and W_gate, W_up quantised along I.  dG
+    and the weight gradients use the unquantised u, h, da, db, x and dy.
     Returns dict(dx [T, D], dg [T, k], dwg, dwu [n_local, I, D], dwd [n_local, D, I])."""
     T, k = ids.shape
     n_local, I, D = wg.shape
@@ -360,17 +346,9 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
         s = sigmoid(a)
         da = dh * b * s * (1.0 + a * (1.0 - s))
         db = dh * silu(a)
-        if mxfp8:
-            # weight gradients: K is the expert's rows, so both operands are quantised
-            # along them
-            xr = mx_roundtrip_rows(xe)
-            dwd[e] = mx_roundtrip_rows(dye).T @ mx_roundtrip_rows((g * h).astype(np.float32))
-            dwg[e] = mx_roundtrip_rows(da.astype(np.float32)).T @ xr
-            dwu[e] = mx_roundtrip_rows(db.astype(np.float32)).T @ xr
-        else:
-            dwd[e] = (g * dye).T @ h
-            dwg[e] = da.T @ xe
-            dwu[e] = db.T @ xe
+        dwd[e] = (g * dye).T @ h
+        dwg[e] = da.T @ xe
+        dwu[e] = db.T @ xe
         if mxfp8:
             # W_gate, W_up [I, D] quantised along I: the round trips of their transposes
             dxr[r0:r1] = (mx_roundtrip(da.astype(np.float32)) @ mx_roundtrip(wg_e.T).T +
