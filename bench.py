@@ -559,7 +559,7 @@ def trace_forward(args):
     over = {k: v for k, v in (("M", args.M), ("S", args.S), ("comm_cus", args.comm_cus)) if v}
     cfg = cfg.replace(**over)
     dev = torch.device("cuda:0")
-    save = cfg.precision == L.MOK_PREC_BF16 and args.config == 5
+    save = args.config == 5 or cfg.precision == L.MOK_PREC_MXFP8
     d, t, layer = setup(cfg, False, save, dev)
     flags = L.MOK_FLAG_TRACE | (L.MOK_FLAG_SAVE_FOR_BWD if save else 0)
     tl = MoKLayer(L.desc_from_config(cfg, flags=flags), device=dev)
@@ -583,7 +583,10 @@ def trace_forward(args):
     if save:
         # the backward's persistent launch, traced on the same workspace (its records
         # replace the forward's)
-        tl.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
+        if "wt" in t:
+            tl.backward_mx(t["dy"], t["x"], t["ids"], t["gates"], t["wt"])
+        else:
+            tl.backward(t["dy"], t["x"], t["ids"], t["gates"], t["wg"], t["wu"], t["wd"])
         torch.cuda.synchronize()
         if tl.status() != 0:
             raise SystemExit(f"device status {tl.status():#x} after the backward")

@@ -85,14 +85,17 @@ def summarize(tiles: np.ndarray, wgs: np.ndarray, comm_cus: int) -> dict:
     return out
 
 
-BWD_KINDS = ("dh", "dx", "dw", "row_sums")
+BWD_KINDS = ("dh", "dx", "dw", "row_sums", "mx_quant")
 
 
 def bwd_tickets(desc, m_tiles: int) -> int:
-    """Tickets of the backward's persistent launch: dH, dX, dW tiles and row-sum chunks."""
+    """Tickets of the backward's persistent launch: dH, dX, dW tiles and row-sum chunks,
+    and in MXFP8 one quantisation ticket per m-tile."""
+    from . import _lib as L
     nDt = (desc.hidden + 255) // 256
     nIt = (desc.intermediate + 255) // 256
-    return m_tiles * (nIt + nDt) + desc.num_local_experts * 3 * nDt * nIt + \
+    mx = 1 if desc.precision == L.MOK_PREC_MXFP8 else 0
+    return m_tiles * (nIt + nDt + mx) + desc.num_local_experts * 3 * nDt * nIt + \
         (desc.num_tokens + 31) // 32
 
 
@@ -119,7 +122,8 @@ def summarize_bwd(recs: np.ndarray, wgs: np.ndarray) -> dict:
         busy += float((t_end - t_tk)[m].sum())
         out["kinds"][name] = {
             "n": int(m.sum()), "wait_us": round(float(wait.mean()) * TICK_US, 2),
-            "k_loop_us" if k < 3 else "sum_us": round(float(body.mean()) * TICK_US, 2),
+            ("k_loop_us" if k < 3 else "sum_us" if k == 3 else "work_us"):
+                round(float(body.mean()) * TICK_US, 2),
             "epilogue_us": round(float(epi.mean()) * TICK_US, 2),
             "share": round(float((t_end - t_tk)[m].sum()) / tot, 4)}
     out["outside_tickets_share"] = round(1.0 - busy / tot, 4)
