@@ -74,6 +74,14 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
   return r;
 }
 
+// The resource, or with `empty` the same one with no records: a load through it reads no
+// memory and returns zeros (the loads a K loop issues past its last step).
+__device__ __forceinline__ i32x4_t rsrc_or_empty(const i32x4_t& r, bool empty) {
+  i32x4_t e = r;
+  e.z = empty ? 0 : r.z;
+  return e;
+}
+
 // Direct-to-LDS load of 16 bytes per lane from rsrc + voff + soff: lane l's bytes land
 // at LDS address lds_wave_base + 16 * l (the wave-uniform base travels in M0).  COH adds
 // sc1 (device scope).
@@ -235,7 +243,8 @@ __device__ __forceinline__ void frag_mma(const TileFrag& f, TileAcc& acc) {
 static __shared__ v4u g_lds_dummy[(kThreads / 64) * 64];
 
 // One direct-to-LDS load (q = 0..3: A load q; 4..7: B load q - 4) into stage STAGE, or,
-// with `dummy`, into the scratch area (loads past the last step: no branch in the step).
+// with `dummy`, into the scratch area through an empty resource (loads past the last
+// step: no branch in the step and no memory read).
 template <bool COH, int STAGE>
 __device__ __forceinline__ void tile_issue_sel(const TileSrc& s, int k0, int q, bool dummy) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -246,12 +255,12 @@ __device__ __forceinline__ void tile_issue_sel(const TileSrc& s, int k0, int q, 
                        : lds_addr(stage_b<STAGE>() + ((q - 4) * 8 + w) * 64);
   dst = dummy ? lds_addr(g_lds_dummy) + uint32_t(w) * 1024u : dst;
   if (q < 4) {
-    dma16_at<COH>(s.ra, s.oa[q], kb, dst);
+    dma16_at<COH>(rsrc_or_empty(s.ra, dummy), s.oa[q], kb, dst);
   } else {
     const int p = q - 4;
     const bool paired_up = s.layout == geom::kPaired && ((w >> 1) & 1);
     const bool use_b1 = s.layout == geom::kPaired ? paired_up : (p >= 2);
-    dma16_at<false>(use_b1 ? s.rb1 : s.rb0, s.ob[p], kb, dst);
+    dma16_at<false>(rsrc_or_empty(use_b1 ? s.rb1 : s.rb0, dummy), s.ob[p], kb, dst);
   }
 }
 
@@ -261,7 +270,8 @@ __device__ __forceinline__ void tile_issue_sel(const TileSrc& s, int k0, int q, 
 // vector-memory command queue and holds up the MFMAs behind it (measured on MI355X:
 // 1091 -> 1121 TFLOP/s on a plain 16384 x 4096 x 7168 GEMM).  That needs a step body
 // without a branch around the MFMAs (with one, the compiler spills), so the loads are
-// always issued; past the last step they re-read step kb into g_lds_dummy.
+// always issued; past the last step they go to g_lds_dummy through an empty resource
+// (no memory read).
 template <bool COH, int S>
 __device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa, int kb, int nk,
                                           TileFrag& f0, TileFrag& f1, TileAcc& acc) {
@@ -284,7 +294,7 @@ __device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa
     asm volatile("" ::: "memory");
   }
   __builtin_amdgcn_sched_barrier(0);
-  // loads of step kb + 2; past the end they re-read step kb into the scratch area
+  // loads of step kb + 2; past the end they go to the scratch area and read nothing
   const bool past = kb + 2 >= nk;
   const int kn = __builtin_amdgcn_readfirstlane(past ? kb * kBK : (kb + 2) * kBK);
   frag_load<SN>(f0, fa, 0);  // past the last step: stale, unused
@@ -569,7 +579,8 @@ __device__ __forceinline__ void km_issue_step(KmOp& a, KmOp& b, int k0) {
 }
 
 // Load p (0..3) of one K step of a non-gathered K-major or K-contiguous operand, into
-// stage STAGE of lds, or with `dummy` into g_lds_dummy (loads past the last step).
+// stage STAGE of lds, or with `dummy` into g_lds_dummy through an empty resource (loads
+// past the last step: they read no memory).
 template <int KIND, int STAGE>
 __device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* lds, bool dummy) {
   static_assert(KIND != kKG, "gathered operands are issued per step (km_issue)");
@@ -577,16 +588,16 @@ __device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* 
   const uint32_t dst = dummy ? lds_addr(g_lds_dummy) + uint32_t(w) * 1024u
                              : lds_addr(lds + STAGE * kStageChunks + (p * 8 + w) * 64);
   if (km_kcontig(KIND)) {
-    dma16_at<KIND == kKCD>(o.r0, o.off[p], uint32_t(k0) * 2, dst);
+    dma16_at<KIND == kKCD>(rsrc_or_empty(o.r0, dummy), o.off[p], uint32_t(k0) * 2, dst);
   } else if (KIND == kKW) {
     const bool second = k0 >= o.ksplit;
     const uint32_t so = uint32_t(second ? k0 - o.ksplit : k0) * o.ld2;
-    dma16_at<false>(second ? o.r1 : o.r0, o.off[p], so, dst);
+    dma16_at<false>(rsrc_or_empty(second ? o.r1 : o.r0, dummy), o.off[p], so, dst);
   } else {
     const int l = threadIdx.x & 63;
     const int r = o.rbeg + k0 + geom::km_row(p, w, l);
     const uint32_t voff = r < o.rend ? __umul24(uint32_t(r), o.ld2) + o.off[p] : kKmOutOfRange;
-    dma16_at<KIND == kKRD>(o.r0, voff, 0u, dst);
+    dma16_at<KIND == kKRD>(rsrc_or_empty(o.r0, dummy), voff, 0u, dst);
   }
 }
 
