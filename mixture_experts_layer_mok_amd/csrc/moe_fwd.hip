@@ -194,7 +194,7 @@ __device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
     const MxOperands o = mx_ops_gemm2(p, p.P.full_h + int64_t(e.x) * p.I,
                                       p.P.full_hs + int64_t(e.x) * p.hs_ld, e.z);
     run_tile_mx<false>(false, o, e.y, nt * kBN2, p.D, p.I, acc);
-    epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
+    epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
     return;
   }
   const uint16_t* H = reinterpret_cast<const uint16_t*>(p.P.full_h);
@@ -203,7 +203,7 @@ __device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
   run_tile<false>(false, H + int64_t(e.x) * p.I, e.y,
                   reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nullptr, nt * kBN2, p.D,
                   p.I, acc);
-  epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf);
+  epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
 }
 
 template <bool MX>
@@ -556,7 +556,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
                                           slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
         run_tile_mx<true>(false, o, e.y, n0, p.D, p.I, acc);
         const uint32_t t_k = trace ? trace_now() : 0u;
-        epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+        epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
         const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(done + mb, 1);
@@ -580,7 +580,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
       perturb_pause(p.perturb, tk);
       wg_signal_add(hd, 1);
     } else {
-      epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf);
+      epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
       t_e = trace ? trace_now() : 0u;
       perturb_pause(p.perturb, tk);
       wg_signal_add(done + mb, 1);

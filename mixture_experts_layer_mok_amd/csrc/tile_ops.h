@@ -303,15 +303,17 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
 
 // Epilogue of GEMM2 and of dX: rows [0, rows), columns [n0, n0 + 256) of D (B tile row b
 // is column n0 + b in the split layout); row r's result goes to obuf row perm_rows[r]
-// (its pair index t*k + j).  The tile is first staged in LDS as bf16 rows (tile rows
-// 0..127 in the A stages, 128..255 in the B stages; free once the K loop has ended), so
-// that each wave then writes whole 512-byte row segments, 8 bytes a lane, instead of
-// 2-byte pieces.  A row's staged columns are XOR-swizzled by 32 on bit 2 of the row: the
+// (its pair index t*k + j; obuf holds obuf_rows rows of D).  The tile is first staged in
+// LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255 in the B stages; free once
+// the K loop has ended), so that each wave then writes whole 512-byte row segments, 16
+// bytes a lane when every byte offset of obuf fits in 32 bits (two rows a store through
+// one resource), else 8 bytes a lane through a resource per row.  A row's staged columns are XOR-swizzled by 32 on bit 2 of the row: the
 // two half-waves of an MFMA block write rows 4 apart, which would otherwise share
 // banks.  With kCoherent the row stores are device scope.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
-                                            const int32_t* perm_rows, uint16_t* obuf) {
+                                            const int32_t* perm_rows, uint16_t* obuf,
+                                            int64_t obuf_rows) {
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -340,6 +342,31 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
   const int wr = __builtin_amdgcn_readfirstlane(w);
   const int my_r = wr + (kThreads / 64) * (lane % kRowsPerWave);
   const int my_dst = my_r < rows ? perm_rows[my_r] : 0;
+  if (obuf_rows * int64_t(D) * 2 < (int64_t(1) << 32)) {
+    // two rows a store, 16 bytes a lane (each half-wave one 512-byte row segment), with
+    // one resource for the whole buffer: every offset fits in 32 bits
+    const int h = lane >> 5, l32 = lane & 31;
+    v4u val[kRowsPerWave / 2];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave / 2; ++k) {
+      const int r = wr + (kThreads / 64) * (2 * k + h);
+      val[k] = *reinterpret_cast<__attribute__((address_space(3))) const v4u*>(
+          stage16(r >> 7) + (r & 127) * 256 + ((8 * l32) ^ (((r >> 2) & 1) << 5)));
+    }
+    const rsrc_t rb = row_rsrc(obuf, uint32_t(obuf_rows * int64_t(D) * 2));
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave / 2; ++k) {
+      const int r = wr + (kThreads / 64) * (2 * k + h);
+      if (wr + (kThreads / 64) * 2 * k >= rows) break;  // wave-uniform; row r checked below
+      const int d0 = __builtin_amdgcn_readlane(my_dst, 2 * k);
+      const int d1 = __builtin_amdgcn_readlane(my_dst, 2 * k + 1);
+      const int dst = h ? d1 : d0;
+      if (r < rows && n0 + 8 * l32 < D)
+        buf_st16<kPol>(rb, (uint32_t(dst) * uint32_t(D) + uint32_t(n0 + 8 * l32)) * 2u, val[k]);
+    }
+    __syncthreads();
+    return;
+  }
   uint64_t val[kRowsPerWave];
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
