@@ -322,21 +322,32 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
     dwg = np.zeros((n_local, I, D))
     dwu = np.zeros((n_local, I, D))
     dwd = np.zeros((n_local, D, I))
-    for e in range(n_local):
+    used = [e for e in range(n_local) if sch.offsets[e + 1] > sch.offsets[e]]
+    wq = {}
+    if mxfp8:
+        # the weights' round trips: W_gate, W_up along D (the forward's a, b); W_down along
+        # D (the round trip of its transpose) for u; W_gate, W_up along I for dx.  They are
+        # independent, so they run side by side (NumPy releases the interpreter lock)
+        mats = [(e, n, m) for e in used for n, m in
+                (("g", lambda e: wg[e]), ("u", lambda e: wu[e]), ("dt", lambda e: wd[e].T),
+                 ("gt", lambda e: wg[e].T), ("ut", lambda e: wu[e].T))]
+        with cf.ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+            for (e, n, _), v in zip(mats, ex.map(
+                    lambda t: mx_roundtrip(np.asarray(t[2](t[0]), np.float64)), mats)):
+                wq[e, n] = v
+    for e in used:
         r0, r1 = int(sch.offsets[e]), int(sch.offsets[e + 1])
-        if r0 == r1:
-            continue
         pairs = sch.perm[r0:r1]
         xe = xd[r0:r1]
         dye = dy64[pairs // k]
         wg_e, wu_e, wd_e = (np.asarray(w[e], np.float64) for w in (wg, wu, wd))
         if mxfp8:
             xq = mx_roundtrip(xe)
-            a = xq @ mx_roundtrip(wg_e).T
-            b = xq @ mx_roundtrip(wu_e).T
+            a = xq @ wq[e, "g"].T
+            b = xq @ wq[e, "u"].T
             h = silu(a) * b
             # W_down [D, I] quantised along D: the round trip of its transpose
-            u = mx_roundtrip(dye) @ mx_roundtrip(wd_e.T).T
+            u = mx_roundtrip(dye) @ wq[e, "dt"].T
         else:
             a, b, h, _ = expert_ffn(xe, wg_e, wu_e, wd_e)
             u = dye @ wd_e
@@ -351,8 +362,8 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
         dwu[e] = db.T @ xe
         if mxfp8:
             # W_gate, W_up [I, D] quantised along I: the round trips of their transposes
-            dxr[r0:r1] = (mx_roundtrip(da.astype(np.float32)) @ mx_roundtrip(wg_e.T).T +
-                          mx_roundtrip(db.astype(np.float32)) @ mx_roundtrip(wu_e.T).T)
+            dxr[r0:r1] = (mx_roundtrip(da.astype(np.float32)) @ wq[e, "gt"].T +
+                          mx_roundtrip(db.astype(np.float32)) @ wq[e, "ut"].T)
         else:
             dxr[r0:r1] = da @ wg_e + db @ wu_e
     dx = np.zeros((T, D))
