@@ -2,6 +2,7 @@
 hand-made records: shares of the compute workgroups' time and per-kind means."""
 import numpy as np
 
+from mixture_experts_layer_mok_amd import _lib as L
 from mixture_experts_layer_mok_amd import trace as TR
 
 
@@ -48,5 +49,7 @@ def test_backward_summary():
     assert k["dx"]["wait_us"] == 0.1 and k["dx"]["k_loop_us"] == 1.4
     assert k["row_sums"]["sum_us"] == 0.3 and "dw" not in k
     assert abs(s["outside_tickets_share"] - (1 - 290 / 400)) < 1e-4
-    assert TR.bwd_tickets(type("D", (), dict(hidden=512, intermediate=256, num_local_experts=2,
-                                             num_tokens=64))(), 3) == 3 * (1 + 2) + 2 * 3 * 2 + 2
+    shape = dict(hidden=512, intermediate=256, num_local_experts=2, num_tokens=64)
+    for prec, quant in ((L.MOK_PREC_BF16, 0), (L.MOK_PREC_MXFP8, 1)):
+        desc = type("D", (), dict(shape, precision=prec))()
+        assert TR.bwd_tickets(desc, 3) == 3 * (1 + 2 + quant) + 2 * 3 * 2 + 2
