@@ -46,9 +46,10 @@ Readings taken where the pages are silent:
   * MXFP8 mode quantises X (along D), W_gate/W_up (along D), W_down (along I) and
     H (along I, from its float32 value); all arithmetic between those points is exact
     float64 on the dequantised values;
-  * the MXFP8 backward quantises the operands of the two data-gradient GEMMs along
-    their K: dY and W_down along D (for u), da, db (from float32) and W_gate, W_up
-    along I (for dx); the weight gradients and dG use unquantised values.
+  * the MXFP8 backward reads a, b as the bfloat16 rows the MXFP8 forward saves, and
+    quantises the operands of the two data-gradient GEMMs along their K: dY and W_down
+    along D (for u), da, db (from their bfloat16 rows) and W_gate, W_up along I (for dx);
+    the weight gradients and dG use unquantised values.
 """
 from __future__ import annotations
 
@@ -253,6 +254,15 @@ def mx_roundtrip(v: np.ndarray) -> np.ndarray:
     return mx_dequantize(*mx_quantize(v))
 
 
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """v rounded to float32 and then to the nearest bfloat16 (ties to even), as float64:
+    the top 16 bits of the float32 pattern after adding 0x7FFF plus the lowest kept bit
+    (finite values)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 # =================================================================================
 # Forward and backward
 # =================================================================================
@@ -306,10 +316,11 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
       dW_down[e] += (g dy[t])^T h;  dW_gate[e] += da^T x;  dW_up[e] += db^T x
       dx_row = da W_gate[e] + db W_up[e];   dX[t] = sum over local slots of dx_row
     With ``mxfp8`` (the MXFP8 mode covers the backward, [L] §03): a and b are those of the
-    MXFP8 forward, and the two GEMMs that produce data gradients read MX round-tripped
+    MXFP8 forward, rounded to the bfloat16 rows it saves, and the two GEMMs that produce data gradients read MX round-tripped
     operands, each quantised along that GEMM's K: u from dy rows and W_down quantised
-    along D; dx_row from da, db (from float32) and W_gate, W_up quantised along I.  dG
-    and the weight gradients use the unquantised u, h, da, db, x and dy.
+    along D; dx_row from da, db (rounded to bfloat16, the rows the MX quantiser reads)
+    and W_gate, W_up quantised along I.  dG and the weight gradients use the
+    unquantised u, h, da, db, x and dy.
     Returns dict(dx [T, D], dg [T, k], dwg, dwu [n_local, I, D], dwd [n_local, D, I])."""
     T, k = ids.shape
     n_local, I, D = wg.shape
@@ -343,8 +354,9 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
         wg_e, wu_e, wd_e = (np.asarray(w[e], np.float64) for w in (wg, wu, wd))
         if mxfp8:
             xq = mx_roundtrip(xe)
-            a = xq @ wq[e, "g"].T
-            b = xq @ wq[e, "u"].T
+            # a and b as the MXFP8 forward saves them for the backward: bfloat16 rows
+            a = bf16_round(xq @ wq[e, "g"].T)
+            b = bf16_round(xq @ wq[e, "u"].T)
             h = silu(a) * b
             # W_down [D, I] quantised along D: the round trip of its transpose
             u = mx_roundtrip(dye) @ wq[e, "dt"].T
@@ -362,8 +374,8 @@ def backward(dy, x, ids, gates, wg, wu, wd, *, e0: int, E: int, M: int, mxfp8: b
         dwu[e] = db.T @ xe
         if mxfp8:
             # W_gate, W_up [I, D] quantised along I: the round trips of their transposes
-            dxr[r0:r1] = (mx_roundtrip(da.astype(np.float32)) @ wq[e, "gt"].T +
-                          mx_roundtrip(db.astype(np.float32)) @ wq[e, "ut"].T)
+            dxr[r0:r1] = (mx_roundtrip(bf16_round(da)) @ wq[e, "gt"].T +
+                          mx_roundtrip(bf16_round(db)) @ wq[e, "ut"].T)
         else:
             dxr[r0:r1] = da @ wg_e + db @ wu_e
     dx = np.zeros((T, D))

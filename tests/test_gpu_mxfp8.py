@@ -7,7 +7,8 @@ ceil scale rule).
   the encoding: all-zero blocks, subnormal bf16, amax exactly 448 * 2^n, mantissas
   just above and below 1.75, round-to-nearest-even ties, signs.
 - Layer outputs are compared by relative Frobenius error against the MX-emulating
-  oracle (bound 5e-2); the error against the unquantised oracle is printed only.
+  oracle (bound 1e-2; 5e-2 on a single row); the error against the unquantised oracle
+  is printed only.
 - Fused and unfused runs, and runs with other minibatch sizes, ring slots and comm CUs,
   must agree bit for bit; the config-4 run is repeated and compared bit for bit."""
 import numpy as np
@@ -21,7 +22,13 @@ from mixture_experts_layer_mok_amd.layer import MoKLayer, bf16_tensor
 from tests.gpu_util import DevInputs, rel_fro, row_errors, say, y_values
 
 pytestmark = pytest.mark.gpu
-TOL_MX = 5e-2
+# Relative Frobenius bar: the MX oracle applies the same round trips, and each code is
+# decided from values of the precision the kernels hold, so what is left is bf16 rounding
+# of stored values and float32 accumulation order, the bf16 bar.  A row can still hold a
+# code that the two accumulation orders put on either side of an e4m3 rounding midpoint
+# (one element off by one e4m3 step, up to 2^-3 of it), so the per-row bar is wider.
+TOL_MX = 1e-2
+TOL_MX_ROW = 5e-2
 
 
 class MxWeights:
@@ -140,8 +147,8 @@ def test_forward_config4_sampled_and_deterministic():
     oracle on sampled tokens: tokens of every local expert, and the tokens that own the
     rows on both sides of every minibatch window boundary and of the first m-tile start
     (256 rows from the expert's first row) at or after it; plus tokens with no local slot,
-    which must be exactly zero.  Relative Frobenius error and the largest per-row error
-    are both below 5e-2.  Then a bitwise repeat."""
+    which must be exactly zero.  Relative Frobenius error below 1e-2 and the largest
+    per-row error below 5e-2.  Then a bitwise repeat."""
     cfg = gen.CONFIGS[4]
     say("[c4] generating")
     d = gen.make_inputs(cfg)
@@ -176,5 +183,5 @@ def test_forward_config4_sampled_and_deterministic():
     yv = y_values(y)
     fro, worst, stray = row_errors(yv[toks], ref)
     say(f"[c4] sampled rel_fro vs MX oracle {fro:.3e}, worst row {worst:.3e}")
-    assert fro < TOL_MX and worst < TOL_MX and stray == 0
+    assert fro < TOL_MX and worst < TOL_MX_ROW and stray == 0
     assert np.all(yv[none] == 0)

@@ -1,8 +1,8 @@
 """GPU parity of the MXFP8 backward (mok_moe_bwd_mx) against the float64 oracle that
-applies the same MX round trips (oracle.backward(mxfp8=True): dY and W_down along D for
-u, da / db and W_gate / W_up along I for the dX rows; weight gradients unquantised):
-relative Frobenius error below 5e-2 on dX, dG and the three weight gradients, plus the
-largest per-row error of dX; the transposing weight quantiser bit-exact against the
+applies the same MX round trips (oracle.backward(mxfp8=True): a, b as saved bf16 rows; dY
+and W_down along D for u, da / db from their bf16 rows and W_gate / W_up along I for the
+dX rows; weight gradients unquantised): relative Frobenius error below 1e-2 on dX, dG and
+the three weight gradients, and below 5e-2 for the largest per-row error of dX; the transposing weight quantiser bit-exact against the
 oracle's quantiser; bitwise repeats and fused / unfused forwards giving the same
 gradients."""
 import numpy as np
@@ -17,7 +17,13 @@ from tests.gpu_util import DevInputs, rel_fro, row_errors, say
 from tests.test_gpu_mxfp8 import _edge_matrix
 
 pytestmark = pytest.mark.gpu
-TOL_MX = 5e-2
+# Relative Frobenius bar: the MX oracle applies the same round trips, and each code is
+# decided from values of the precision the kernels hold, so what is left is bf16 rounding
+# of stored values and float32 accumulation order, the bf16 bar.  A row can still hold a
+# code that the two accumulation orders put on either side of an e4m3 rounding midpoint
+# (one element off by one e4m3 step, up to 2^-3 of it), so the per-row bar is wider.
+TOL_MX = 1e-2
+TOL_MX_ROW = 5e-2
 
 
 def run_mx_fwd_bwd(cfg, dev, flags=0, **over):
@@ -43,7 +49,7 @@ def _compare(cfg, d, ids, g, tag):
         f" dx worst row={worst:.2e}")
     for k, v in errs.items():
         assert v < TOL_MX, (k, v)
-    assert worst < TOL_MX and stray == 0, (worst, stray)
+    assert worst < TOL_MX_ROW and stray == 0, (worst, stray)
     assert np.all(got["dg"][ref["schedule"].pos.reshape(ids.shape) < 0] == 0)
 
 
@@ -167,7 +173,7 @@ def test_backward_mx_config4_sampled():
     fro, worst, stray = row_errors(dx, ref["dx"])
     dg_err = rel_fro(g["dg"].cpu().numpy()[toks], ref["dg"])
     say(f"[mx-bwd c4] dx rel_fro {fro:.2e} worst row {worst:.2e}, dg {dg_err:.2e}")
-    assert fro < TOL_MX and worst < TOL_MX and stray == 0 and dg_err < TOL_MX
+    assert fro < TOL_MX and worst < TOL_MX_ROW and stray == 0 and dg_err < TOL_MX
     e_min = int(np.argmin(np.where(s.counts > 0, s.counts, np.iinfo(np.int64).max)))
     tok_e = np.flatnonzero((ids == cfg.e0 + e_min).any(axis=1))
     ids_e = np.where(ids[tok_e] == cfg.e0 + e_min, ids[tok_e], -1)

@@ -447,11 +447,28 @@ def test_two_waves_rule_reproduces_printed_floor():
     assert layer_two_wave_min_rows(256, 32, 2048) == 2 * 224 * 256 * 256 / 4096
 
 
+def test_bf16_round_matches_torch():
+    """bf16_round equals torch's float32 -> bfloat16 conversion (round to nearest, ties to
+    even) on random values over many binades, on exact ties in both directions, and on
+    values whose rounding carries into the exponent."""
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(4096) * np.ldexp(1.0, rng.integers(-60, 60, 4096))).astype(np.float32)
+    bits = rng.integers(0, 1 << 16, 512).astype(np.uint32)
+    ties = ((bits << 16) | 0x8000).view(np.float32)                 # halfway, both parities
+    carry = ((bits << 16) | 0xFFFF).view(np.float32)                # rounds up into the next binade
+    for w in (v, ties[np.isfinite(ties)], carry[np.isfinite(carry)], np.float32([0.0, -0.0, 1.0])):
+        ref = torch.from_numpy(w).to(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(O.bf16_round(w), ref)
+    # an exact tie with an even kept bit stays, with an odd one rounds away
+    assert O.bf16_round(np.float32([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert O.bf16_round(np.float32([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
 def _torch_mx_backward(dy, x, ids, gates, wg, wu, wd, e0, transposed=()):
     """The MXFP8 backward as per-expert masked torch products (no schedule), written apart
-    from the oracle: a, b from the MX forward's operands; u from dY rows and W_down^T
-    round-tripped along D; dx rows from da, db (float32) and W_gate^T, W_up^T round-tripped
-    along I; dG and the weight gradients from the unquantised values.  `transposed` names
+    from the oracle: a, b from the MX forward's operands, saved as bfloat16; u from dY rows and W_down^T
+    round-tripped along D; dx rows from da, db (rounded to float32, then bfloat16) and
+    W_gate^T, W_up^T round-tripped along I; dG and the weight gradients from the unquantised values.  `transposed` names
     quantisation points ("dy", "wdt", "dab", "wgut") taken along the other axis instead."""
     def q(v, name):
         if name not in transposed:
@@ -474,8 +491,8 @@ def _torch_mx_backward(dy, x, ids, gates, wg, wu, wd, e0, transposed=()):
             continue
         Wg, Wu, Wd = (torch.tensor(w[e], dtype=torch.float64) for w in (wg, wu, wd))
         Xq = _torch_mx_roundtrip(X[tok])
-        a = F.linear(Xq, _torch_mx_roundtrip(Wg))
-        b = F.linear(Xq, _torch_mx_roundtrip(Wu))
+        a = F.linear(Xq, _torch_mx_roundtrip(Wg)).to(torch.float32).to(torch.bfloat16).double()
+        b = F.linear(Xq, _torch_mx_roundtrip(Wu)).to(torch.float32).to(torch.bfloat16).double()
         h = F.silu(a) * b
         u = F.linear(q(DY[tok], "dy"), q(Wd.T, "wdt"))          # [n, I]
         g = G[tok, slot][:, None]
@@ -486,8 +503,8 @@ def _torch_mx_backward(dy, x, ids, gates, wg, wu, wd, e0, transposed=()):
         dWd[e] = (g * DY[tok]).T @ h
         dWg[e] = da.T @ X[tok]
         dWu[e] = db.T @ X[tok]
-        daq = q(da.to(torch.float32).to(torch.float64), "dab")
-        dbq = q(db.to(torch.float32).to(torch.float64), "dab")
+        daq = q(da.to(torch.float32).to(torch.bfloat16).to(torch.float64), "dab")
+        dbq = q(db.to(torch.float32).to(torch.bfloat16).to(torch.float64), "dab")
         dx = F.linear(daq, q(Wg.T, "wgut")) + F.linear(dbq, q(Wu.T, "wgut"))
         dX = dX.index_add(0, tok, dx)
     return dict(dx=dX.numpy(), dg=dG.numpy(), dwg=dWg.numpy(), dwu=dWu.numpy(), dwd=dWd.numpy())
