@@ -7,9 +7,12 @@
 //
 // The 256 B rows come from two matrices (B0, B1) so the same tile serves
 //   GEMM1: W_gate and W_up rows of the same 128 intermediate columns, paired per MFMA
-//          block (16 gate rows then the same 16 up rows), so the SwiGLU epilogue pairs
-//          each gate value with the up value one lane swap (l ^ 16) away;
+//          block (16 gate rows then the same 16 up rows), so that in a transposed tile
+//          (TR: the MFMA computes C^T, one row of C per lane) every lane holds each of
+//          its gate values and the matching up value;
 //   GEMM2: B0, B1 = two consecutive 128-row blocks of W_down.
+// The epilogues take transposed tiles: a lane's sixteen values of a block are then
+// columns of one row in groups of four, which the epilogues stage as 8-byte LDS writes.
 //
 // Data movement per K step of 64 (128 bytes per row, whole cache lines): 64 KB of A and
 // B move from global memory straight into LDS with gfx950's direct-to-LDS loads
@@ -231,11 +234,21 @@ __device__ __forceinline__ void frag_load(TileFrag& f, const FragAddr& fa, int k
     f.b[j] = *reinterpret_cast<lds_cv4u*>(uintptr_t(fa.b[ks] + S * kStageBytes + j * 32 * 128));
 }
 
+// One MFMA block: C += A B^T, or with TR its transpose C^T += B A^T (the B fragment
+// takes the MFMA's A slot).  Transposed, lane l of block (i, j) holds tile row
+// 32 i + l % 32 (+ 128 wm) at B rows brow_of(j, wn) + 8 (v / 4) + 4 (l / 32) + v % 4:
+// sixteen columns of one row, in groups of four consecutive ones.
+template <bool TR>
+__device__ __forceinline__ f32x16_t mma_blk(v4u a, v4u b, f32x16_t c) {
+  return TR ? mfma32x32x16(b, a, c) : mfma32x32x16(a, b, c);
+}
+
+template <bool TR = false>
 __device__ __forceinline__ void frag_mma(const TileFrag& f, TileAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc.c[i][j] = mfma32x32x16(f.a[i], f.b[j], acc.c[i][j]);
+    for (int j = 0; j < 2; ++j) acc.c[i][j] = mma_blk<TR>(f.a[i], f.b[j], acc.c[i][j]);
 }
 
 // 8 KB of LDS that takes the loads a step issues past the last step (one 1 KB block
@@ -272,21 +285,21 @@ __device__ __forceinline__ void tile_issue_sel(const TileSrc& s, int k0, int q, 
 // without a branch around the MFMAs (with one, the compiler spills), so the loads are
 // always issued; past the last step they go to g_lds_dummy through an empty resource
 // (no memory read).
-template <bool COH, int S>
+template <bool COH, int S, bool TR>
 __device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa, int kb, int nk,
                                           TileFrag& f0, TileFrag& f1, TileAcc& acc) {
   constexpr int SN = S ^ 1;
   frag_load<S>(f1, fa, 1);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f0, acc);
+  frag_mma<TR>(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   frag_load<S>(f0, fa, 2);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f1, acc);
+  frag_mma<TR>(f1, acc);
   __builtin_amdgcn_sched_barrier(0);
   frag_load<S>(f1, fa, 3);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f0, acc);
+  frag_mma<TR>(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if (kb + 1 < nk) {
     wait_loads_and_lds();
@@ -302,15 +315,15 @@ __device__ __forceinline__ void tile_step(const TileSrc& src, const FragAddr& fa
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int i = q >> 1, j = q & 1;
-    acc.c[i][j] = mfma32x32x16(f1.a[i], f1.b[j], acc.c[i][j]);
+    acc.c[i][j] = mma_blk<TR>(f1.a[i], f1.b[j], acc.c[i][j]);
     tile_issue_sel<COH, S>(src, kn, q, past);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Full K loop (K a multiple of kBK).  Ends with a barrier, so the stages may be
-// reused as soon as it returns.
-template <bool COH>
+// Full K loop (K a multiple of kBK); with TR the accumulators hold C^T (see mma_blk).
+// Ends with a barrier, so the stages may be reused as soon as it returns.
+template <bool COH, bool TR = false>
 __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -335,8 +348,8 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, int K, TileAcc& ac
   TileFrag f0, f1;
   frag_load<0>(f0, fa, 0);
   for (int kb = 0; kb < nk; kb += 2) {
-    tile_step<COH, 0>(src, fa, kb, nk, f0, f1, acc);
-    if (kb + 1 < nk) tile_step<COH, 1>(src, fa, kb + 1, nk, f0, f1, acc);
+    tile_step<COH, 0, TR>(src, fa, kb, nk, f0, f1, acc);
+    if (kb + 1 < nk) tile_step<COH, 1, TR>(src, fa, kb + 1, nk, f0, f1, acc);
   }
   wait_vmcnt<0>();  // the loads issued past the last step
   __builtin_amdgcn_s_barrier();
@@ -605,21 +618,21 @@ __device__ __forceinline__ void km_issue_one(const KmOp& o, int k0, int p, v4u* 
 // each non-gathered operand go out one per MFMA of the last slice (past the last step
 // into g_lds_dummy, so the MFMAs sit in no branch); a gathered operand's loads, which
 // read their offsets from the LDS row table, go out in one group before them.
-template <int AK, int BK, int S>
+template <int AK, int BK, int S, bool TR>
 __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, int kb, int nk,
                                         TileFrag& f0, TileFrag& f1, TileAcc& acc) {
   constexpr int SN = S ^ 1;
   km_frag_load<AK, S>(f1, fa, 1);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f0, acc);
+  frag_mma<TR>(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   km_frag_load<AK, S>(f0, fa, 2);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f1, acc);
+  frag_mma<TR>(f1, acc);
   __builtin_amdgcn_sched_barrier(0);
   km_frag_load<AK, S>(f1, fa, 3);
   __builtin_amdgcn_sched_barrier(0);
-  frag_mma(f0, acc);
+  frag_mma<TR>(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if (kb + 1 < nk) {
     wait_loads_and_lds();
@@ -638,7 +651,7 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int i = q >> 1, j = q & 1;
-    acc.c[i][j] = mfma32x32x16(f1.a[i], f1.b[j], acc.c[i][j]);
+    acc.c[i][j] = mma_blk<TR>(f1.a[i], f1.b[j], acc.c[i][j]);
     if (q < 4) {
       if (AK != kKG) km_issue_one<AK == kKG ? kKC : AK, S>(a, kn, q, g_lds_a, past);
     } else {
@@ -651,8 +664,9 @@ __device__ __forceinline__ void km_step(KmOp& a, KmOp& b, const KmFragAddr& fa, 
 // K loop of nk steps over operands a (kind AK: kKC, kKCD, kKR or kKG) and b (kind BK: kKW,
 // kKR or kKG; at most one kKG operand: they share the LDS offset table).
 // C = A B^T as for tile_gemm, with A's tile row m / B's tile row n read as column m / n
-// of a K-major operand.  Ends with a barrier.
-template <int AK, int BK>
+// of a K-major operand; with TR the accumulators hold C^T (see mma_blk).  Ends with a
+// barrier.
+template <int AK, int BK, bool TR = false>
 __device__ __forceinline__ void tile_gemm_km(KmOp& a, KmOp& b, int nk, TileAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -676,8 +690,8 @@ __device__ __forceinline__ void tile_gemm_km(KmOp& a, KmOp& b, int nk, TileAcc& 
   TileFrag f0, f1;
   km_frag_load<AK, 0>(f0, fa, 0);
   for (int kb = 0; kb < nk; kb += 2) {
-    km_step<AK, BK, 0>(a, b, fa, kb, nk, f0, f1, acc);
-    if (kb + 1 < nk) km_step<AK, BK, 1>(a, b, fa, kb + 1, nk, f0, f1, acc);
+    km_step<AK, BK, 0, TR>(a, b, fa, kb, nk, f0, f1, acc);
+    if (kb + 1 < nk) km_step<AK, BK, 1, TR>(a, b, fa, kb + 1, nk, f0, f1, acc);
   }
   wait_vmcnt<0>();  // the loads issued past the last step
   __builtin_amdgcn_s_barrier();

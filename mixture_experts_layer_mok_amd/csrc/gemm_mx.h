@@ -214,13 +214,17 @@ __device__ __forceinline__ void mx_scales_read(MxScales& sc) {
   for (int j = 0; j < 2; ++j) sc.b[j] = g_lds_sb[S * 256 + wn * 64 + j * 32 + r32] >> sh;
 }
 
-template <int SL>
+// With TR the B fragment (and its scales) takes the MFMA's A slot: the block holds C^T,
+// as for the bf16 tile (mma_blk).
+template <int SL, bool TR>
 __device__ __forceinline__ void mx_mma_row(const i32x8_t& a, const i32x8_t (&b)[2], uint32_t sa,
                                            const MxScales& sc, f32x16_t (&c)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], c[j], 0, 0, 2 * SL, int(sa),
-                                                            2 * SL, int(sc.b[j]));
+    c[j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a, c[j], 0, 0, 2 * SL,
+                                                                 int(sc.b[j]), 2 * SL, int(sa))
+              : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], c[j], 0, 0, 2 * SL,
+                                                                 int(sa), 2 * SL, int(sc.b[j]));
 }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0): every load of this wave, global and LDS, has landed.
@@ -234,7 +238,7 @@ __device__ __forceinline__ void wait_all_loads() {
 // MFMAs of row block i have issued, a[i] is refilled with the next slice's block i, so
 // only the B fragments are double-buffered; the scales are replaced after the last MFMA
 // that reads them.  The body has no branches, so the compiler keeps its order.
-template <bool COH, int S>
+template <bool COH, int S, bool TR>
 __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, int ks, int nk,
                                         i32x8_t (&a)[4], i32x8_t (&b)[2], MxScales& sc,
                                         TileAcc& acc) {
@@ -246,7 +250,7 @@ __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    mx_mma_row<0>(a[i], b, sc.a[i], sc, acc.c[i]);
+    mx_mma_row<0, TR>(a[i], b, sc.a[i], sc, acc.c[i]);
     __builtin_amdgcn_sched_barrier(0);
     a[i] = mx_read_a<S>(fa, 1, i);
   }
@@ -275,7 +279,7 @@ __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    mx_mma_row<1>(a[i], b, s1.a[i], s1, acc.c[i]);
+    mx_mma_row<1, TR>(a[i], b, s1.a[i], s1, acc.c[i]);
     mx_issue_part<COH, S>(src, ks + 2, nk, nvalid, nhalf, 2 * i);
     mx_issue_part<COH, S>(src, ks + 2, nk, nvalid, nhalf, 2 * i + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -287,9 +291,10 @@ __device__ __forceinline__ void mx_step(const MxSrc& src, const MxFragAddr& fa, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Full K loop; K (elements = bytes) a multiple of 64.  Ends with a barrier after all of
-// its loads have landed, so the stages may be reused as soon as it returns.
-template <bool COH>
+// Full K loop; K (elements = bytes) a multiple of 64; with TR the accumulators hold C^T.
+// Ends with a barrier after all of its loads have landed, so the stages may be reused as
+// soon as it returns.
+template <bool COH, bool TR = false>
 __device__ __forceinline__ void mx_gemm(const MxSrc& src, int K, TileAcc& acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -315,8 +320,8 @@ __device__ __forceinline__ void mx_gemm(const MxSrc& src, int K, TileAcc& acc) {
   b[0] = mx_read_b<0>(fa, 0, 0);
   b[1] = mx_read_b<0>(fa, 0, 1);
   for (int ks = 0; ks < nk; ks += 2) {
-    mx_step<COH, 0>(src, fa, ks, nk, a, b, sc, acc);
-    if (ks + 1 < nk) mx_step<COH, 1>(src, fa, ks + 1, nk, a, b, sc, acc);
+    mx_step<COH, 0, TR>(src, fa, ks, nk, a, b, sc, acc);
+    if (ks + 1 < nk) mx_step<COH, 1, TR>(src, fa, ks + 1, nk, a, b, sc, acc);
   }
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(512) void k_bwd_gemm1(BwdParams p) {
     TileSrc src;
     tile_src_init_gather(src, geom::kPaired, p.a.x, p.D, p.P.perm + e.x, p.k, e.y,
                          p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.D, nt * kBN1, nt * kBN1, p.I);
-    tile_gemm<false>(src, p.D, acc);
+    tile_gemm<false, true>(src, p.D, acc);
     epi_swiglu<false>(acc, e.y, nt * kBN1, p.I, nullptr, p.I, p.P.bab + int64_t(e.x) * 2 * p.I);
   }
 }
@@ -221,12 +221,12 @@ __device__ __forceinline__ uint32_t dx_tile(const BwdParams& p, int g, int nt) {
     MxSrc src;
     mx_src_init(src, geom::kSplit, p.P.dabq + int64_t(e.x) * K, p.P.dabqs + int64_t(e.x) * p.abq_ld,
                 K, p.abq_ld, e.y, B, Bs, B, Bs, K, p.abq_ld, n0, n0 + 128, p.D, int(K));
-    mx_gemm<true>(src, int(K), acc);
+    mx_gemm<true, true>(src, int(K), acc);
   } else {
     KmOp a, b;
     km_init_kc(a, p.P.bdab + int64_t(e.x) * K, K, e.y);
     km_init_weights(b, p.a.wg + e.z * wsz, p.a.wu + e.z * wsz, p.I, p.D, n0, p.D);
-    tile_gemm_km<kKCD, kKW>(a, b, int(K / kBK), acc);
+    tile_gemm_km<kKCD, kKW, true>(a, b, int(K / kBK), acc);
   }
   const uint32_t t_k = uint32_t(wall_clock64());
   epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf, int64_t(p.T) * p.k);

@@ -169,48 +169,59 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
 // ------------------------------------------------------------------------------------
 // GEMM tiles
 // ------------------------------------------------------------------------------------
-// The gate/up pre-activations of a GEMM1 tile (paired layout, as in epi_swiglu) stored
-// as bf16 rows [rows, 2I] at AB: gate in [0, I), up in [I, 2I).  Staged in LDS as rows of
-// 256 columns (tile rows 0..127 in the A stages, 128..255 in the B stages), then written
-// as whole row segments, 16 bytes a lane.  Ends with a barrier.
+// The gate/up pre-activations of a transposed GEMM1 tile (tile_gemm with TR, paired
+// layout; see epi_swiglu) stored as bf16 rows [rows, 2I] at AB: gate in [0, I), up in
+// [I, 2I).  Staged in LDS as rows of 256 columns (tile rows 0..127 in the A stages,
+// 128..255 in the B stages; 16-byte chunk c of row r at c ^ (r % 32)), one 8-byte write
+// per group of four columns, then written as whole row segments, 16 bytes a lane.  Ends
+// with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n0, int I,
-                                             uint16_t* AB) {
+                                               uint16_t* AB) {
   constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
   constexpr int W = kThreads / 64;
+  typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wn = w & 3;
+  const int wm = w >> 2, wn = w & 3;
+  const int hs = lane >> 5, l32 = lane & 31;
   const int wr = __builtin_amdgcn_readfirstlane(w);
-  const bool gate_lane = (lane & 16) == 0;
-  const int rbit = lane >> 5;  // bit 2 of every row this lane holds
-  lds_u16_t* st = stage16(w >> 2);
+  lds_u64_t* st = reinterpret_cast<lds_u64_t*>(stage16(wm));
   auto stage_row = [](int r) { return stage16(r >> 7); };
+  auto pack4 = [](float a, float b, float c, float d) {
+    return uint64_t(pack_bf16x2(a, b)) | (uint64_t(pack_bf16x2(c, d)) << 32);
+  };
   {
-    // rows of 256 columns: gate 0..127, up 128..255
-    const int sw = ((gate_lane ? 0 : 2) | rbit) << 4;
+    // rows of 256 columns: gate chunks 0..15, up chunks 16..31
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 32 * i + l32;  // row within the wave's half; rr % 32 = l32
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int c = (16 * (2 * wn + j) + (lane & 15) + (gate_lane ? 0 : 128)) ^ sw;
+        if (n0 + 16 * (2 * wn + j) >= I) continue;  // wave-uniform: never stored
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          st[(acc_row(tid, i, v) & 127) * 256 + c] = f32_to_bf16(acc.c[i][j][v]);
+        for (int g = 0; g < 2; ++g) {
+          const f32x16_t& c = acc.c[i][j];
+          const int ch = 2 * (2 * wn + j) + g;
+          st[rr * 64 + (ch ^ l32) * 2 + hs] = pack4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+          st[rr * 64 + ((ch + 16) ^ l32) * 2 + hs] =
+              pack4(c[8 + 4 * g], c[9 + 4 * g], c[10 + 4 * g], c[11 + 4 * g]);
+        }
       }
+    }
     __syncthreads();
     // wave w: row pairs 2w, 2w + 1, 2w + 16, ..: lanes 0..31 write one row, 32..63 the
     // next; in each half-wave 16 lanes write the gate segment and 16 the up segment
     constexpr int kPairs = 128 / W;
     const int rs = lane >> 5, seg = (lane >> 4) & 1, l16 = lane & 15;
-    const bool col16_ok = n0 + 8 * l16 < I;  // I % 64 == 0: an 8-column group is all in or out
+    const bool col16_ok = n0 + 8 * l16 < I;  // I % 16 == 0: an 8-column group is all in or out
     v4u val[kPairs];
 #pragma unroll
     for (int k = 0; k < kPairs; ++k) {
       const int r = 2 * (wr + W * k) + rs;
-      const int c = (8 * l16 + 128 * seg) ^ (((seg << 1) | ((r >> 2) & 1)) << 4);
-      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 256 + c);
+      const int ch = (l16 + 16 * seg) ^ (r & 31);
+      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 256 + 8 * ch);
     }
     const rsrc_t rab = row_rsrc(AB, uint32_t(rows) * uint32_t(2 * I) * 2u);
     const uint32_t coff = uint32_t((seg ? I : 0) + n0 + 8 * l16) * 2u;
@@ -224,59 +235,57 @@ __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n
   }
 }
 
-// Epilogue of GEMM1 (SwiGLU): the tile covered rows [0, rows) (rows <= 256) and
-// intermediate columns [n0, n0 + 128) of W_gate and W_up in the paired layout: in MFMA
-// block j of wave column wn (B rows brow_of(j, wn)), lanes with (l & 16) == 0 hold gate
-// column n0 + 16 * (brow_of(j, wn) / 32) + (l & 15) and lane l ^ 16 holds its up value.
-// Writes H (when H != null) and, when AB != null, the gate/up pre-activations as
-// [rows, 2I]: gate in [0, I), up in [I, 2I).  h is formed from the fp32 accumulators.
-// Each output is staged in LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255
-// in the B stages) and then written as whole row segments, 16 bytes a lane.  Staged
-// columns are XOR-swizzled in 16-column groups by (up half, bit 2 of the row), so that
-// the four lane groups of an MFMA block that write at once hit different banks.  With
-// kCoherent both are written at device scope: in the fused kernel a ring slot is
-// rewritten by workgroups on other XCDs within one launch, and a plain store would leave
-// a dirty line in one XCD's L2 that could be written back after a newer one from another
-// XCD.  Ends with a barrier.
+// Epilogue of GEMM1 (SwiGLU) on a transposed tile (tile_gemm with TR, paired layout).
+// Lane l of MFMA block (i, j) of wave (wm, wn) holds tile row 128 wm + 32 i + l % 32;
+// its values v < 8 are the gate pre-activations of intermediate columns
+// n0 + 16 (2 wn + j) + 8 (v / 4) + 4 (l / 32) + v % 4 and v + 8 the up ones of the same
+// columns.  So each lane forms h for two groups of four consecutive columns of its row
+// with no data exchange, and stages each group as one 8-byte LDS write (lanes l and
+// l + 32 fill one 16-byte chunk).  Writes H [rows, ldh] at column n0.. (when H != null)
+// and, when AB != null, the gate/up pre-activations as [rows, 2I]: gate in [0, I), up in
+// [I, 2I); h is formed from the fp32 accumulators.  Each output is staged as bf16 rows
+// (tile rows 0..127 in the A stages, 128..255 in the B stages; 16-byte chunk c of row r
+// at c ^ (r % 32) for rows of 256 columns, c ^ (r % 16) for rows of 128, so that the 32
+// rows of a write and the chunks of a row read hit different banks) and then written as
+// whole row segments, 16 bytes a lane.  With kCoherent the stores are device scope: in
+// the fused kernel a ring slot is rewritten by workgroups on other XCDs within one
+// launch.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0, int I,
-                                           uint16_t* H, int64_t ldh, uint16_t* AB) {
+                                             uint16_t* H, int64_t ldh, uint16_t* AB) {
   constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
   constexpr int W = kThreads / 64;
+  typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wn = w & 3;
+  const int wm = w >> 2, wn = w & 3;
+  const int hs = lane >> 5, l32 = lane & 31;
   const int wr = __builtin_amdgcn_readfirstlane(w);
-  const bool gate_lane = (lane & 16) == 0;
-  const int rbit = lane >> 5;  // bit 2 of every row this lane holds
-  lds_u16_t* st = stage16(w >> 2);
+  lds_u64_t* st = reinterpret_cast<lds_u64_t*>(stage16(wm));
   auto stage_row = [](int r) { return stage16(r >> 7); };
+  auto pack4 = [](float a, float b, float c, float d) {
+    return uint64_t(pack_bf16x2(a, b)) | (uint64_t(pack_bf16x2(c, d)) << 32);
+  };
   if (AB) epi_store_ab<kCoherent>(acc, rows, n0, I, AB);
   if (H) {
-    // rows of 128 columns.  A gate lane and its up lane (l ^ 16) split the 16 rows of
-    // their column: one gfx950 v_permlane16_swap per row pair hands the up lane's value
-    // of row v to the gate lane and the gate lane's value of row v + 8 to the up lane,
-    // so that every lane forms 8 of the h values (rows v and v + 8 lie 16 tile rows
-    // apart).  Staged columns are XOR-swizzled by 16 on bit 2 of the row and by 8 on
-    // bit 4, so the two lanes of a pair and the two half-waves hit different banks.
-    const int cl = 16 * (2 * wn) + (lane & 15);
+    // rows of 128 columns
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 32 * i + l32;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if (n0 + 16 * (2 * wn + j) >= I) continue;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float xa = acc.c[i][j][v], xb = acc.c[i][j][v + 8];
-          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xa),
-                                                           __float_as_uint(xb), false, false);
-          const float g = gate_lane ? xa : __uint_as_float(sw[0]);
-          const float u = gate_lane ? __uint_as_float(sw[1]) : xb;
-          const int r = acc_row(tid, i, v) + (gate_lane ? 0 : 16);
-          const int c = (cl + 16 * j) ^ (rbit << 4) ^ (((r >> 4) & 1) << 3);
-          st[(r & 127) * 128 + c] = f32_to_bf16(silu_f(g) * u);
+        for (int g = 0; g < 2; ++g) {
+          const f32x16_t& c = acc.c[i][j];
+          const int ch = 2 * (2 * wn + j) + g;
+          st[rr * 32 + (ch ^ (l32 & 15)) * 2 + hs] =
+              pack4(silu_f(c[4 * g]) * c[8 + 4 * g], silu_f(c[4 * g + 1]) * c[9 + 4 * g],
+                    silu_f(c[4 * g + 2]) * c[10 + 4 * g], silu_f(c[4 * g + 3]) * c[11 + 4 * g]);
         }
       }
+    }
     __syncthreads();
     // wave w: row quads w, w + 8, ..; a 256-byte segment is 16 lanes: four rows a store
     constexpr int kQuads = 64 / W;
@@ -286,8 +295,7 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
 #pragma unroll
     for (int k = 0; k < kQuads; ++k) {
       const int r = 4 * (wr + W * k) + rq;
-      const int c = (8 * l16) ^ (((r >> 2) & 1) << 4) ^ (((r >> 4) & 1) << 3);
-      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 128 + c);
+      val[k] = *reinterpret_cast<lds_cv4u*>(stage_row(r) + (r & 127) * 128 + 8 * (l16 ^ (r & 15)));
     }
     const rsrc_t rh = row_rsrc(H, uint32_t(rows) * uint32_t(ldh) * 2u);
     const uint32_t coff = uint32_t(n0 + 8 * l16) * 2u;
@@ -301,15 +309,18 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
   }
 }
 
-// Epilogue of GEMM2 and of dX: rows [0, rows), columns [n0, n0 + 256) of D (B tile row b
-// is column n0 + b in the split layout); row r's result goes to obuf row perm_rows[r]
-// (its pair index t*k + j; obuf holds obuf_rows rows of D).  The tile is first staged in
-// LDS as bf16 rows (tile rows 0..127 in the A stages, 128..255 in the B stages; free once
-// the K loop has ended), so that each wave then writes whole 512-byte row segments, 16
-// bytes a lane when every byte offset of obuf fits in 32 bits (two rows a store through
-// one resource), else 8 bytes a lane through a resource per row.  A row's staged columns are XOR-swizzled by 32 on bit 2 of the row: the
-// two half-waves of an MFMA block write rows 4 apart, which would otherwise share
-// banks.  With kCoherent the row stores are device scope.  Ends with a barrier.
+// Epilogue of GEMM2 and of dX on a transposed tile (tile_gemm, tile_gemm_km or mx_gemm
+// with TR): rows [0, rows), columns [n0, n0 + 256) of D (B tile row b is column n0 + b in
+// the split layout); row r's result goes to obuf row perm_rows[r] (its pair index t*k + j;
+// obuf holds obuf_rows rows of D).  Lane l of block (i, j) holds row 128 wm + 32 i + l % 32
+// at columns brow_of(j, wn) + 8 (v / 4) + 4 (l / 32) + v % 4, so each group of four
+// columns is staged in LDS with one 8-byte write, lanes l and l + 32 filling one 16-byte
+// chunk (tile rows 0..127 in the A stages, 128..255 in the B stages, free once the K loop
+// has ended; chunk c of row r at c ^ (r % 32), so the 32 rows of a write and the chunks
+// of a row read hit different banks).  Each wave then writes whole 512-byte row segments,
+// 16 bytes a lane when every byte offset of obuf fits in 32 bits (two rows a store
+// through one resource), else 8 bytes a lane through a resource per row.  With kCoherent
+// the row stores are device scope.  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
                                             const int32_t* perm_rows, uint16_t* obuf,
@@ -319,19 +330,23 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
   const int w = tid >> 6;
   const int wn = w & 3;
   {
-    lds_u16_t* st = stage16(w >> 2);
-    const int swz = (lane >> 5) << 5;  // bit 2 of every row this lane holds
+    typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
+    lds_u64_t* st = reinterpret_cast<lds_u64_t*>(stage16(w >> 2));
+    const int l32 = lane & 31, hs = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 32 * i + l32;  // row within the wave's half; rr % 32 = l32
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int b = (brow_of(j, wn) + (lane & 31)) ^ swz;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rl = acc_row(tid, i, v) & 127;
-          st[rl * 256 + b] = f32_to_bf16(acc.c[i][j][v]);
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& c = acc.c[i][j];
+          const int ch = 8 * wn + 4 * j + g;
+          st[rr * 64 + (ch ^ l32) * 2 + hs] =
+              uint64_t(pack_bf16x2(c[4 * g], c[4 * g + 1])) |
+              (uint64_t(pack_bf16x2(c[4 * g + 2], c[4 * g + 3])) << 32);
         }
-      }
+    }
   }
   __syncthreads();
   // wave w writes tile rows w, w + 8, ..: their destinations are loaded one per lane
@@ -351,7 +366,7 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
     for (int k = 0; k < kRowsPerWave / 2; ++k) {
       const int r = wr + (kThreads / 64) * (2 * k + h);
       val[k] = *reinterpret_cast<__attribute__((address_space(3))) const v4u*>(
-          stage16(r >> 7) + (r & 127) * 256 + ((8 * l32) ^ (((r >> 2) & 1) << 5)));
+          stage16(r >> 7) + (r & 127) * 256 + 8 * (l32 ^ (r & 31)));
     }
     const rsrc_t rb = row_rsrc(obuf, uint32_t(obuf_rows * int64_t(D) * 2));
 #pragma unroll
@@ -371,9 +386,8 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
     const int r = wr + (kThreads / 64) * k;
-    val[k] = *reinterpret_cast<lds_cu64_t*>(
-        stage16(r >> 7) + (r & 127) * 256 +
-        ((4 * lane) ^ (((r >> 2) & 1) << 5)));
+    val[k] = *reinterpret_cast<lds_cu64_t*>(stage16(r >> 7) + (r & 127) * 256 +
+                                            8 * ((lane >> 1) ^ (r & 31)) + 4 * (lane & 1));
   }
   const uint32_t row_bytes = uint32_t(D) * 2u;
   const uint32_t off = uint32_t(n0 + 4 * lane) * 2u;  // columns past D are dropped
@@ -387,58 +401,59 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
   __syncthreads();
 }
 
-// Epilogue of the MXFP8 GEMM1: SwiGLU as in epi_swiglu, then H is MX-quantised along I.
-// A 32-column MX block [n0 + 32 wn, +32) is exactly MFMA blocks j = 0, 1 of wave column
-// wn.  As in epi_swiglu, a gate lane and its up lane (l ^ 16) split the rows of their
-// column with one v_permlane16_swap per row pair and value block, so each 16-lane DPP
-// row then holds the 32 h values of one tile row's MX block (two per lane): the block
-// maximum is a 16-lane DPP reduction.  The codes and scales are staged in LDS (codes of
-// row r at byte r * 128, XOR-swizzled by 32 on bit 2 and by 64 on bit 4 of the row so
-// the four lane groups of a write hit different banks; scales after them), then written
-// as 128-byte row segments, 4 bytes a lane, and one byte per row and block.  Writes codes
-// Hc[row * ldh + col] and scales Hs[row * hs_ld + col / 32]; I is a multiple of 32, so a
-// block is wholly inside or outside [0, I).  With AB, the gate/up pre-activations are
-// stored first, as bf16 rows (epi_store_ab).  Ends with a barrier.
+// Epilogue of the MXFP8 GEMM1 on a transposed tile (mx_gemm with TR, paired layout; the
+// lanes' values as in epi_swiglu): SwiGLU, then H MX-quantised along I.  A 32-column MX
+// block [n0 + 32 wn, +32) of tile row r is MFMA blocks j = 0, 1 of wave column wn: lane l
+// holds 16 of its h values (columns 16 j + 8 g + 4 (l / 32) + 0..3 of the block) and lane
+// l ^ 32 the other 16, so the block maximum is the lane's own maximum and one exchange.
+// The codes are staged in LDS (row r at byte r * 128; its 4-byte chunk c at
+// c ^ 2 ((r / 2) % 16), so the 32 rows of a write hit different banks; scales after
+// them), then written as 128-byte row segments, 4 bytes a lane, and one byte per row and
+// block.  Writes codes Hc[row * ldh + col] and scales Hs[row * hs_ld + col / 32]; I is a
+// multiple of 32, so a block is wholly inside or outside [0, I).  With AB, the gate/up
+// pre-activations are stored first, as bf16 rows (epi_store_ab).  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int n0, int I,
-                                              uint8_t* Hc, int64_t ldh, uint8_t* Hs,
-                                              int64_t hs_ld, uint16_t* AB = nullptr) {
+                                                uint8_t* Hc, int64_t ldh, uint8_t* Hs,
+                                                int64_t hs_ld, uint16_t* AB = nullptr) {
   if (AB) epi_store_ab<kCoherent>(acc, rows, n0, I, AB);  // bf16 a, b for the backward
   constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
   constexpr int W = kThreads / 64;
   typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-  typedef __attribute__((address_space(3))) const uint32_t lds_cu32_t;
+  typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wn = w & 3;
-  const bool gate_lane = (lane & 16) == 0;
-  lds_u8_t* sc = reinterpret_cast<lds_u8_t*>(uintptr_t(lds_addr(g_lds_a)));  // [256][128]
-  lds_u8_t* ss = sc + 256 * 128;                                              // [256][4]
-  auto swz = [](int r) { return (((r >> 2) & 1) << 5) | (((r >> 4) & 1) << 6); };
+  const int wm = w >> 2, wn = w & 3;
+  const int hs = lane >> 5, l32 = lane & 31;
+  lds_u32_t* sc = reinterpret_cast<lds_u32_t*>(uintptr_t(lds_addr(g_lds_a)));  // [256][32]
+  lds_u8_t* ss = reinterpret_cast<lds_u8_t*>(uintptr_t(lds_addr(g_lds_a))) + 256 * 128;  // [256][4]
+  auto swz = [](int r) { return 2 * ((r >> 1) & 15); };
   if (n0 + 32 * wn < I) {  // wave-uniform
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int r = 128 * wm + 32 * i + l32;
+      float h[2][8];
+      float m = 0.f;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const auto s0 = __builtin_amdgcn_permlane16_swap(
-            __float_as_uint(acc.c[i][0][v]), __float_as_uint(acc.c[i][0][v + 8]), false, false);
-        const auto s1 = __builtin_amdgcn_permlane16_swap(
-            __float_as_uint(acc.c[i][1][v]), __float_as_uint(acc.c[i][1][v + 8]), false, false);
-        const float g0 = gate_lane ? acc.c[i][0][v] : __uint_as_float(s0[0]);
-        const float u0 = gate_lane ? __uint_as_float(s0[1]) : acc.c[i][0][v + 8];
-        const float g1 = gate_lane ? acc.c[i][1][v] : __uint_as_float(s1[0]);
-        const float u1 = gate_lane ? __uint_as_float(s1[1]) : acc.c[i][1][v + 8];
-        const float h0 = silu_f(g0) * u0, h1 = silu_f(g1) * u1;
-        const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
-        const int n = mx_shared_exp(amax);
-        const uint32_t cc = e4m3x2(ldexpf(h0, -n), ldexpf(h1, -n));
-        const int r = (acc_row(tid, i, v) + (gate_lane ? 0 : 16)) & 255;
-        const int c = (32 * wn + (lane & 15)) ^ swz(r);
-        sc[r * 128 + c] = uint8_t(cc);
-        sc[r * 128 + (c ^ 16)] = uint8_t(cc >> 8);
-        if ((lane & 15) == 0) ss[r * 4 + wn] = uint8_t(n + 127);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          h[j][v] = silu_f(acc.c[i][j][v]) * acc.c[i][j][v + 8];
+          m = fmaxf(m, fabsf(h[j][v]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const int n = mx_shared_exp(m);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint32_t code =
+              e4m3x2(ldexpf(h[j][4 * g], -n), ldexpf(h[j][4 * g + 1], -n)) |
+              (e4m3x2(ldexpf(h[j][4 * g + 2], -n), ldexpf(h[j][4 * g + 3], -n)) << 16);
+          sc[r * 32 + ((8 * wn + 4 * j + 2 * g + hs) ^ swz(r))] = code;
+        }
+      if (hs == 0) ss[r * 4 + wn] = uint8_t(n + 127);
       __builtin_amdgcn_sched_barrier(0);  // one block row at a time: few live registers
     }
   }
@@ -446,18 +461,16 @@ __device__ __forceinline__ void epi_swiglu_mx(const TileAcc& acc, int rows, int 
   // wave w: row pairs w, w + 8, ..; lanes 0..31 write row 2p, lanes 32..63 row 2p + 1
   // (one resource for the tile's rows: a buffer resource's base is wave-uniform, and the
   // two half-waves write different rows)
-  const int half = lane >> 5, l32 = lane & 31;
   const bool col_ok = n0 + 4 * l32 < I;  // I % 32 == 0: a 4-column group is all in or out
   const rsrc_t rh = row_rsrc(Hc, uint32_t(rows) * uint32_t(ldh));
   const int wr = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll 4
   for (int k = 0; k < 128 / W; ++k) {
-    const int r = 2 * (wr + W * k) + half;
+    const int r = 2 * (wr + W * k) + hs;
     if (2 * (wr + W * k) >= rows) break;  // wave-uniform; the odd row is checked below
-    if (r < rows && col_ok) {
-      const uint32_t val = *reinterpret_cast<lds_cu32_t*>(sc + r * 128 + ((4 * l32) ^ swz(r)));
-      buf_st4<kPol>(rh, uint32_t(r) * uint32_t(ldh) + uint32_t(n0 + 4 * l32), val);
-    }
+    if (r < rows && col_ok)
+      buf_st4<kPol>(rh, uint32_t(r) * uint32_t(ldh) + uint32_t(n0 + 4 * l32),
+                    sc[r * 32 + (l32 ^ swz(r))]);
   }
   if (tid < rows) {
 #pragma unroll
@@ -487,6 +500,7 @@ struct MxOperands {
   int64_t ws_ld;
 };
 
+// Both GEMMs' tiles come out transposed (epi_swiglu_mx, epi_scatter).
 template <bool kCoherent>
 __device__ __forceinline__ void run_tile_mx(bool gemm1, const MxOperands& o, int rows, int n0,
                                             int D, int I, TileAcc& acc) {
@@ -497,20 +511,25 @@ __device__ __forceinline__ void run_tile_mx(bool gemm1, const MxOperands& o, int
   else
     mx_src_init(src, geom::kSplit, o.A, o.As, I, o.as_ld, rows, o.w0, o.w0s, o.w0, o.w0s, I,
                 o.ws_ld, n0, n0 + 128, D, I);
-  mx_gemm<kCoherent>(src, gemm1 ? D : I, acc);
+  mx_gemm<kCoherent, true>(src, gemm1 ? D : I, acc);
 }
 
 // Operands of one tile of either GEMM (one K loop serves both).
 //   GEMM1: A = dispatched rows [rows, D], B = W_gate/W_up rows n0.., K = D.
 //   GEMM2: A = hidden rows [rows, I], B = W_down rows n0..n0+255, K = I.
+// Both GEMMs' tiles come out transposed (epi_swiglu, epi_scatter).
 template <bool kCoherent>
 __device__ __forceinline__ void run_tile(bool gemm1, const uint16_t* A, int rows,
                                          const uint16_t* w0, const uint16_t* w1, int n0, int D,
                                          int I, TileAcc& acc) {
   TileSrc src;
-  if (gemm1) tile_src_init(src, geom::kPaired, A, D, rows, w0, w1, D, n0, n0, I);
-  else tile_src_init(src, geom::kSplit, A, I, rows, w0, w0, I, n0, n0 + 128, D);
-  tile_gemm<kCoherent>(src, gemm1 ? D : I, acc);
+  if (gemm1) {
+    tile_src_init(src, geom::kPaired, A, D, rows, w0, w1, D, n0, n0, I);
+    tile_gemm<kCoherent, true>(src, D, acc);
+  } else {
+    tile_src_init(src, geom::kSplit, A, I, rows, w0, w0, I, n0, n0 + 128, D);
+    tile_gemm<kCoherent, true>(src, I, acc);
+  }
 }
 
 // Epilogue of the dH GEMM of the backward (SwiGLU backward and router-weight gradient
