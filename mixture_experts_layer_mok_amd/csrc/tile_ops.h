@@ -644,24 +644,43 @@ __device__ __forceinline__ void epi_dh(const TileAcc& acc, int rows, int row0, i
 }
 
 // Epilogue storing the fp32 tile: rows [0, rows) at C + row * ldc, columns n0 + b for
-// B tile row b (split layout) below N.
+// B tile row b (split layout) below N.  Untransposed (lane l of block (i, j) holds column
+// brow_of(j, wn) + l % 32 at rows acc_row), each store writes 128-byte row segments;
+// transposed (TR: lane l holds row 128 wm + 32 i + l % 32 at columns brow_of(j, wn) +
+// 8 (v / 4) + 4 (l / 32) + v % 4), four consecutive columns (16 bytes) a store, N and ldc
+// multiples of 4.
+template <bool TR>
 __device__ __forceinline__ void epi_store_f32(const TileAcc& acc, int rows, int n0, int N,
                                               float* C, int64_t ldc) {
   const int tid = opaque(threadIdx.x);
   const int lane = tid & 63;
-  const int wn = (tid >> 6) & 3;
+  const int w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      const f32x16_t& c = acc.c[i][j];
+      if (TR) {
+        const int row = 128 * wm + 32 * i + (lane & 31);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = acc_row(tid, i, v);
-        if (row < rows && col < N) C[int64_t(row) * ldc + col] = acc.c[i][j][v];
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + brow_of(j, wn) + 8 * g + 4 * (lane >> 5);
+          if (row < rows && col < N)
+            *reinterpret_cast<float4*>(C + int64_t(row) * ldc + col) =
+                make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+        }
+      } else {
+        const int col = n0 + brow_of(j, wn) + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = acc_row(tid, i, v);
+          if (row < rows && col < N) C[int64_t(row) * ldc + col] = c[v];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
 }
 
 }  // namespace mok
