@@ -651,6 +651,12 @@ static int fused_grid_size(const void* kernel) {
 
 mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hipStream_t st) {
   FwdParams p = make_params(L, P, a);
+  // the fused kernel's grid (device queries only), checked before anything is enqueued
+  const void* kern = L.mx ? reinterpret_cast<const void*>(k_fwd_fused<true>)
+                          : reinterpret_cast<const void*>(k_fwd_fused<false>);
+  const int grid = L.unfused ? 0 : fused_grid_size(kern);
+  if (!L.unfused && grid <= 0) return MOK_E_DEVICE;
+  if (!L.unfused && a.comm_cus >= grid) return MOK_E_SHAPE;
   if (L.repack_wg) {
     launch_mx_repack(a.sg, L.nl * L.I, int(L.D / 32), P.wsg, int(L.wgs_ld), st);
     launch_mx_repack(a.su, L.nl * L.I, int(L.D / 32), P.wsu, int(L.wgs_ld), st);
@@ -673,11 +679,6 @@ mok_status_t launch_forward(const Layout& L, const Ptrs& P, const FwdArgs& a, hi
     hipLaunchKernelGGL(k_combine_all, dim3(gc), dim3(256), 0, st, p);
     return hipGetLastError() == hipSuccess ? MOK_OK : MOK_E_LAUNCH;
   }
-  const void* kern = L.mx ? reinterpret_cast<const void*>(k_fwd_fused<true>)
-                          : reinterpret_cast<const void*>(k_fwd_fused<false>);
-  const int grid = fused_grid_size(kern);
-  if (grid <= 0) return MOK_E_DEVICE;
-  if (a.comm_cus >= grid) return MOK_E_SHAPE;
   hipLaunchKernelGGL(k_fwd_prep, dim3(64), dim3(256), 0, st, p);
   if (L.mx)
     hipLaunchKernelGGL(k_fwd_fused<true>, dim3(grid), dim3(kThreads), 0, st, p);

@@ -111,6 +111,27 @@ def test_forward_mx_small_parity(cfg):
     assert err < TOL_MX
 
 
+def test_forward_mx_comm_cus_too_large_enqueues_nothing():
+    """comm_cus at or above the persistent kernel's grid (one workgroup per CU) is refused
+    with MOK_E_SHAPE before anything is enqueued: with D % 128 == 64 the forward would first
+    repack the weight scales into the workspace, and the workspace stays untouched."""
+    cfg = gen.small_config("mxcomm", T=64, D=192, I=128, E=4, k=2, M=32, S=2, comm_cus=8)
+    d = gen.make_inputs(cfg, seed=4)
+    dev = DevInputs(d)
+    w = MxWeights(MoKLayer(L.desc_from_config(cfg, precision=L.MOK_PREC_MXFP8)), dev)
+    layer = MoKLayer(L.desc_from_config(cfg, precision=L.MOK_PREC_MXFP8,
+                                        comm_cus=L.mok_device_cus()))
+    layer.schedule(dev.ids)
+    torch.cuda.synchronize()
+    layer.ws.fill_(0x5A)
+    torch.cuda.synchronize()
+    with pytest.raises(L.MokError) as err:
+        layer.forward(dev.x, dev.ids, dev.gates, w.g, w.u, w.d, scales=(w.gs, w.us, w.ds))
+    assert err.value.code == L.MOK_E_SHAPE
+    torch.cuda.synchronize()
+    assert bool((layer.ws == 0x5A).all())
+
+
 def test_forward_mx_ring_and_split_invariance():
     cfg = SMALL[3]
     d = gen.make_inputs(cfg, seed=17)
