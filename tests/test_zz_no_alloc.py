@@ -83,3 +83,33 @@ def test_noalloc_status_and_refusals():
     torch.cuda.synchronize()
     assert bool((y == 1.0).all())
     assert np.isfinite(y.float().cpu().numpy()).all()
+
+
+def test_noalloc_inside_a_graph():
+    """The entry point captured in a HIP graph (the use it is for) and replayed with new
+    routing, activations and gates written into the captured inputs, with eager work in
+    between: each replay equals mok_schedule + mok_moe_fwd on a caller-owned workspace."""
+    cfg = gen.small_config("graph", T=300, D=192, I=192, E=6, k=2, M=96, S=2, comm_cus=8)
+    desc = L.desc_from_config(cfg)
+    dev = DevInputs(gen.make_inputs(cfg, seed=80))
+    status = torch.full((1,), 0xFFFF, dtype=torch.int32, device="cuda")
+    y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device="cuda")
+    L.mok_moe_fwd_noalloc(desc, dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd, None, None,
+                          None, y, status)  # eager first call: the area's address is known
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.mok_moe_fwd_noalloc(desc, dev.x, dev.ids, dev.gates, dev.wg, dev.wu, dev.wd, None,
+                              None, None, y)
+    torch.cuda.synchronize()
+    for i, seed in enumerate((81, 82)):
+        d = gen.make_inputs(cfg, seed=seed)
+        src = DevInputs(d)
+        ref = _reference(cfg, src, L.MOK_PREC_BF16, (src.wg, src.wu, src.wd), (None,) * 3)
+        for name in ("x", "ids", "gates", "wg", "wu", "wd"):
+            getattr(dev, name).copy_(getattr(src, name))
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[noalloc] graph replay {i} (seed {seed})")
+        assert torch.equal(y, ref), f"replay {i} differs from the workspace forward"
