@@ -27,6 +27,8 @@ taken.  `phases_unfused` times the forward's four steps as separate launches wit
 in-kernel phase clock: dispatch and combine against HBM bandwidth, GEMM1 and GEMM2
 against the MFMA peak.  `mxfp8_fwd` does the same for the MXFP8 forward (config 4), and
 `mxfp8_fwd_bwd` times forward + backward on that workload in MXFP8 and in bf16.
+`mxfp8_permuted` times MXFP8 forward + backward on config 6 (the same skew with permuted
+expert ranks: about 3.8k routed rows, the under-filled share).
 `macrobatch` compares successive forwards run one after another with the same forwards
 interleaved as macrobatches (MOK_FLAG_OVERLAP_NEXT, two workspaces and streams).
 `ring_recycling` times the step again with 4 and 2 ring slots (fewer than the
@@ -432,6 +434,28 @@ def mx_backward_figure(args):
     return out
 
 
+def mx_permuted_figure(args):
+    """Forward + backward in MXFP8 on config 6: config 4's Zipf skew with the popularity
+    ranks permuted, so this GPU's experts hold about 3.8k routed rows (two minibatches,
+    experts of 35 to 2k rows): the under-filled share, beside config 4's overloaded one."""
+    import torch
+
+    from mixture_experts_layer_mok_amd import gen
+    cfg = gen.CONFIGS[6]
+    d, t, layer = setup(cfg, False, True, torch.device("cuda:0"))
+    R = routed_rows(cfg, d["ids"])
+    log(f"timing the MXFP8 forward + backward on {cfg.name} ({R} routed rows)")
+    r = time_layer(cfg, t, layer, args.steps, args.warmup, True)
+    fwd, bwd = float(np.mean(r["fwd_ms"])), float(np.mean(r["bwd_ms"]))
+    out = {"workload": f"{cfg.name}: Zipf(1.2) routing with permuted ranks, {R} routed rows",
+           "fwd_ms": stats(r["fwd_ms"]), "bwd_ms": stats(r["bwd_ms"]),
+           "fwd_tflops": round(6.0 * cfg.D * cfg.I * R / (fwd * 1e-3) / 1e12, 2),
+           "bwd_tflops": round(12.0 * cfg.D * cfg.I * R / (bwd * 1e-3) / 1e12, 2)}
+    del layer, t, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def macrobatch_figure(args, n=4):
     """Macrobatch interleave on the config-3 workload (four ring slots, eight minibatches,
     so slots recycle): n forwards one after another on one stream and workspace, against
@@ -721,6 +745,7 @@ def main():
     if not mx and not args.no_mx and args.config == 5:
         out["mxfp8_fwd"] = mx_forward_figure(args)
         out["mxfp8_fwd_bwd"] = mx_backward_figure(args)
+        out["mxfp8_permuted"] = mx_permuted_figure(args)
     if not args.no_macrobatch and args.config == 5:
         out["macrobatch"] = macrobatch_figure(args)
     if not args.no_ring and args.config == 5:

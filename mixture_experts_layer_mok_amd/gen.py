@@ -14,7 +14,10 @@ Routing is upstream of the layer: the generator turns logits into top-k expert i
 (k largest logits, descending, ties to the lower id) and gates (softmax over the
 selected logits).  Both the GPU path and the oracle read the same ids and gates.
 The Zipf-skewed variant adds ln p_e with p_e proportional to (e+1)^-s to every
-token's logits, so low expert ids are the popular ones.
+token's logits, so low expert ids are the popular ones.  Its permuted-rank variant gives
+expert e the popularity rank perm[e] instead, with perm a permutation of the expert ids
+drawn from its own generator (``default_rng(zipf_perm_seed)``, outside the draw order
+above), so that the local experts hold ranks spread over the whole range.
 """
 from __future__ import annotations
 
@@ -44,6 +47,7 @@ class LayerConfig:
     comm_cus: int = 32      # workgroups given to dispatch/combine in the fused kernel
     precision: int = PREC_BF16
     zipf_s: float = 0.0     # 0 -> uniform router logits
+    zipf_perm_seed: int = -1  # >= 0: popularity ranks permuted over the expert ids
     x_std: float = 1.0
     w_std: float = 0.02
 
@@ -75,6 +79,11 @@ CONFIGS = {
     # per-shape tuner and a comm-CU sweep of the whole step agree)
     5: LayerConfig("c5-share-fwd-bwd-bf16", T=16384, D=7168, I=2048, E=64, k=8, E_loc=8,
                    M=2048, S=8, comm_cus=16),
+    # config 4's skew with the popularity ranks permuted: this GPU's eight experts get
+    # ranks spread over the range and hold about 3.8k routed rows, two minibatches
+    6: LayerConfig("c6-share-zipf-permuted-mxfp8", T=16384, D=7168, I=2048, E=64, k=8,
+                   E_loc=8, M=2048, S=4, comm_cus=32, precision=PREC_MXFP8, zipf_s=1.2,
+                   zipf_perm_seed=1004),
 }
 
 
@@ -139,7 +148,10 @@ def make_inputs(cfg: LayerConfig, seed: int | None = None, *, with_dy: bool = Fa
         x *= np.float32(cfg.x_std)
     logits = rng.standard_normal((T, E), dtype=np.float32)
     if cfg.zipf_s > 0:
-        logits = logits + zipf_bias(E, cfg.zipf_s)[None, :]
+        bias = zipf_bias(E, cfg.zipf_s)
+        if cfg.zipf_perm_seed >= 0:
+            bias = bias[np.random.default_rng(cfg.zipf_perm_seed).permutation(E)]
+        logits = logits + bias[None, :]
     ids, gates = route_topk(logits, k)
     wg = rng.standard_normal((nl, I, D), dtype=np.float32) * np.float32(cfg.w_std)
     wu = rng.standard_normal((nl, I, D), dtype=np.float32) * np.float32(cfg.w_std)

@@ -163,21 +163,23 @@ def test_forward_mx_edge_cases():
     assert rel_fro(y_values(y), ref) < TOL_MX
 
 
-def test_forward_config4_sampled_and_deterministic():
-    """Config 4 (MXFP8, Zipf routing, about 86k routed rows) against the MX-emulating
-    oracle on sampled tokens: tokens of every local expert, and the tokens that own the
-    rows on both sides of every minibatch window boundary and of the first m-tile start
-    (256 rows from the expert's first row) at or after it; plus tokens with no local slot,
-    which must be exactly zero.  Relative Frobenius error below 1e-2 and the largest
-    per-row error below 5e-2.  Then a bitwise repeat."""
-    cfg = gen.CONFIGS[4]
-    say("[c4] generating")
+@pytest.mark.parametrize("c", [4, 6], ids=["c4", "c6"])
+def test_forward_config4_sampled_and_deterministic(c):
+    """Config 4 (MXFP8, Zipf routing, about 86k routed rows) and config 6 (the same skew
+    with permuted ranks: about 3.8k rows, experts of 35 to 2k rows) against the
+    MX-emulating oracle on sampled tokens: tokens of every local expert, and the tokens
+    that own the rows on both sides of every minibatch window boundary and of the first
+    m-tile start (256 rows from the expert's first row) at or after it; plus tokens with no
+    local slot, which must be exactly zero.  Relative Frobenius error below 1e-2 and the
+    largest per-row error below 5e-2.  Then a bitwise repeat."""
+    cfg = gen.CONFIGS[c]
+    say(f"[c{c}] generating")
     d = gen.make_inputs(cfg)
     dev = DevInputs(d)
     y, layer = run_mx(cfg, dev)
     assert layer.status() == 0
     tab = layer.tables()
-    say(f"[c4] routed rows {tab['R']}, per expert {tab['counts'].tolist()}")
+    say(f"[c{c}] routed rows {tab['R']}, per expert {tab['counts'].tolist()}")
     y2, _ = run_mx(cfg, dev)
     assert torch.equal(y, y2), "MXFP8 forward not deterministic"
     ids = d["ids"]
@@ -198,11 +200,11 @@ def test_forward_config4_sampled_and_deterministic():
     toks = np.unique(s.perm[sorted(rows)] // cfg.k)
     local = (ids >= cfg.e0) & (ids < cfg.e0 + cfg.n_local)
     none = np.flatnonzero(~local.any(axis=1))[:8]
-    say(f"[c4] oracle on {len(toks)} tokens")
+    say(f"[c{c}] oracle on {len(toks)} tokens")
     ref = O.forward_tokens(toks, d["x"], ids, d["gates"], d["wg"], d["wu"], d["wd"], e0=cfg.e0,
                            mxfp8=True)
     yv = y_values(y)
     fro, worst, stray = row_errors(yv[toks], ref)
-    say(f"[c4] sampled rel_fro vs MX oracle {fro:.3e}, worst row {worst:.3e}")
+    say(f"[c{c}] sampled rel_fro vs MX oracle {fro:.3e}, worst row {worst:.3e}")
     assert fro < TOL_MX and worst < TOL_MX_ROW and stray == 0
     assert np.all(yv[none] == 0)

@@ -141,15 +141,17 @@ def test_backward_mx_perturbed_is_bitwise_neutral():
         assert torch.equal(g0[k], g1[k]), k
 
 
-def test_backward_mx_config4_sampled():
-    """Config 4 (MXFP8, Zipf routing, about 86k routed rows): dX and dG of sampled tokens
+@pytest.mark.parametrize("c", [4, 6], ids=["c4", "c6"])
+def test_backward_mx_config4_sampled(c):
+    """Config 4 (MXFP8, Zipf routing, about 86k routed rows) and config 6 (permuted ranks,
+    about 3.8k rows in experts of 35 to 2k rows): dX and dG of sampled tokens
     (tokens of every local expert and those owning the rows on both sides of every
     minibatch window boundary) against the MX oracle's backward on the pool of just those
     tokens (a token's dx and dG depend only on its own rows and the weights); and the three
     weight gradients of the local expert with the fewest rows against the oracle's
     backward on the tokens routed to it (their other slots masked)."""
-    cfg = gen.CONFIGS[4]
-    say("[mx-bwd c4] generating")
+    cfg = gen.CONFIGS[c]
+    say(f"[mx-bwd c{c}] generating")
     d = gen.make_inputs(cfg, with_dy=True)
     dev = DevInputs(d)
     _, g, layer = run_mx_fwd_bwd(cfg, dev)
@@ -166,21 +168,21 @@ def test_backward_mx_config4_sampled():
     for b in range(cfg.M, s.R, cfg.M):
         rows.update(r for r in (b - 1, b) if 0 <= r < s.R)
     toks = np.unique(s.perm[sorted(rows)] // cfg.k)
-    say(f"[mx-bwd c4] oracle backward on {len(toks)} tokens")
+    say(f"[mx-bwd c{c}] oracle backward on {len(toks)} tokens")
     ref = O.backward(d["dy"][toks], d["x"][toks], ids[toks], d["gates"][toks], d["wg"], d["wu"],
                      d["wd"], e0=cfg.e0, E=cfg.E, M=cfg.M, mxfp8=True)
     dx = bf16_values(g["dx"])[toks]
     fro, worst, stray = row_errors(dx, ref["dx"])
     dg_err = rel_fro(g["dg"].cpu().numpy()[toks], ref["dg"])
-    say(f"[mx-bwd c4] dx rel_fro {fro:.2e} worst row {worst:.2e}, dg {dg_err:.2e}")
+    say(f"[mx-bwd c{c}] dx rel_fro {fro:.2e} worst row {worst:.2e}, dg {dg_err:.2e}")
     assert fro < TOL_MX and worst < TOL_MX_ROW and stray == 0 and dg_err < TOL_MX
     e_min = int(np.argmin(np.where(s.counts > 0, s.counts, np.iinfo(np.int64).max)))
     tok_e = np.flatnonzero((ids == cfg.e0 + e_min).any(axis=1))
     ids_e = np.where(ids[tok_e] == cfg.e0 + e_min, ids[tok_e], -1)
-    say(f"[mx-bwd c4] oracle weight gradients of expert {e_min} ({len(tok_e)} rows)")
+    say(f"[mx-bwd c{c}] oracle weight gradients of expert {e_min} ({len(tok_e)} rows)")
     ref_w = O.backward(d["dy"][tok_e], d["x"][tok_e], ids_e, d["gates"][tok_e], d["wg"],
                        d["wu"], d["wd"], e0=cfg.e0, E=cfg.E, M=cfg.M, mxfp8=True)
     for name in ("dwg", "dwu", "dwd"):
         err = rel_fro(g[name][e_min].cpu().numpy(), ref_w[name][e_min])
-        say(f"[mx-bwd c4] {name}[{e_min}] rel_fro {err:.2e}")
+        say(f"[mx-bwd c{c}] {name}[{e_min}] rel_fro {err:.2e}")
         assert err < TOL_MX, (name, err)
