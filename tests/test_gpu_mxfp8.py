@@ -164,7 +164,7 @@ def test_forward_mx_edge_cases():
 
 
 @pytest.mark.parametrize("c", [4, 6], ids=["c4", "c6"])
-def test_forward_config4_sampled_and_deterministic(c):
+def test_forward_zipf_shares_sampled_and_deterministic(c):
     """Config 4 (MXFP8, Zipf routing, about 86k routed rows) and config 6 (the same skew
     with permuted ranks: about 3.8k rows, experts of 35 to 2k rows) against the
     MX-emulating oracle on sampled tokens: tokens of every local expert, and the tokens

@@ -142,7 +142,7 @@ def test_backward_mx_perturbed_is_bitwise_neutral():
 
 
 @pytest.mark.parametrize("c", [4, 6], ids=["c4", "c6"])
-def test_backward_mx_config4_sampled(c):
+def test_backward_mx_zipf_shares_sampled(c):
     """Config 4 (MXFP8, Zipf routing, about 86k routed rows) and config 6 (permuted ranks,
     about 3.8k rows in experts of 35 to 2k rows): dX and dG of sampled tokens
     (tokens of every local expert and those owning the rows on both sides of every
