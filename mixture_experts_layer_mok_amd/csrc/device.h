@@ -91,9 +91,14 @@ __device__ __forceinline__ void st_dev_b128(void* p, v4u v) {
 // row's length, so loads past the end read zero and stores past it are dropped, which
 // lets a row loop run without per-chunk branches.  The base is made wave-uniform.
 // kCpolDev (sc1) makes an access device scope, as the handoff protocol above requires.
+// kCpolStream (nt) marks an access non-temporal, for rows written once and read once by
+// a later step (results, saved activations): they then do not displace the L2 lines
+// that the GEMM tiles re-read (measured on MI355X: the MXFP8 forward at config 4 4.70 ->
+// 4.50 ms, the config-4 combine as its own launch 320 -> 265 us).  It combines with sc1.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kCpolPlain = 0;
 constexpr int kCpolDev = 16;
+constexpr int kCpolStream = 2;
 
 __device__ __forceinline__ rsrc_t row_rsrc(const void* base, uint32_t bytes) {
   const uint64_t x = reinterpret_cast<uint64_t>(base);

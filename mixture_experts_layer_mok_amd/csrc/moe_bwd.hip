@@ -229,7 +229,7 @@ __device__ __forceinline__ uint32_t dx_tile(const BwdParams& p, int g, int nt) {
     tile_gemm_km<kKCD, kKW, true>(a, b, int(K / kBK), acc);
   }
   const uint32_t t_k = uint32_t(wall_clock64());
-  epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf, int64_t(p.T) * p.k);
+  epi_scatter<true, false>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.dxbuf, int64_t(p.T) * p.k);
   return t_k;
 }
 

@@ -98,7 +98,7 @@ __device__ __forceinline__ void combine_if_last(const FwdParams& p, int r) {
   const int32_t ps = lane < p.k ? p.P.pos[q0 + lane] : -1;
   const float g = lane < p.k ? p.a.gates[q0 + lane] : 0.f;
   if (wave_max(ps) == r)
-    wave_pair_sum_loaded<kCpolDev, 4>(p.a.y + q0 / p.k * p.D, p.P.obuf, q0, p.D, ps, g);
+    wave_pair_sum_loaded<kCpolDev | kCpolStream, 4>(p.a.y + q0 / p.k * p.D, p.P.obuf, q0, p.D, ps, g);
 }
 
 // ------------------------------------------------------------------------------------
@@ -194,7 +194,7 @@ __device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
     const MxOperands o = mx_ops_gemm2(p, p.P.full_h + int64_t(e.x) * p.I,
                                       p.P.full_hs + int64_t(e.x) * p.hs_ld, e.z);
     run_tile_mx<false>(false, o, e.y, nt * kBN2, p.D, p.I, acc);
-    epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
+    epi_scatter<false, true>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
     return;
   }
   const uint16_t* H = reinterpret_cast<const uint16_t*>(p.P.full_h);
@@ -203,7 +203,7 @@ __device__ __forceinline__ void gemm2_tile_unfused(const FwdParams& p) {
   run_tile<false>(false, H + int64_t(e.x) * p.I, e.y,
                   reinterpret_cast<const uint16_t*>(p.a.wd) + e.z * wsz, nullptr, nt * kBN2, p.D,
                   p.I, acc);
-  epi_scatter<false>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
+  epi_scatter<false, true>(acc, e.y, nt * kBN2, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
 }
 
 template <bool MX>
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_combine_all(FwdParams p) {
     const float g = g_n;
     load(t + nw, ps_n, g_n);
     if (wave_max(ps) >= 0)
-      wave_pair_sum_loaded<kCpolPlain, 2, 16>(p.a.y + int64_t(t) * p.D, p.P.obuf, int64_t(t) * p.k,
+      wave_pair_sum_loaded<kCpolStream, 2, 16>(p.a.y + int64_t(t) * p.D, p.P.obuf, int64_t(t) * p.k,
                                           p.D, ps, g);
     else
       wave_zero_row(p.a.y + int64_t(t) * p.D, p.D);
@@ -556,7 +556,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
                                           slot + p.slot_hs + int64_t(r0) * p.hs_ld, e.z);
         run_tile_mx<true>(false, o, e.y, n0, p.D, p.I, acc);
         const uint32_t t_k = trace ? trace_now() : 0u;
-        epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
+        epi_scatter<true, true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
         const uint32_t t_e = trace ? trace_now() : 0u;
         perturb_pause(p.perturb, tk);
         wg_signal_add(done + mb, 1);
@@ -580,7 +580,7 @@ __device__ __forceinline__ void compute_role(const FwdParams& p, int vid, int C,
       perturb_pause(p.perturb, tk);
       wg_signal_add(hd, 1);
     } else {
-      epi_scatter<true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
+      epi_scatter<true, true>(acc, e.y, n0, p.D, p.P.perm + e.x, p.P.obuf, int64_t(p.T) * p.k);
       t_e = trace ? trace_now() : 0u;
       perturb_pause(p.perturb, tk);
       wg_signal_add(done + mb, 1);

@@ -74,7 +74,8 @@ __device__ __forceinline__ void wave_zero_row(uint16_t* dst, int D) {
 // take 4 slots of kCombChunks, which their registers allow beside the tile code of the
 // same kernel).  Source
 // loads use the cache policy kPol (device scope for rows written by other workgroups of
-// a running kernel); every access goes through a row-length buffer resource.
+// a running kernel); the destination row is stored non-temporally (nothing in the layer
+// reads it again); every access goes through a row-length buffer resource.
 constexpr int kCombChunks = 8;
 
 __device__ __forceinline__ void acc_gated(float (&acc)[8], v4u v, float g) {
@@ -113,7 +114,7 @@ __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16
       for (int u = 0; u < kRowBatch; ++u) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         acc_gated(acc, v[u], g);
-        buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * u) * 16, pack_acc(acc));
+        buf_st16<kCpolStream>(ry, b0 + (lane + 64 * u) * 16, pack_acc(acc));
       }
     }
     return;
@@ -152,7 +153,7 @@ __device__ __forceinline__ void wave_pair_sum_loaded(uint16_t* dst, const uint16
     }
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
-      buf_st16<kCpolPlain>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
+      buf_st16<kCpolStream>(ry, b0 + (lane + 64 * c) * 16, pack_acc(acc[c]));
   }
 }
 
@@ -173,12 +174,12 @@ __device__ __forceinline__ void wave_pair_sum(uint16_t* dst, const uint16_t* row
 // layout; see epi_swiglu) stored as bf16 rows [rows, 2I] at AB: gate in [0, I), up in
 // [I, 2I).  Staged in LDS as rows of 256 columns (tile rows 0..127 in the A stages,
 // 128..255 in the B stages; 16-byte chunk c of row r at c ^ (r % 32)), one 8-byte write
-// per group of four columns, then written as whole row segments, 16 bytes a lane.  Ends
-// with a barrier.
+// per group of four columns, then written as whole row segments, 16 bytes a lane,
+// non-temporally (the rows are read by the backward's launch).  Ends with a barrier.
 template <bool kCoherent>
 __device__ __forceinline__ void epi_store_ab(const TileAcc& acc, int rows, int n0, int I,
                                                uint16_t* AB) {
-  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int kPol = (kCoherent ? kCpolDev : kCpolPlain) | kCpolStream;
   constexpr int W = kThreads / 64;
   typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
   const int tid = opaque(threadIdx.x);
@@ -320,8 +321,9 @@ __device__ __forceinline__ void epi_swiglu(const TileAcc& acc, int rows, int n0,
 // of a row read hit different banks).  Each wave then writes whole 512-byte row segments,
 // 16 bytes a lane when every byte offset of obuf fits in 32 bits (two rows a store
 // through one resource), else 8 bytes a lane through a resource per row.  With kCoherent
-// the row stores are device scope.  Ends with a barrier.
-template <bool kCoherent>
+// the row stores are device scope; with kStream non-temporal (GEMM2 results, read once by
+// the combine).  Ends with a barrier.
+template <bool kCoherent, bool kStream>
 __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0, int D,
                                             const int32_t* perm_rows, uint16_t* obuf,
                                             int64_t obuf_rows) {
@@ -352,7 +354,7 @@ __device__ __forceinline__ void epi_scatter(const TileAcc& acc, int rows, int n0
   // wave w writes tile rows w, w + 8, ..: their destinations are loaded one per lane
   // and all 32 staged rows are read before the first store, so that no load waits
   // behind a store (vector memory operations complete in order)
-  constexpr int kPol = kCoherent ? kCpolDev : kCpolPlain;
+  constexpr int kPol = (kCoherent ? kCpolDev : kCpolPlain) | (kStream ? kCpolStream : 0);
   constexpr int kRowsPerWave = 256 / (kThreads / 64);
   const int wr = __builtin_amdgcn_readfirstlane(w);
   const int my_r = wr + (kThreads / 64) * (lane % kRowsPerWave);
