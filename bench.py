@@ -248,7 +248,9 @@ def time_cold(cfg, t, layer, steps, with_bwd):
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=t["x"].device)
     y = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=t["x"].device)
     fwd, bwd = [], []
-    for i in range(steps):
+    # one untimed step first: with the scrub buffer taken, the gradient outputs may need
+    # fresh device allocations, which must not fall inside a timed phase
+    for i in range(-1, steps):
         scrub.fill_(i & 0xFF)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         layer.schedule(t["ids"])
@@ -266,6 +268,8 @@ def time_cold(cfg, t, layer, steps, with_bwd):
             ev.append(torch.cuda.Event(enable_timing=True))
             ev[3].record(stream)
         torch.cuda.synchronize()
+        if i < 0:
+            continue
         fwd.append(ev[0].elapsed_time(ev[1]))
         if with_bwd:
             bwd.append(ev[2].elapsed_time(ev[3]))
